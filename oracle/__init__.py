@@ -1,0 +1,203 @@
+"""CPU oracle for the MoE forward path -- TEST INFRASTRUCTURE ONLY.
+
+The product (the HIP library and its Python binding) never imports this
+package.  Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` use it.  The arithmetic lives in ``oracle.c`` (plain C
+loops, fp64 accumulation); this module builds it with gcc and wraps each
+function for numpy arrays.  It shares no code with the HIP path.
+
+Each wrapper names the page passage its C function follows; see oracle.c.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle355.so")
+
+F32, BF16, F64 = 0, 1, 2
+SOFTMAX, SIGMOID = 0, 1
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile oracle.c into liboracle355.so (gcc, OpenMP, no contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wno-unknown-pragmas", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.orc_sigmoid_pinned.argtypes = [ctypes.c_float]
+    lib.orc_sigmoid_pinned.restype = ctypes.c_float
+    lib.orc_sigmoid_pinned_array.argtypes = [P, P, i64]
+    lib.orc_route.argtypes = [P, i32, i32, i32, i32, i32, i32, i32, P, P]
+    lib.orc_route.restype = i32
+    lib.orc_send_counts.argtypes = [P, i32, i32, i32, i32, P]
+    lib.orc_send_counts.restype = i32
+    lib.orc_permute_index.argtypes = [P, i64, i32, P, P, P, P]
+    lib.orc_permute_index.restype = i32
+    lib.orc_gather_rows.argtypes = [P, i64, P, i64, i32, P]
+    lib.orc_expert_swiglu_rows.argtypes = [P, i32, i64, i32, i32, P, P, P, P]
+    lib.orc_combine.argtypes = [P, i32, i64, i32, i32, P, P, P, i32, P]
+    lib.orc_alltoall_bytes.argtypes = [i64, i32, i64, i32, f64, f64, i32]
+    lib.orc_alltoall_bytes.restype = f64
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype=None):
+    return np.ascontiguousarray(a if dtype is None else a.astype(dtype, copy=False))
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"unsupported oracle dtype {a.dtype}")
+
+
+def sigmoid_pinned(x: np.ndarray) -> np.ndarray:
+    """The pinned fp32 sigmoid used for group scores (oracle.c, orc_sigmoid_pinned)."""
+    x = _c(x, np.float32)
+    y = np.empty_like(x)
+    _load().orc_sigmoid_pinned_array(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def route(logits: np.ndarray, k: int, gating: str = "softmax", renormalize: int = 1,
+          n_groups: int = 1, topk_groups: int = 1):
+    """O1: top-k ids [T,k] int32 and gates [T,k] fp32 (oracle.c, orc_route)."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    g = SOFTMAX if gating == "softmax" else SIGMOID
+    rc = _load().orc_route(_ptr(logits), T, E, k, g, int(renormalize), n_groups, topk_groups,
+                           _ptr(ids), _ptr(w))
+    if rc != 0:
+        raise ValueError("orc_route: arguments outside the contract")
+    return ids, w
+
+
+def send_counts(ids: np.ndarray, E: int, n_ep: int) -> np.ndarray:
+    """O2: send-count matrix S [n_ep, n_ep], row = source rank (oracle.c, orc_send_counts)."""
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    S = np.empty((n_ep, n_ep), np.int32)
+    if _load().orc_send_counts(_ptr(ids), T, k, E, n_ep, _ptr(S)) != 0:
+        raise ValueError("orc_send_counts: arguments outside the contract")
+    return S
+
+
+def permute_index(ids: np.ndarray, E: int):
+    """O3: counts [E], offsets [E+1], order [M], inv [M] (oracle.c, orc_permute_index)."""
+    flat = _c(ids, np.int32).reshape(-1)
+    M = flat.size
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    order = np.empty(M, np.int32)
+    inv = np.empty(M, np.int32)
+    if _load().orc_permute_index(_ptr(flat), M, E, _ptr(counts), _ptr(offsets), _ptr(order),
+                                 _ptr(inv)) != 0:
+        raise ValueError("orc_permute_index: expert id out of range")
+    return counts, offsets, order, inv
+
+
+def gather_rows(x: np.ndarray, order: np.ndarray, k: int) -> np.ndarray:
+    """X[order] with packed row p = token order[p] // k, bit for bit (oracle.c, orc_gather_rows)."""
+    x = _c(x)
+    order = _c(order, np.int32)
+    out = np.empty((order.size,) + x.shape[1:], x.dtype)
+    row_bytes = x.strides[0] if x.shape[0] else x.itemsize * int(np.prod(x.shape[1:]))
+    _load().orc_gather_rows(_ptr(x), row_bytes, _ptr(order), order.size, k, _ptr(out))
+    return out
+
+
+def expert_swiglu_rows(xrows: np.ndarray, expert_of_row: np.ndarray, w13: np.ndarray,
+                       w2: np.ndarray) -> np.ndarray:
+    """O4: y[r] = W_down,e (SiLU(W_gate,e x_r) * W_up,e x_r) in fp64 (oracle.c)."""
+    xrows = _c(xrows)
+    w13 = _c(w13)
+    w2 = _c(w2)
+    dt = _dtype_code(xrows)
+    if _dtype_code(w13) != dt or _dtype_code(w2) != dt:
+        raise TypeError("rows and weights must share a dtype")
+    R, d = xrows.shape
+    G, two, ffn, d2 = w13.shape
+    assert two == 2 and d2 == d and w2.shape == (G, d, ffn)
+    e = _c(expert_of_row, np.int32).reshape(-1)
+    assert e.size == R and (R == 0 or (e.min() >= 0 and e.max() < G))
+    y = np.empty((R, d), np.float64)
+    _load().orc_expert_swiglu_rows(_ptr(xrows), dt, R, d, ffn, _ptr(e), _ptr(w13), _ptr(w2), _ptr(y))
+    return y
+
+
+def combine(y_perm: np.ndarray, inv: np.ndarray, w: np.ndarray, y_shared=None) -> np.ndarray:
+    """O5: y[t] = sum_j w[t,j] y_perm[inv[t k + j]] (+ y_shared[t]) in fp64 (oracle.c)."""
+    y_perm = _c(y_perm)
+    w = _c(w, np.float32)
+    T, k = w.shape
+    d = y_perm.shape[1]
+    inv = _c(inv, np.int32).reshape(-1)
+    assert inv.size == T * k
+    y = np.empty((T, d), np.float64)
+    if y_shared is not None:
+        y_shared = _c(y_shared)
+        assert y_shared.shape == (T, d)
+        sh_ptr, sh_dt = _ptr(y_shared), _dtype_code(y_shared)
+    else:
+        sh_ptr, sh_dt = None, 0
+    _load().orc_combine(_ptr(y_perm), _dtype_code(y_perm), T, k, d, _ptr(inv), _ptr(w), sh_ptr,
+                        sh_dt, _ptr(y))
+    return y
+
+
+def alltoall_bytes(T_loc: int, k: int, d: int, n_ep: int, s_disp: float, s_comb: float,
+                   training: bool = False) -> float:
+    """Dispatch + combine bytes one GPU sends per layer (oracle.c, orc_alltoall_bytes)."""
+    return _load().orc_alltoall_bytes(T_loc, k, d, n_ep, s_disp, s_comb, int(training))
+
+
+# --------------------------------------------------------------------------
+# Compositions of O1..O5 (step order of the forward pass in "Expert parallelism").
+# --------------------------------------------------------------------------
+
+def layer_tokens(x, ids, w, w13, w2, tokens, sh_w13=None, sh_w2=None):
+    """The plain definition for selected tokens: y[t] = sum_j w[t,j] f_{ids[t,j]}(x[t])
+    (+ f_shared(x[t])), evaluated with O4 and O5 in fp64.  Returns [len(tokens), d]."""
+    tokens = np.asarray(tokens, np.int64)
+    k = ids.shape[1]
+    xs = _c(x[tokens])
+    rows = np.repeat(xs, k, axis=0)
+    y_rows = expert_swiglu_rows(rows, ids[tokens].reshape(-1), w13, w2)
+    y_sh = None
+    if sh_w13 is not None:
+        y_sh = expert_swiglu_rows(xs, np.zeros(len(tokens), np.int32), sh_w13, sh_w2)
+    inv = np.arange(len(tokens) * k, dtype=np.int32)
+    return combine(y_rows, inv, w[tokens], y_sh)

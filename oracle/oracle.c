@@ -1,0 +1,335 @@
+/*
+ * CPU oracle for one GPU's share of an expert-parallel MoE forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is what the HIP path is checked
+ * against; it is never part of the product.  Only the tests, the smoke
+ * check and the CPU-baseline leg of the benchmark load it.  It shares no
+ * source with the HIP library and includes nothing from it.
+ *
+ * Plain loops, written for a reader to check against the pages by eye:
+ *   - "Expert parallelism" (zerotofrontier.app/moe/expert-parallel), the
+ *     textbook section: the numbered forward-pass steps in section "Expert
+ *     parallelism", the send matrix in "A dispatch you can check by hand",
+ *     the byte count in "How many bytes move", node-limited routing in "What
+ *     DeepSeek-V3 did about it", and order / counts / inverse in "Token
+ *     permutation and grouped GEMMs".
+ *   - "05 - Expert Parallelism (MoE)" (project-fortress), section "The
+ *     all-to-all pattern": top-k routing and the router-probability-weighted
+ *     sum; section "Fine-grained vs coarse experts": the always-active shared
+ *     expert.
+ *
+ * Precision: routing keys and the group scores are fp32 (the logits are fp32
+ * inputs and the selection must be bit-exact); every other floating-point
+ * result is accumulated and returned in fp64.  bf16 values are widened
+ * exactly.  Build with -ffp-contract=off and without fast-math.
+ *
+ * Parity: every function here is pinned by the CPU tests (hand-worked
+ * example, invariants, brute force, closed forms); none is unpinned.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+#define ORC_F64 2
+
+#define ORC_SOFTMAX 0
+#define ORC_SIGMOID 1
+
+static double widen(const void *base, int dtype, int64_t i)
+{
+    if (dtype == ORC_F32) return (double)((const float *)base)[i];
+    if (dtype == ORC_F64) return ((const double *)base)[i];
+    uint32_t u = (uint32_t)((const uint16_t *)base)[i] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* ------------------------------------------------------------------------
+ * Pinned fp32 sigmoid.
+ *
+ * DeepSeek-V3's node-limited routing scores a group of experts by the sum of
+ * the token's two highest affinities there ("What DeepSeek-V3 did about it");
+ * the affinity is the sigmoid of the logit.  Which groups survive is an
+ * integer decision taken on fp32 sums, so both sides must produce the same
+ * fp32 sigmoid bits.  This is that function, written from the mathematics:
+ *
+ *   exp(y), y <= 0: Cody & Waite range reduction y = n ln2 + r, |r| <= ln2/2,
+ *   with ln2 split as C_HI + C_LO (C_HI has 12 significant bits, so n*C_HI is
+ *   exact), then the degree-7 Taylor polynomial of exp(r) in Horner form with
+ *   coefficients fl(1/i!), then scaling by 2^n.  Every operation is one IEEE
+ *   fp32 operation (fmaf where written), rounded to nearest even.
+ *   Results that would leave the normal range (y < -87) return 0.
+ *
+ *   sigmoid(x) = 1/(1+t) for x >= 0 and t/(1+t) for x < 0, with t = exp(-|x|).
+ * ---------------------------------------------------------------------- */
+static float pinned_exp_nonpos(float y)
+{
+    const float log2e = (float)1.4426950408889634074;       /* fl(log2 e) */
+    const float c_hi = 2839.0f / 4096.0f;                    /* ln2 to 12 significant bits */
+    const float c_lo = (float)(0.69314718055994530942 - 2839.0 / 4096.0);
+    static const float inv_fact[8] = {
+        1.0f, 1.0f, (float)(1.0 / 2), (float)(1.0 / 6), (float)(1.0 / 24),
+        (float)(1.0 / 120), (float)(1.0 / 720), (float)(1.0 / 5040)};
+    if (y < -87.0f) return 0.0f;
+    float n = rintf(y * log2e);
+    float r = fmaf(-n, c_hi, y);
+    r = fmaf(-n, c_lo, r);
+    float p = inv_fact[7];
+    for (int i = 6; i >= 0; --i) p = fmaf(p, r, inv_fact[i]);
+    return ldexpf(p, (int)n);
+}
+
+float orc_sigmoid_pinned(float x)
+{
+    float t = pinned_exp_nonpos(-fabsf(x));
+    float den = 1.0f + t;
+    return x >= 0.0f ? 1.0f / den : t / den;
+}
+
+void orc_sigmoid_pinned_array(const float *x, float *y, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) y[i] = orc_sigmoid_pinned(x[i]);
+}
+
+/* ------------------------------------------------------------------------
+ * O1  Route: top-k per token, optionally node (group) limited, plus gates.
+ *
+ * Step 1 of the forward pass ("Expert parallelism": compute the router and
+ * the top-k choices for the local tokens).  The key of expert e is the fp32
+ * logit with -0 read as +0; both gating maps are increasing, so ranking by
+ * the logit ranks by the gate.  Among equal keys the lower expert id wins,
+ * and slot j holds the j-th pick.
+ *
+ * Group limit ("What DeepSeek-V3 did about it"): score each of n_groups
+ * contiguous groups by the fp32 sum of its two highest pinned-sigmoid
+ * affinities, keep the best topk_groups groups (lower group id on ties), and
+ * pick the k experts only among them.
+ *
+ * Gates, in fp64, rounded once to fp32:
+ *   softmax, renormalised: exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0)
+ *   softmax, not renorm.:  exp(l_j - m) / sum_e exp(l_e - m), m = max_e l_e
+ *   sigmoid, renormalised: s(l_j) / sum_{i<k} s(l_i)
+ *   sigmoid, not renorm.:  s(l_j)
+ * Returns 0, or -1 on arguments outside the contract.
+ * ---------------------------------------------------------------------- */
+int orc_route(const float *logits, int T, int E, int k, int gating, int renorm,
+              int n_groups, int topk_groups, int32_t *ids, float *w)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E || k > 64 || n_groups < 1 || E % n_groups != 0 ||
+        topk_groups < 1 || topk_groups > n_groups)
+        return -1;
+    const int gs = E / n_groups;
+    if (n_groups > 1 && (gs < 2 || topk_groups * gs < k)) return -1;
+
+#pragma omp parallel
+    {
+        float *key = malloc(sizeof(float) * (size_t)E);
+        char *allowed = malloc((size_t)E);
+        char *taken = malloc((size_t)E);
+        float *gscore = malloc(sizeof(float) * (size_t)n_groups);
+        char *gkept = malloc((size_t)n_groups);
+#pragma omp for schedule(static)
+        for (int t = 0; t < T; ++t) {
+            const float *l = logits + (int64_t)t * E;
+            for (int e = 0; e < E; ++e) {
+                key[e] = l[e] + 0.0f;          /* -0 + +0 = +0 */
+                allowed[e] = 1;
+                taken[e] = 0;
+            }
+            if (n_groups > 1) {
+                for (int g = 0; g < n_groups; ++g) {
+                    float a1 = -INFINITY, a2 = -INFINITY;
+                    for (int e = g * gs; e < (g + 1) * gs; ++e) {
+                        float a = orc_sigmoid_pinned(key[e]);
+                        if (a > a1) { a2 = a1; a1 = a; }
+                        else if (a > a2) { a2 = a; }
+                    }
+                    gscore[g] = a1 + a2;
+                    gkept[g] = 0;
+                }
+                for (int r = 0; r < topk_groups; ++r) {
+                    int best = -1;
+                    for (int g = 0; g < n_groups; ++g)
+                        if (!gkept[g] && (best < 0 || gscore[g] > gscore[best])) best = g;
+                    gkept[best] = 1;
+                }
+                for (int e = 0; e < E; ++e) allowed[e] = gkept[e / gs];
+            }
+            int32_t *id = ids + (int64_t)t * k;
+            for (int j = 0; j < k; ++j) {
+                int best = -1;
+                for (int e = 0; e < E; ++e)
+                    if (allowed[e] && !taken[e] && (best < 0 || key[e] > key[best])) best = e;
+                taken[best] = 1;
+                id[j] = best;
+            }
+            float *wt = w + (int64_t)t * k;
+            double v[64], sum = 0.0;     /* k <= 64 is checked above */
+            if (gating == ORC_SOFTMAX) {
+                if (renorm) {
+                    double l0 = (double)key[id[0]];
+                    for (int j = 0; j < k; ++j) { v[j] = exp((double)key[id[j]] - l0); sum += v[j]; }
+                } else {
+                    double m = (double)key[0];
+                    for (int e = 1; e < E; ++e) if ((double)key[e] > m) m = (double)key[e];
+                    for (int e = 0; e < E; ++e) sum += exp((double)key[e] - m);
+                    for (int j = 0; j < k; ++j) v[j] = exp((double)key[id[j]] - m);
+                }
+            } else {
+                for (int j = 0; j < k; ++j) { v[j] = 1.0 / (1.0 + exp(-(double)key[id[j]])); sum += v[j]; }
+                if (!renorm) sum = 1.0;
+            }
+            for (int j = 0; j < k; ++j) wt[j] = (float)(v[j] / sum);
+        }
+        free(key); free(allowed); free(taken); free(gscore); free(gkept);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * O2  Send-count matrix ("A dispatch you can check by hand").
+ * Entry (s, q) counts the rows GPU s sends to GPU q.  Token t belongs to
+ * source rank s = floor(t / T_loc) (each GPU holds its own T_loc tokens,
+ * section "Expert parallelism"), and expert i lives on GPU floor(i n_ep / E)
+ * (step 2 of the forward pass).
+ * ---------------------------------------------------------------------- */
+int orc_send_counts(const int32_t *ids, int T, int k, int E, int n_ep, int32_t *S)
+{
+    if (n_ep < 1 || T % n_ep != 0 || E % n_ep != 0) return -1;
+    const int T_loc = T / n_ep;
+    memset(S, 0, sizeof(int32_t) * (size_t)n_ep * (size_t)n_ep);
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int e = ids[(int64_t)t * k + j];
+            if (e < 0 || e >= E) return -1;
+            int s = t / T_loc;
+            int q = (int)(((int64_t)e * n_ep) / E);
+            S[(int64_t)s * n_ep + q] += 1;
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * O3  Permutation ("Token permutation and grouped GEMMs").
+ * order is the stable argsort of the expert ids of the M = T k assignments
+ * (assignment a = t k + j), counts the per-expert histogram, offsets its
+ * exclusive prefix sum (offsets[E] = M), and inv the inverse permutation,
+ * inv[order[p]] = p.  Written as a textbook stable counting sort.
+ * ---------------------------------------------------------------------- */
+int orc_permute_index(const int32_t *ids, int64_t M, int E, int32_t *counts,
+                      int32_t *offsets, int32_t *order, int32_t *inv)
+{
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t a = 0; a < M; ++a) {
+        if (ids[a] < 0 || ids[a] >= E) return -1;
+        counts[ids[a]] += 1;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t *cursor = malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+    for (int e = 0; e < E; ++e) cursor[e] = offsets[e];
+    for (int64_t a = 0; a < M; ++a) {
+        int32_t p = cursor[ids[a]]++;
+        order[p] = (int32_t)a;
+        inv[a] = p;
+    }
+    free(cursor);
+    return 0;
+}
+
+/* X[order]: packed row p is a copy of token order[p] / k, bit for bit. */
+void orc_gather_rows(const void *x, int64_t row_bytes, const int32_t *order, int64_t M,
+                     int k, void *x_perm)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < M; ++p)
+        memcpy((char *)x_perm + p * row_bytes, (const char *)x + (int64_t)(order[p] / k) * row_bytes,
+               (size_t)row_bytes);
+}
+
+/* ------------------------------------------------------------------------
+ * O4  Expert MLP on a list of rows (step 5 of the forward pass).
+ * A SwiGLU expert has three d x ffn matrices and costs 6 d ffn forward FLOPs
+ * per row ("A worked example at DeepSeek-V3's shape", "DeepSeek-V3's layout,
+ * counted"):
+ *   g = W_gate x,  u = W_up x,  h = SiLU(g) * u,  y = W_down h,
+ *   SiLU(z) = z / (1 + exp(-z)).
+ * w13 is [G][2][ffn][d] (gate rows, then up rows), w2 is [G][d][ffn].  Row r
+ * uses expert expert_of_row[r].  All sums run in fp64 in index order.
+ * ---------------------------------------------------------------------- */
+void orc_expert_swiglu_rows(const void *xrows, int dtype, int64_t R, int d, int ffn,
+                            const int32_t *expert_of_row, const void *w13, const void *w2,
+                            double *y)
+{
+#pragma omp parallel
+    {
+        double *xv = malloc(sizeof(double) * (size_t)d);
+        double *h = malloc(sizeof(double) * (size_t)ffn);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < R; ++r) {
+            int64_t e = expert_of_row[r];
+            for (int i = 0; i < d; ++i) xv[i] = widen(xrows, dtype, r * d + i);
+            int64_t gate0 = e * 2 * (int64_t)ffn * d;
+            int64_t up0 = gate0 + (int64_t)ffn * d;
+            for (int n = 0; n < ffn; ++n) {
+                double g = 0.0, u = 0.0;
+                for (int i = 0; i < d; ++i) {
+                    g += widen(w13, dtype, gate0 + (int64_t)n * d + i) * xv[i];
+                    u += widen(w13, dtype, up0 + (int64_t)n * d + i) * xv[i];
+                }
+                h[n] = g / (1.0 + exp(-g)) * u;
+            }
+            int64_t down0 = e * (int64_t)d * ffn;
+            for (int m = 0; m < d; ++m) {
+                double acc = 0.0;
+                for (int n = 0; n < ffn; ++n) acc += widen(w2, dtype, down0 + (int64_t)m * ffn + n) * h[n];
+                y[r * d + m] = acc;
+            }
+        }
+        free(xv);
+        free(h);
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * O5  Unpermute and weight (step 7 of the forward pass; "Token permutation
+ * and grouped GEMMs": Y_sorted[inv] restores token order).  Each token's k
+ * expert outputs are added with their gates, slot order j = 0..k-1, then the
+ * shared expert's output (weight 1) if given:
+ *   y[t] = sum_j w[t,j] y_perm[inv[t k + j]]  (+ y_shared[t]).
+ * ---------------------------------------------------------------------- */
+void orc_combine(const void *y_perm, int dtype, int64_t T, int k, int d, const int32_t *inv,
+                 const float *w, const void *y_shared, int sh_dtype, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int m = 0; m < d; ++m) {
+            double acc = 0.0;
+            for (int j = 0; j < k; ++j) {
+                int64_t p = inv[t * k + j];
+                acc += (double)w[t * k + j] * widen(y_perm, dtype, p * d + m);
+            }
+            if (y_shared) acc += widen(y_shared, sh_dtype, t * d + m);
+            y[t * d + m] = acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Bytes one GPU sends in the dispatch plus the combine all-to-all ("How many
+ * bytes move"): each of the T_loc k assignments carries d numbers, of which
+ * a fraction (n_ep - 1)/n_ep leaves the GPU; dispatch at s_disp bytes per
+ * number, combine at s_comb.  A training step does both twice.
+ * ---------------------------------------------------------------------- */
+double orc_alltoall_bytes(int64_t T_loc, int k, int64_t d, int n_ep, double s_disp,
+                          double s_comb, int training)
+{
+    double per = (double)T_loc * k * (double)d * (double)(n_ep - 1) / (double)n_ep;
+    double b = per * s_disp + per * s_comb;
+    return training ? 2.0 * b : b;
+}

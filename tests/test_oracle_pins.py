@@ -1,0 +1,441 @@
+"""Pins of the CPU oracle to facts fixed outside it: the pages' hand-worked
+example and printed numbers, stated invariants, closed forms, brute force on
+tiny inputs and special cases that reduce to library routines.  CPU only.
+
+Page references:
+  EP  = "Expert parallelism", zerotofrontier.app/moe/expert-parallel
+  RM  = "05 - Expert Parallelism (MoE)", project-fortress inference roadmap
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from token_routing_expert_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# EP, "A dispatch you can check by hand"
+# --------------------------------------------------------------------------
+
+def test_hand_dispatch_send_counts():
+    g = _golden("hand_dispatch.json")
+    ids = np.array(g["topk_ids"], np.int32)
+    S = oracle.send_counts(ids, g["E"], g["n_ep"])
+    assert S.sum(axis=1).tolist() == g["stated"]["row_sums"]
+    assert S.sum(axis=0).tolist() == g["stated"]["column_sums"]
+    assert S[0, 0] == g["stated"]["gpu0_keeps"] and S[0, 1] == g["stated"]["gpu0_sends"]
+    assert S[1, 1] == g["stated"]["gpu1_keeps"] and S[1, 0] == g["stated"]["gpu1_sends"]
+    assert S.tolist() == g["derived"]["send_counts"]
+    # "Now suppose every token had chosen {0, 1}."
+    all01 = np.tile(np.array([[0, 1]], np.int32), (g["T"], 1))
+    assert oracle.send_counts(all01, g["E"], g["n_ep"]).tolist() == g["stated"]["all_choose_0_1_matrix"]
+
+
+def test_hand_dispatch_permutation():
+    g = _golden("hand_dispatch.json")
+    ids = np.array(g["topk_ids"], np.int32)
+    counts, offsets, order, inv = oracle.permute_index(ids, g["E"])
+    assert counts.tolist() == g["derived"]["counts"]
+    assert offsets.tolist() == g["derived"]["offsets"]
+    assert order.tolist() == g["derived"]["order"]
+    assert inv.tolist() == g["derived"]["inv"]
+
+
+def _two_stage_order(ids: np.ndarray, E: int, n_ep: int):
+    """EP steps 2, 4 and 5 simulated with Python lists: every source stably
+    sorts its own assignments by expert, blocks travel source-major, and each
+    receiver stably sorts what it received by local expert."""
+    T, k = ids.shape
+    T_loc = T // n_ep
+    flat = ids.reshape(-1).tolist()
+    rank_of = lambda e: (e * n_ep) // E
+    sent = []
+    for s in range(n_ep):
+        mine = list(range(s * T_loc * k, (s + 1) * T_loc * k))
+        sent.append(sorted(mine, key=lambda a: flat[a]))
+    received = []
+    for q in range(n_ep):
+        got = [a for s in range(n_ep) for a in sent[s] if rank_of(flat[a]) == q]
+        received.append(sorted(got, key=lambda a: flat[a]))
+    return received
+
+
+def test_two_stage_ep_equals_global_order_hand():
+    g = _golden("hand_dispatch.json")
+    ids = np.array(g["topk_ids"], np.int32)
+    recv = _two_stage_order(ids, g["E"], g["n_ep"])
+    assert recv[1] == g["derived"]["gpu1_received_rows_in_expert_order"]
+    _, _, order, _ = oracle.permute_index(ids, g["E"])
+    assert sum(recv, []) == order.tolist()
+
+
+@pytest.mark.parametrize("T,k,E,n_ep", [(64, 2, 8, 4), (96, 3, 12, 4), (128, 8, 32, 8)])
+def test_two_stage_ep_equals_global_order_random(T, k, E, n_ep):
+    r = np.random.default_rng(T * 7 + k)
+    ids = np.stack([r.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    recv = _two_stage_order(ids, E, n_ep)
+    _, _, order, _ = oracle.permute_index(ids, E)
+    assert sum(recv, []) == order.tolist()
+    S = oracle.send_counts(ids, E, n_ep)
+    assert [len(x) for x in recv] == S.sum(axis=0).tolist()
+
+
+# --------------------------------------------------------------------------
+# EP, "Token permutation and grouped GEMMs": order, counts, offsets, inverse
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,E", [(0, 4), (1, 1), (37, 5), (4096, 256), (20000, 8)])
+def test_permute_matches_library_routines(M, E):
+    r = np.random.default_rng(M + E)
+    ids = r.integers(0, E, size=M).astype(np.int32)
+    if M > 100:
+        ids[: M // 3] = 0            # a hot expert
+        ids[ids == E - 1] = 0        # an empty expert
+    counts, offsets, order, inv = oracle.permute_index(ids, E)
+    assert np.array_equal(order, np.argsort(ids, kind="stable"))
+    assert np.array_equal(counts, np.bincount(ids, minlength=E))
+    assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+    assert np.array_equal(inv[order], np.arange(M))
+    assert np.array_equal(order[inv], np.arange(M))
+    assert counts.sum() == M
+
+
+def test_gather_rows_bitwise():
+    r = np.random.default_rng(3)
+    T, k, E, d = 33, 3, 5, 24
+    ids = np.stack([r.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    x = inputs.f32_to_bf16_bits(r.standard_normal((T, d), dtype=np.float32))
+    _, _, order, inv = oracle.permute_index(ids, E)
+    xp = oracle.gather_rows(x, order, k)
+    assert np.array_equal(xp, x[order // k])
+    xf = r.standard_normal((T, d), dtype=np.float32)
+    assert np.array_equal(oracle.gather_rows(xf, order, k).view(np.uint32), xf[order // k].view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# Send counts: stated invariants (EP, "A dispatch you can check by hand")
+# --------------------------------------------------------------------------
+
+def test_send_count_invariants_random():
+    r = np.random.default_rng(11)
+    T, k, E, n_ep = 8192, 8, 256, 64
+    ids = np.stack([r.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    S = oracle.send_counts(ids, E, n_ep)
+    assert (S.sum(axis=1) == k * T // n_ep).all()          # rows sum to k T_loc
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    per = E // n_ep
+    assert np.array_equal(S.sum(axis=0), counts.reshape(n_ep, per).sum(axis=1))  # columns = rank load
+    assert S.sum() == T * k
+    off = S.sum() - np.trace(S)
+    assert abs(off / S.sum() - (n_ep - 1) / n_ep) < 0.01   # "How many bytes move": (n-1)/n leave
+
+
+def test_per_token_bytes_closed_form():
+    """RM, "The all-to-all pattern": dispatch + combine = 2 top_k hidden bytes per token."""
+    g = _golden("closed_forms.json")["mixtral_per_token"]
+    r = np.random.default_rng(5)
+    T, E, n_ep = 512, 8, 8
+    ids = np.stack([r.choice(E, size=g["k"], replace=False) for _ in range(T)]).astype(np.int32)
+    S = oracle.send_counts(ids, E, n_ep)
+    per_token = 2 * S.sum() * g["d"] * g["bytes"] / T
+    assert per_token == g["printed_bytes"]
+
+
+def test_alltoall_bytes_worked_example():
+    """EP, "A worked example at DeepSeek-V3's shape": 693 MB, 13.9 ms / 4.3 ms, 2.9e12 FLOPs."""
+    g = _golden("closed_forms.json")["dsv3_alltoall"]
+    a = g["args"]
+    b = oracle.alltoall_bytes(a["T_loc"], a["k"], a["d"], a["n_ep"], a["s_disp"], a["s_comb"])
+    assert int(b / 1e6) == g["printed_MB"]          # 693.6 MB, printed as 693 MB
+    for bw, ms in g["printed_wire_ms"].items():
+        assert round(b / float(bw) * 1e3, 1) == ms
+    assert oracle.alltoall_bytes(a["T_loc"], a["k"], a["d"], a["n_ep"], a["s_disp"], a["s_comb"],
+                                 training=True) == 2 * b
+    # a single GPU (n_ep = 1) sends nothing; dispatch and combine precisions both count
+    assert oracle.alltoall_bytes(4096, 8, 7168, 1, 1, 2) == 0
+    assert oracle.alltoall_bytes(10, 1, 10, 2, 1, 0) == 50
+    assert oracle.alltoall_bytes(10, 1, 10, 2, 0, 1) == 50
+    flops = 4096 * 8 * 6 * 7168 * 2048
+    assert round(flops / 1e12, 1) == g["printed_flops"] / 1e12
+    assert round(flops / 989e12 * 1e3, 1) == g["printed_compute_ms_at_989e12"]
+
+
+def test_expert_parameter_count():
+    """EP, "DeepSeek-V3's layout, counted": one expert is 3 * 7168 * 2048 parameters."""
+    g = _golden("closed_forms.json")["dsv3_expert_params"]
+    cfg = inputs.CONFIGS["dsv3_prefill"]
+    w13_per, w2_per = 2 * cfg.ffn * cfg.d, cfg.d * cfg.ffn     # shapes gen_expert_weights returns
+    assert w13_per + w2_per == g["printed"]
+    small = inputs.MoeConfig("t", 1, T=4, E=3, k=1, d=8, ffn=16, dtype="bf16", gating="softmax")
+    w13, w2 = inputs.gen_expert_weights(small)
+    assert w13.shape == (3, 2, 16, 8) and w2.shape == (3, 8, 16)
+
+
+def test_tokens_per_expert_decode():
+    g = _golden("closed_forms.json")["routing_example_expected_tokens_per_expert"]
+    cfg = inputs.CONFIGS["dsv3_decode"]
+    assert (cfg.T, cfg.k, cfg.E) == (g["B"], g["k"], g["E"])
+    assert cfg.T * cfg.k // cfg.E == g["printed"]
+
+
+# --------------------------------------------------------------------------
+# Pinned sigmoid: against the fp64 definition, special values, symmetry
+# --------------------------------------------------------------------------
+
+def _ulp_dist(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in fp32 ulps between non-negative fp32 arrays."""
+    return np.abs(a.view(np.int32).astype(np.int64) - b.view(np.int32).astype(np.int64))
+
+
+def test_sigmoid_pinned_ulp_strided_enumeration():
+    lo = np.float32(-87.0).view(np.uint32)        # negative floats: larger bit pattern = more negative
+    hi = np.float32(88.0).view(np.uint32)
+    neg = np.arange(0x80000000, int(lo) + 1, 97, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    pos = np.arange(0, int(hi) + 1, 97, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    x = np.concatenate([neg, pos, np.float32([-87.0, 88.0, 0.0, -0.0, 1.0, -1.0, 1e-30, -1e-30])])
+    y = oracle.sigmoid_pinned(x)
+    ref = (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+    d = _ulp_dist(y, ref)
+    assert d.max() <= 2, (x[d.argmax()], y[d.argmax()], ref[d.argmax()])
+
+
+def test_sigmoid_pinned_special_values():
+    s = oracle.sigmoid_pinned
+    assert s(np.float32([0.0]))[0] == 0.5 and s(np.float32([-0.0]))[0] == 0.5
+    assert s(np.float32([200.0]))[0] == 1.0 and s(np.float32([np.inf]))[0] == 1.0
+    assert s(np.float32([-200.0]))[0] == 0.0 and s(np.float32([-np.inf]))[0] == 0.0
+    below = np.float32([-87.0001, -90.0, -100.0])
+    assert (s(below) == 0).all()                   # true value < 1.7e-38: outside the normal range
+    x = np.linspace(-20, 20, 200001, dtype=np.float32)
+    y = s(x)
+    assert (np.diff(y) >= 0).all()                 # monotone
+    sym = y.astype(np.float64) + s(-x).astype(np.float64)
+    assert np.abs(sym - 1.0).max() < 3e-7
+    assert s(np.float32([np.log(3.0)]))[0] == pytest.approx(0.75, rel=2e-7)
+
+
+# --------------------------------------------------------------------------
+# Route: brute force over subsets, library special cases, ties, gates
+# --------------------------------------------------------------------------
+
+def _brute_topk(key, cand, k):
+    """The k-subset whose members, listed best first by (key desc, id asc), is
+    lexicographically best; returned in that order."""
+    best = None
+    for comb in itertools.combinations(cand, k):
+        seq = sorted(comb, key=lambda e: (-key[e], e))
+        score = [(key[e], -e) for e in seq]
+        if best is None or score > best[0]:
+            best = (score, seq)
+    return best[1]
+
+
+def _brute_route(key, k, n_groups, topk_groups, aff):
+    E = len(key)
+    gs = E // n_groups
+    cand = list(range(E))
+    if n_groups > 1:
+        gscore = []
+        for g in range(n_groups):
+            a = sorted(aff[g * gs:(g + 1) * gs], reverse=True)
+            gscore.append(np.float32(a[0]) + np.float32(a[1]))
+        kept = _brute_topk(gscore, list(range(n_groups)), topk_groups)
+        cand = [e for e in range(E) if e // gs in kept]
+    return _brute_topk(key, cand, k)
+
+
+@pytest.mark.parametrize("E,k,n_groups,topk_groups,integer", [
+    (6, 1, 1, 1, False), (6, 3, 1, 1, False), (8, 2, 1, 1, True), (8, 3, 4, 2, False),
+    (12, 4, 4, 2, True), (12, 2, 3, 1, False), (16, 4, 8, 4, True), (9, 9, 1, 1, True)])
+def test_route_selection_bruteforce(E, k, n_groups, topk_groups, integer):
+    r = np.random.default_rng(E * 100 + k * 10 + n_groups)
+    T = 60
+    if integer:                                   # adversarial ties: integer logits in -2..2
+        logits = r.integers(-2, 3, size=(T, E)).astype(np.float32)
+    else:
+        logits = r.standard_normal((T, E), dtype=np.float32)
+    ids, _ = oracle.route(logits, k, "sigmoid", 1, n_groups, topk_groups)
+    aff = oracle.sigmoid_pinned(logits)
+    for t in range(T):
+        want = _brute_route(logits[t].tolist(), k, n_groups, topk_groups, aff[t].tolist())
+        assert ids[t].tolist() == want, (t, logits[t])
+
+
+def test_route_plain_equals_stable_argsort():
+    r = np.random.default_rng(2)
+    logits = r.standard_normal((1000, 256), dtype=np.float32)
+    logits[:, 7] = logits[:, 3]                   # planted equal keys
+    ref = np.argsort(-logits, axis=1, kind="stable")[:, :8]
+    for gating in ("softmax", "sigmoid"):
+        ids, _ = oracle.route(logits, 8, gating, 1, 1, 1)
+        assert np.array_equal(ids, ref)
+    # keeping every group is no limit at all
+    ids, _ = oracle.route(logits, 8, "sigmoid", 1, 8, 8)
+    assert np.array_equal(ids, ref)
+
+
+def test_route_group_limit_confines_choices():
+    r = np.random.default_rng(9)
+    logits = r.standard_normal((500, 256), dtype=np.float32)
+    ids, _ = oracle.route(logits, 8, "sigmoid", 1, 8, 4)
+    groups = ids // 32
+    assert max(len(set(g)) for g in groups.tolist()) <= 4
+    # the kept groups are the 4 best by the sum of their two highest affinities
+    aff = oracle.sigmoid_pinned(logits).reshape(500, 8, 32)
+    top2 = np.sort(aff, axis=2)[:, :, -2:]
+    gscore = top2[:, :, 1] + top2[:, :, 0]
+    kept = np.argsort(-gscore, axis=1, kind="stable")[:, :4]
+    for t in range(500):
+        assert set(groups[t].tolist()) <= set(kept[t].tolist())
+        allowed = np.concatenate([np.arange(g * 32, g * 32 + 32) for g in sorted(kept[t])])
+        best = allowed[np.argsort(-logits[t, allowed], kind="stable")[:8]]
+        assert ids[t].tolist() == best.tolist()
+
+
+def test_route_negative_zero_ties_lower_id():
+    logits = np.float32([[0.0, -0.0, -1.0, -0.0], [-0.0, 0.0, 0.0, -3.0]])
+    ids, _ = oracle.route(logits, 3, "softmax", 1)
+    assert ids.tolist() == [[0, 1, 3], [0, 1, 2]]
+
+
+def test_route_gates():
+    r = np.random.default_rng(4)
+    logits = r.standard_normal((300, 16), dtype=np.float32)
+    l64 = logits.astype(np.float64)
+    k = 4
+    # softmax renormalised == softmax over all E, then renormalised over the chosen
+    ids, w = oracle.route(logits, k, "softmax", 1)
+    p = np.exp(l64 - l64.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    pk = np.take_along_axis(p, ids, axis=1)
+    np.testing.assert_allclose(w, pk / pk.sum(axis=1, keepdims=True), rtol=1e-6)
+    np.testing.assert_allclose(w.sum(axis=1, dtype=np.float64), 1.0, rtol=1e-6)
+    assert (np.diff(w, axis=1) <= 0).all()        # slots are in descending gate order
+    ids2, w2 = oracle.route(logits, k, "softmax", 0)
+    assert np.array_equal(ids, ids2)
+    np.testing.assert_allclose(w2, pk, rtol=1e-6)
+    # sigmoid: gate = s(l) / sum over chosen, or s(l) itself
+    ids3, w3 = oracle.route(logits, k, "sigmoid", 1)
+    assert np.array_equal(ids, ids3)
+    s = 1.0 / (1.0 + np.exp(-np.take_along_axis(l64, ids3, axis=1)))
+    np.testing.assert_allclose(w3, s / s.sum(axis=1, keepdims=True), rtol=1e-6)
+    _, w4 = oracle.route(logits, k, "sigmoid", 0)
+    np.testing.assert_allclose(w4, s, rtol=1e-6)
+
+
+def test_route_rejects_bad_arguments():
+    logits = np.zeros((2, 8), np.float32)
+    for args in [(9, "softmax", 1, 1, 1), (2, "sigmoid", 1, 3, 1), (2, "sigmoid", 1, 4, 5),
+                 (8, "sigmoid", 1, 4, 1), (1, "sigmoid", 1, 8, 2)]:
+        with pytest.raises(ValueError):
+            oracle.route(logits, *args)
+
+
+# --------------------------------------------------------------------------
+# Expert MLP and combine: textbook dense forms, identities, dense-masked layer
+# --------------------------------------------------------------------------
+
+def _swiglu_dense(x, wg, wu, wd):
+    g = x @ wg.T
+    u = x @ wu.T
+    return ((g / (1.0 + np.exp(-g))) * u) @ wd.T
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_expert_rows_match_dense_swiglu(dtype):
+    cfg = inputs.MoeConfig("t", 1, T=10, E=3, k=1, d=32, ffn=48, dtype=dtype, gating="softmax",
+                           w_std=0.2)
+    w13, w2 = inputs.gen_expert_weights(cfg)
+    x = inputs.gen_x(cfg)
+    e = np.array([2, 0, 1, 1, 0, 2, 2, 0, 1, 0], np.int32)
+    y = oracle.expert_swiglu_rows(x, e, w13, w2)
+    f = (lambda a: a.astype(np.float64)) if dtype == "f32" else \
+        (lambda a: inputs.bf16_bits_to_f32(a).astype(np.float64).reshape(a.shape))
+    X, W13, W2 = f(x), f(w13), f(w2)
+    for r in range(10):
+        ref = _swiglu_dense(X[r:r + 1], W13[e[r], 0], W13[e[r], 1], W2[e[r]])[0]
+        np.testing.assert_allclose(y[r], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_expert_rows_scalar_closed_form():
+    """d = ffn = 1: y = w_down * SiLU(w_gate x) * (w_up x)."""
+    x = np.float32([[2.0]])
+    w13 = np.float32([[[[0.5]], [[3.0]]]])
+    w2 = np.float32([[[-1.5]]])
+    y = oracle.expert_swiglu_rows(x, np.int32([0]), w13, w2)[0, 0]
+    g, u = 1.0, 6.0
+    assert y == pytest.approx(-1.5 * (g / (1 + np.exp(-g))) * u, rel=1e-15)
+    # swapping the gate and up roles changes the answer
+    w13s = w13[:, ::-1].copy()
+    assert oracle.expert_swiglu_rows(x, np.int32([0]), w13s, w2)[0, 0] != pytest.approx(y)
+
+
+def test_unpermute_of_permute_is_identity():
+    r = np.random.default_rng(6)
+    T, E, d = 50, 6, 40
+    ids = r.integers(0, E, size=(T, 1)).astype(np.int32)
+    x = inputs.f32_to_bf16_bits(r.standard_normal((T, d), dtype=np.float32))
+    _, _, order, inv = oracle.permute_index(ids, E)
+    xp = oracle.gather_rows(x, order, 1)
+    y = oracle.combine(xp, inv, np.ones((T, 1), np.float32))
+    assert np.array_equal(y, inputs.bf16_bits_to_f32(x).reshape(T, d).astype(np.float64))
+    # k copies with gates summing to one return the token itself (identical experts)
+    k = 3
+    ids3 = np.stack([r.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    _, _, order3, inv3 = oracle.permute_index(ids3, E)
+    xf = r.standard_normal((T, d), dtype=np.float32)
+    w = np.float32([[0.5, 0.25, 0.25]]).repeat(T, axis=0)
+    y3 = oracle.combine(oracle.gather_rows(xf, order3, k), inv3, w)
+    np.testing.assert_allclose(y3, xf.astype(np.float64), rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("gating,n_groups,topk_groups,shared", [
+    ("softmax", 1, 1, False), ("sigmoid", 4, 2, True)])
+def test_sparse_layer_equals_dense_masked(gating, n_groups, topk_groups, shared):
+    """EP, "Expert parallelism": on one device an MoE layer is a gather, some
+    matrix products and a scatter.  The sparse path (route, permute, experts on
+    packed rows, combine) equals evaluating every expert on every token and
+    masking with the gate."""
+    cfg = inputs.MoeConfig("t", 1, T=16, E=8, k=2, d=16, ffn=24, dtype="f32", gating=gating,
+                           n_groups=n_groups, topk_groups=topk_groups, shared=shared, w_std=0.3)
+    logits = inputs.gen_logits(cfg)
+    x = inputs.gen_x(cfg)
+    w13, w2 = inputs.gen_expert_weights(cfg)
+    ids, w = oracle.route(logits, cfg.k, gating, 1, n_groups, topk_groups)
+    counts, offsets, order, inv = oracle.permute_index(ids, cfg.E)
+    xp = oracle.gather_rows(x, order, cfg.k)
+    expert_of_row = np.repeat(np.arange(cfg.E, dtype=np.int32), counts)
+    yp = oracle.expert_swiglu_rows(xp, expert_of_row, w13, w2)
+    y_sh = None
+    if shared:
+        s13, s2 = inputs.gen_expert_weights(cfg, shared=True)
+        y_sh = oracle.expert_swiglu_rows(x, np.zeros(cfg.T, np.int32), s13, s2)
+    y = oracle.combine(yp, inv, w, y_sh)
+
+    X = x.astype(np.float64)
+    mask = np.zeros((cfg.T, cfg.E))
+    np.put_along_axis(mask, ids, w.astype(np.float64), axis=1)
+    dense = np.zeros((cfg.T, cfg.d))
+    for e in range(cfg.E):
+        fe = _swiglu_dense(X, w13[e, 0].astype(np.float64), w13[e, 1].astype(np.float64),
+                           w2[e].astype(np.float64))
+        dense += mask[:, e:e + 1] * fe
+    if shared:
+        dense += _swiglu_dense(X, s13[0, 0].astype(np.float64), s13[0, 1].astype(np.float64),
+                               s2[0].astype(np.float64))
+    np.testing.assert_allclose(y, dense, rtol=1e-11, atol=1e-13)
+    # the token-sample composition used for large workloads gives the same rows
+    tok = np.array([0, 5, 15])
+    yt = oracle.layer_tokens(x, ids, w, w13, w2, tok, *( (s13, s2) if shared else (None, None)))
+    np.testing.assert_allclose(yt, dense[tok], rtol=1e-11, atol=1e-13)
