@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Throughput of one MoE layer forward on one MI355X.
+
+A step is one pass of the whole hot path over one batch: route (top-k
+gating), send counts, permute, grouped SwiGLU experts (routed, then the
+shared expert), unpermute + gate-weighted combine.  Inputs and weights are
+resident in HBM before the timed region.  The default workload is the
+DeepSeek-V3-shaped prefill layer: T = 8192 tokens, d = 7168, 256 routed
+experts (ffn 2048) + 1 shared, group-limited sigmoid routing (8 groups of 32,
+top-4 groups, top-8), send counts for a simulated 64-way EP group.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "MoE-layer fwd tokens/s at DSV3 shape, 1 GPU; % MFMA peak; permute % HBM BW"
+PEAK_MFMA = {"bf16": 2.5e15, "f32": 157.3e12}     # dense, MI355X published
+PEAK_HBM = 8.0e12
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def stage_bytes(cfg):
+    """Algorithmic HBM bytes of the permute and combine stages (per layer)."""
+    s = cfg.elem_bytes
+    T, k, d = cfg.T, cfg.k, cfg.d
+    permute = T * (d * s + k * d * s + 12 * k)     # read x once, write k copies, ids/order/inv
+    combine = T * (k * d * s + d * s + 8 * k + (d * s if cfg.shared else 0))
+    return permute, combine
+
+
+def expert_flops(cfg):
+    routed = 6 * cfg.T * cfg.k * cfg.d * cfg.ffn
+    shared = 6 * cfg.T * cfg.d * cfg.ffn if cfg.shared else 0
+    return routed, shared
+
+
+def cpu_baseline(cfg, data, budget_s=12.0, max_tokens=256):
+    """The oracle, untuned, on the host cores: route, send counts and permute on
+    every token, then experts and combine on seeded tokens until about budget_s
+    has passed; per-token costs extrapolated to the full batch."""
+    import numpy as np
+
+    import oracle
+    from token_routing_expert_amd import inputs
+
+    x, w13, w2, logits, sh, ids_in, w_in = data
+    t0 = time.perf_counter()
+    if cfg.gating == "given":
+        ids, w = ids_in, w_in
+    else:
+        ids, w = oracle.route(logits, cfg.k, cfg.gating, cfg.renormalize, cfg.n_groups,
+                              cfg.topk_groups)
+    if cfg.n_ep:
+        oracle.send_counts(ids, cfg.E, cfg.n_ep)
+    _, _, order, _ = oracle.permute_index(ids, cfg.E)
+    oracle.gather_rows(x, order, cfg.k)
+    t_index = time.perf_counter() - t0
+    sample = inputs.sample_tokens(cfg, max_tokens)
+    done, t_exp = 0, 0.0
+    while done < len(sample) and t_exp < budget_s:
+        batch = sample[done:done + 16]
+        t1 = time.perf_counter()
+        oracle.layer_tokens(x, ids, w, w13, w2, batch, *sh)
+        t_exp += time.perf_counter() - t1
+        done += len(batch)
+    per_token = t_index / cfg.T + t_exp / done
+    return {
+        "value": 1.0 / per_token,
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"route, send counts, permute and row gather on all {cfg.T} tokens "
+                   f"({t_index:.2f} s) + experts and combine on {done} seeded tokens "
+                   f"({t_exp:.2f} s); per-token costs extrapolated to {cfg.T} tokens"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the path is one GPU's share of the EP layer and "
+              "this build has no cross-GPU exchange. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from token_routing_expert_amd import inputs, load_library
+    from token_routing_expert_amd.layer import MoeLayer
+
+    load_library()
+    cfg = inputs.CONFIGS[args.workload]
+    log(f"workload {cfg.name}: generating inputs")
+    t0 = time.perf_counter()
+    x = inputs.gen_x(cfg)
+    w13, w2 = inputs.gen_expert_weights(cfg)
+    sh = inputs.gen_expert_weights(cfg, shared=True) if cfg.shared else (None, None)
+    if cfg.gating == "given":
+        logits = None
+        ids_in, w_in = inputs.gen_ep_share_routing(cfg)
+    else:
+        logits = inputs.gen_logits(cfg)
+        ids_in = w_in = None
+    log(f"generated in {time.perf_counter() - t0:.1f} s; uploading")
+    layer = MoeLayer(cfg, x, w13, w2, logits=logits, sh_w13=sh[0], sh_w2=sh[1],
+                     topk_ids=ids_in, topk_w=w_in)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    stages = ["route", "permute", "experts_routed", "experts_shared", "combine"]
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        for i, name in enumerate(stages):
+            getattr(layer, name)()
+            if evs is not None:
+                evs[i + 1].record(stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = wall * 1e3 / K
+    stage_ms = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K
+                for j, name in enumerate(stages)}
+
+    routed_flops, shared_flops = expert_flops(cfg)
+    peak = PEAK_MFMA[cfg.dtype]
+    gemm_ms = stage_ms["experts_routed"]
+    achieved = routed_flops / (gemm_ms * 1e-3)
+    b_perm, b_comb = stage_bytes(cfg)
+    stage_info = {}
+    for name in stages:
+        ms = stage_ms[name]
+        info = {"ms": round(ms, 4)}
+        if name == "permute":
+            info.update(bytes=b_perm, GBps=round(b_perm / ms / 1e6, 1),
+                        hbm_frac=round(b_perm / (ms * 1e-3) / PEAK_HBM, 4))
+        if name == "combine":
+            info.update(bytes=b_comb, GBps=round(b_comb / ms / 1e6, 1),
+                        hbm_frac=round(b_comb / (ms * 1e-3) / PEAK_HBM, 4))
+        if name == "experts_routed":
+            info.update(flops=routed_flops, TFLOPs=round(achieved / 1e12, 1),
+                        mfma_frac=round(achieved / peak, 4))
+        if name == "experts_shared" and shared_flops:
+            sa = shared_flops / (ms * 1e-3)
+            info.update(flops=shared_flops, TFLOPs=round(sa / 1e12, 1), mfma_frac=round(sa / peak, 4))
+        stage_info[name] = info
+
+    result = {
+        "metric": METRIC,
+        "value": cfg.T / (ms_step * 1e-3),
+        "unit": "tokens/s" if cfg.gating != "given" else "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded numpy draws; random-init weights of the stated shapes)",
+        "config": {
+            "workload": cfg.name, "T": cfg.T, "E": cfg.E, "k": cfg.k, "d": cfg.d, "ffn": cfg.ffn,
+            "gating": cfg.gating, "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups,
+            "shared_experts": int(cfg.shared), "n_ep_simulated": cfg.n_ep,
+        },
+        "roofline": {
+            "kernel": "moe_grouped_swiglu, routed experts (gate/up launch + down launch)",
+            "bound": "mfma",
+            "achieved": round(achieved / 1e12, 2),
+            "peak": peak / 1e12,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+        },
+        "stages": stage_info,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(cfg, (x, w13, w2, logits, sh, ids_in, w_in))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+/*
+ * libmoe355 -- one GPU's hot path of an expert-parallel MoE layer forward,
+ * hand-written HIP for gfx950 (MI355X).
+ *
+ * The path follows the numbered forward-pass steps of the textbook section
+ * "Expert parallelism" (zerotofrontier.app/moe/expert-parallel): route (step 1),
+ * permute and count by destination (step 2), expert compute as one grouped
+ * matrix product (step 5), unpermute and weight (step 7).  The cross-GPU
+ * exchanges (steps 3, 4, 6) are not here; moe_send_counts gives the matrix of
+ * rows each simulated rank would send to each other rank.
+ *
+ * Conventions for every call:
+ *  - Every pointer is a DEVICE pointer (hipMalloc'd or equivalent) unless
+ *    stated; every call is asynchronous on `stream` (NULL = the null stream)
+ *    and performs no device-to-host synchronisation.
+ *  - The caller owns every buffer, including scratch.  The library never
+ *    allocates device memory and keeps no state between calls; calls are
+ *    reentrant and may run concurrently on different streams when their
+ *    buffers do not overlap.
+ *  - Outputs are fully overwritten.  Inputs are not modified.  Inputs and
+ *    outputs must not alias.
+ *  - Results are deterministic: the same inputs give the same output bits.
+ *  - Host-side validation happens before any launch; on error nothing is
+ *    launched.  T == 0 (or M == 0) returns MOE_OK and launches nothing,
+ *    except where a call states otherwise.
+ *  - Row-major layouts; all row strides are dense.  Device pointers to
+ *    activations and weights must be 16-byte aligned.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef MOE355_H
+#define MOE355_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,   /* null pointer, bad size, misalignment, workspace too small */
+    MOE_ERR_UNSUPPORTED = -2,   /* a shape or option outside what the kernels implement */
+    MOE_ERR_HIP = -3            /* the HIP runtime reported an error at launch */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_gating;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *moe_status_string(moe_status s);
+
+/*
+ * Route: top-k experts and gates per token (step 1 of the forward pass;
+ * "05 - Expert Parallelism (MoE)", section "The all-to-all pattern"; the
+ * group limit is DeepSeek-V3's node-limited routing, "What DeepSeek-V3 did
+ * about it").
+ *
+ *   logits    [T, E] fp32, the router output for each token.
+ *   k         experts per token, 1 <= k <= min(E, 16).
+ *   gating    MOE_SOFTMAX or MOE_SIGMOID.
+ *   renormalize  1: gates normalised over the k chosen experts
+ *                   (softmax: exp(l_j - l_0) / sum_i exp(l_i - l_0);
+ *                    sigmoid: s(l_j) / sum_i s(l_i));
+ *                0: softmax over all E experts, or the bare sigmoid.
+ *   n_groups, topk_groups  group limit: the E experts form n_groups
+ *                contiguous groups; each group scores the fp32 sum of its two
+ *                largest sigmoid affinities; only experts of the topk_groups
+ *                best groups may be chosen.  1, 1 = no limit.
+ *   topk_ids  [T, k] int32 out: slot 0 is the best expert.
+ *   topk_w    [T, k] fp32 out: the gates.
+ *
+ * Selection ranks experts by their fp32 logit (-0 counts as +0), ties to the
+ * lower expert id; group ties go to the lower group id.  The sigmoid used for
+ * group scores is the pinned fp32 function of moe_sigmoid_pinned, so group
+ * choices are reproducible bit for bit.  NaN logits are outside the contract.
+ * Errors: INVALID_ARG for null pointers, T < 0, k outside [1, E], E % n_groups,
+ * topk_groups outside [1, n_groups], a group of fewer than 2 experts, or
+ * topk_groups * (E / n_groups) < k; UNSUPPORTED for E > 1024, k > 16,
+ * n_groups > 64.
+ */
+moe_status moe_route_topk(const float *logits, int T, int E, int k, moe_gating gating,
+                          int renormalize, int n_groups, int topk_groups, int32_t *topk_ids,
+                          float *topk_w, hipStream_t stream);
+
+/*
+ * The pinned fp32 sigmoid applied elementwise: y[i] = s(x[i]), n elements.
+ * s(x) = 1/(1+t) for x >= 0 and t/(1+t) otherwise, t = exp(-|x|), where exp
+ * is Cody & Waite reduction (ln2 split into a 12-significant-bit head and a
+ * tail) and a degree-7 Taylor polynomial in fp32 fmaf, scaled by 2^n; inputs
+ * below -87 give 0.  Exposed so the group scores of moe_route_topk can be
+ * checked bit for bit.  Errors: INVALID_ARG for null pointers or n < 0.
+ */
+moe_status moe_sigmoid_pinned(const float *x, float *y, int64_t n, hipStream_t stream);
+
+/*
+ * Send-count matrix (step 2; "A dispatch you can check by hand"): entry
+ * (s, q) = number of assignments of source rank s's tokens whose expert lives
+ * on rank q.  Token t belongs to rank floor(t / (T / n_ep)); expert e lives on
+ * rank floor(e * n_ep / E).  Each row sums to k T / n_ep.
+ *
+ *   topk_ids     [T, k] int32, values in [0, E).
+ *   send_counts  [n_ep, n_ep] int32 out, row = source rank.
+ * T = 0 writes an all-zero matrix.
+ * Errors: INVALID_ARG for null pointers, n_ep < 1, T % n_ep or E % n_ep != 0;
+ * UNSUPPORTED for n_ep > 1024.
+ */
+moe_status moe_send_counts(const int32_t *topk_ids, int T, int k, int E, int n_ep,
+                           int32_t *send_counts, hipStream_t stream);
+
+/*
+ * Bytes of device scratch moe_permute needs for M = T k assignments over E
+ * experts (per-chunk histograms).  Host function, no device work.
+ */
+size_t moe_permute_workspace_bytes(int T, int k, int E);
+
+/*
+ * Permute (step 2 and step 5's sort by local expert; "Token permutation and
+ * grouped GEMMs"): order is the stable argsort of the expert ids of the M = T k
+ * assignments (assignment a = t k + j), counts the per-expert histogram,
+ * offsets its exclusive prefix sum, inv the inverse permutation
+ * (inv[order[p]] = p), and x_perm = X[order]: packed row p is a bit copy of
+ * token order[p] / k.  Rows of one expert are contiguous in x_perm, in token
+ * order.
+ *
+ *   x          [T, d] activations, dtype dt.
+ *   topk_ids   [T, k] int32, values in [0, E).  An id outside [0, E) breaks
+ *              the permutation; the kernels never write out of bounds for it
+ *              but leave the affected outputs undefined.
+ *   counts     [E] int32 out;  offsets [E+1] int32 out (offsets[E] = M).
+ *   order, inv [M] int32 out.
+ *   x_perm     [M, d] out, dtype dt.
+ *   workspace  at least moe_permute_workspace_bytes(T, k, E) bytes of device
+ *              scratch owned by the caller; its contents on entry do not matter.
+ * Errors: INVALID_ARG for null pointers, T < 0, k < 1, E < 1, workspace too
+ * small, misaligned x / x_perm; UNSUPPORTED for E > 1024, d % 8 != 0, or
+ * T k >= 2^31.
+ */
+moe_status moe_permute(const void *x, moe_dtype dt, int T, int d, const int32_t *topk_ids,
+                       int k, int E, int32_t *counts, int32_t *offsets, int32_t *order,
+                       int32_t *inv, void *x_perm, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
+ * Grouped SwiGLU expert MLP (step 5; "Token permutation and grouped GEMMs":
+ * one launch computes the products of all experts' row segments, scheduling
+ * output tiles from all of them, with no padding beyond the tile and nothing
+ * dropped).  For each expert g and each packed row p in
+ * [offsets[g], offsets[g+1]):
+ *     h[p] = SiLU(a[p] W_gate,g^T) * (a[p] W_up,g^T),   y[p] = h[p] W_down,g^T,
+ * SiLU(z) = z / (1 + exp(-z)); 6 d ffn FLOPs per row ("A worked example at
+ * DeepSeek-V3's shape").
+ *
+ *   a        [M, d] packed rows, dtype dt.
+ *   offsets  [G+1] int32 device array, non-decreasing, offsets[0] = 0,
+ *            offsets[G] = M.  Row segments may be empty.
+ *   w13      [G, 2, ffn, d]: per expert the gate matrix then the up matrix,
+ *            each row an output feature with d contiguous inputs.
+ *   w2       [G, d, ffn]: the down matrix, ffn contiguous inputs per row.
+ *   h        [M, ffn] caller scratch, dtype dt; holds the SwiGLU activations
+ *            on return.
+ *   y        [M, d] out, dtype dt.
+ * Accumulation is fp32; bf16 outputs are rounded to nearest even.  A single
+ * always-active shared expert is the same call with G = 1 and offsets {0, M}
+ * ("Fine-grained vs coarse experts").
+ * Errors: INVALID_ARG for null pointers, M < 0, G < 1, misalignment;
+ * UNSUPPORTED for d or ffn not a multiple of 128, G > 4096, M >= 2^31.
+ * An offsets array that breaks its precondition is clamped to [0, M] and
+ * never causes an out-of-bounds access.
+ */
+moe_status moe_grouped_swiglu(const void *a, moe_dtype dt, int M, int d, int ffn,
+                              const int32_t *offsets, int G, const void *w13, const void *w2,
+                              void *h, void *y, hipStream_t stream);
+
+/*
+ * Unpermute and weight (step 7; "Token permutation and grouped GEMMs":
+ * Y_sorted[inv] restores the token order): for each token t,
+ *     y[t] = sum_{j<k} topk_w[t, j] * y_perm[inv[t k + j]]  (+ y_shared[t]),
+ * summed in fp32 in slot order, the shared row last with weight 1.
+ *
+ *   y_perm    [T k, d] expert outputs in packed (expert) order, dtype dt.
+ *   inv       [T k] int32 from moe_permute.  Entries outside [0, T k) are
+ *             skipped (contribute nothing).
+ *   topk_w    [T, k] fp32 gates.
+ *   y_shared  [T, d] dtype dt, or NULL for none.
+ *   y         [T, d] out, dtype dt.
+ * Errors: INVALID_ARG for null required pointers, T < 0, k < 1, misalignment;
+ * UNSUPPORTED for d % 8 != 0, k > 64, T k >= 2^31.
+ */
+moe_status moe_unpermute_combine(const void *y_perm, moe_dtype dt, int T, int k, int d,
+                                 const int32_t *inv, const float *topk_w, const void *y_shared,
+                                 void *y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE355_H */

@@ -60,6 +60,7 @@ def _load():
     lib.orc_combine.argtypes = [P, i32, i64, i32, i32, P, P, P, i32, P]
     lib.orc_alltoall_bytes.argtypes = [i64, i32, i64, i32, f64, f64, i32]
     lib.orc_alltoall_bytes.restype = f64
+    lib.orc_num_threads.restype = i32
     _lib = lib
     return lib
 
@@ -80,6 +81,11 @@ def _dtype_code(a: np.ndarray) -> int:
     if a.dtype == np.float64:
         return F64
     raise TypeError(f"unsupported oracle dtype {a.dtype}")
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().orc_num_threads())
 
 
 def sigmoid_pinned(x: np.ndarray) -> np.ndarray:

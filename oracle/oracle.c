@@ -333,3 +333,11 @@ double orc_alltoall_bytes(int64_t T_loc, int k, int64_t d, int n_ep, double s_di
     double b = per * s_disp + per * s_comb;
     return training ? 2.0 * b : b;
 }
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+#ifdef _OPENMP
+#include <omp.h>
+int orc_num_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_num_threads(void) { return 1; }
+#endif

@@ -1,0 +1,121 @@
+"""The C-ABI library loads and exports every entry point include/moe355.h
+declares; host-side argument validation rejects bad calls before any launch.
+CPU only: nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_routing_expert_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe355.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.skip("libmoe355.so not built (run __graft_entry__.build())")
+    return moe.load_library()
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(moe.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3):
+        s = lib.moe_status_string(code).decode()
+        assert s.startswith("MOE_")
+    assert lib.moe_status_string(7).decode() == "unknown moe_status"
+
+
+def test_workspace_bytes(lib):
+    assert lib.moe_permute_workspace_bytes(8192, 8, 256) == 32 * 256 * 4     # 2048-row chunks
+    assert lib.moe_permute_workspace_bytes(1, 1, 4) == 4 * 4
+    assert lib.moe_permute_workspace_bytes(0, 8, 256) == 16
+    big = lib.moe_permute_workspace_bytes(1 << 22, 8, 1024)
+    assert big <= 1024 * 1024 * 4                                           # at most 1024 chunks
+
+
+INVALID, UNSUPPORTED = -1, -2
+NULL = None
+
+
+def test_route_validation(lib):
+    f = lib.moe_route_topk
+    assert f(NULL, -1, 8, 2, 0, 1, 1, 1, NULL, NULL, NULL) == INVALID        # T < 0
+    assert f(NULL, 4, 8, 9, 0, 1, 1, 1, NULL, NULL, NULL) == INVALID         # k > E
+    assert f(NULL, 4, 8, 0, 0, 1, 1, 1, NULL, NULL, NULL) == INVALID         # k < 1
+    assert f(NULL, 4, 8, 2, 0, 1, 3, 1, NULL, NULL, NULL) == INVALID         # E % n_groups
+    assert f(NULL, 4, 8, 2, 1, 1, 4, 5, NULL, NULL, NULL) == INVALID         # topk_groups > n_groups
+    assert f(NULL, 4, 8, 2, 1, 1, 8, 1, NULL, NULL, NULL) == INVALID         # group of one expert
+    assert f(NULL, 4, 8, 8, 1, 1, 4, 1, NULL, NULL, NULL) == INVALID         # kept groups too few
+    assert f(NULL, 4, 8, 2, 5, 1, 1, 1, NULL, NULL, NULL) == INVALID         # bad gating
+    assert f(NULL, 4, 2048, 2, 0, 1, 1, 1, NULL, NULL, NULL) == UNSUPPORTED  # E > 1024
+    assert f(NULL, 4, 64, 17, 0, 1, 1, 1, NULL, NULL, NULL) == UNSUPPORTED   # k > 16
+    assert f(NULL, 4, 8, 2, 0, 1, 1, 1, NULL, NULL, NULL) == INVALID         # null pointers
+    assert f(NULL, 0, 8, 2, 0, 1, 1, 1, NULL, NULL, NULL) == 0               # T = 0: no-op
+
+
+def test_send_counts_validation(lib):
+    f = lib.moe_send_counts
+    assert f(NULL, 6, 2, 4, 4, NULL, NULL) == INVALID                        # T % n_ep
+    assert f(NULL, 8, 2, 6, 4, NULL, NULL) == INVALID                        # E % n_ep
+    assert f(NULL, 8, 2, 8, 0, NULL, NULL) == INVALID
+    assert f(NULL, 4096, 1, 2048, 2048, NULL, NULL) == UNSUPPORTED
+    assert f(NULL, 8, 2, 8, 4, NULL, NULL) == INVALID                        # null pointers
+
+
+def test_permute_validation(lib):
+    f = lib.moe_permute
+    a = ctypes.c_void_p(16)     # a well-aligned non-null value; never dereferenced on error paths
+    b = ctypes.c_void_p(24)     # misaligned
+    ws = lib.moe_permute_workspace_bytes(4, 2, 8)
+    assert f(a, 1, 4, 12, a, 2, 8, a, a, a, a, a, a, ws, NULL) == UNSUPPORTED   # d % 8
+    assert f(a, 1, 4, 16, a, 2, 2000, a, a, a, a, a, a, ws, NULL) == UNSUPPORTED  # E > 1024
+    assert f(a, 1, 4, 16, a, 2, 8, a, a, a, a, a, a, ws - 1, NULL) == INVALID   # workspace
+    assert f(b, 1, 4, 16, a, 2, 8, a, a, a, a, a, a, ws, NULL) == INVALID       # misaligned x
+    assert f(a, 1, 4, 16, NULL, 2, 8, a, a, a, a, a, a, ws, NULL) == INVALID    # null ids
+    assert f(a, 7, 4, 16, a, 2, 8, a, a, a, a, a, a, ws, NULL) == INVALID       # dtype
+    assert f(a, 1, -1, 16, a, 2, 8, a, a, a, a, a, a, ws, NULL) == INVALID
+
+
+def test_grouped_swiglu_validation(lib):
+    f = lib.moe_grouped_swiglu
+    a = ctypes.c_void_p(16)
+    assert f(a, 1, 64, 96, 256, a, 4, a, a, a, a, NULL) == UNSUPPORTED      # d % 128
+    assert f(a, 1, 64, 128, 200, a, 4, a, a, a, a, NULL) == UNSUPPORTED     # ffn % 128
+    assert f(a, 1, 64, 128, 256, a, 5000, a, a, a, a, NULL) == UNSUPPORTED  # G > 4096
+    assert f(a, 1, 64, 128, 256, a, 0, a, a, a, a, NULL) == INVALID         # G < 1
+    assert f(a, 1, 64, 128, 256, NULL, 4, a, a, a, a, NULL) == INVALID      # null offsets
+    assert f(ctypes.c_void_p(8), 1, 64, 128, 256, a, 4, a, a, a, a, NULL) == INVALID
+    assert f(a, 1, 0, 128, 256, NULL, 4, NULL, NULL, NULL, NULL, NULL) == 0  # M = 0: no-op
+
+
+def test_combine_validation(lib):
+    f = lib.moe_unpermute_combine
+    a = ctypes.c_void_p(16)
+    assert f(a, 1, 4, 2, 12, a, a, NULL, a, NULL) == UNSUPPORTED            # d % 8
+    assert f(a, 1, 4, 65, 16, a, a, NULL, a, NULL) == UNSUPPORTED           # k > 64
+    assert f(a, 1, 4, 0, 16, a, a, NULL, a, NULL) == INVALID
+    assert f(a, 1, 4, 2, 16, NULL, a, NULL, a, NULL) == INVALID
+    assert f(a, 1, 4, 2, 16, a, a, ctypes.c_void_p(40), a, NULL) == INVALID  # misaligned shared
+    assert f(a, 1, 0, 2, 16, NULL, NULL, NULL, NULL, NULL) == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(moe.MoeError):
+        moe.load_library(str(tmp_path / "missing.so"))

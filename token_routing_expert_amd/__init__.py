@@ -1,0 +1,212 @@
+"""Python binding of libmoe355: argument marshalling only.
+
+Each function has the name of the C entry point it calls (include/moe355.h),
+takes torch CUDA tensors, passes their device pointers and the current HIP
+stream, and raises ``MoeError`` on a non-zero status.  Every step of the path
+runs in the library's HIP kernels; PyTorch only supplies device memory (output
+tensors are allocated with ``torch.empty`` when not given) and the stream.
+There is no fallback: if libmoe355.so is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmoe355.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+
+# Every symbol include/moe355.h declares.
+EXPORTS = ("moe_status_string", "moe_route_topk", "moe_sigmoid_pinned", "moe_send_counts",
+           "moe_permute_workspace_bytes", "moe_permute", "moe_grouped_swiglu",
+           "moe_unpermute_combine")
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmoe355.so and declare the C signatures.  Raises if it is not built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise MoeError(f"{path} is not built; run `python -m token_routing_expert_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.moe_status_string.argtypes = [i32]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_route_topk.argtypes = [P, i32, i32, i32, i32, i32, i32, i32, P, P, P]
+    lib.moe_sigmoid_pinned.argtypes = [P, P, i64, P]
+    lib.moe_send_counts.argtypes = [P, i32, i32, i32, i32, P, P]
+    lib.moe_permute_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.moe_permute_workspace_bytes.restype = sz
+    lib.moe_permute.argtypes = [P, i32, i32, i32, P, i32, i32, P, P, P, P, P, P, sz, P]
+    lib.moe_grouped_swiglu.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P, P, P]
+    lib.moe_unpermute_combine.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P]
+    for name in ("moe_route_topk", "moe_sigmoid_pinned", "moe_send_counts", "moe_permute",
+                 "moe_grouped_swiglu", "moe_unpermute_combine"):
+        getattr(lib, name).restype = i32
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = load_library().moe_status_string(rc).decode()
+        raise MoeError(f"{what}: {msg}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _dev(t, name, dtypes):
+    if not t.is_cuda:
+        raise MoeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise MoeError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise MoeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    return MOE_BF16 if t.dtype == torch.bfloat16 else MOE_F32
+
+
+def _act_dtypes():
+    torch = _torch()
+    return (torch.float32, torch.bfloat16)
+
+
+def moe_sigmoid_pinned(x, y=None, stream=None):
+    torch = _torch()
+    _dev(x, "x", (torch.float32,))
+    y = torch.empty_like(x) if y is None else _dev(y, "y", (torch.float32,))
+    _check(load_library().moe_sigmoid_pinned(_ptr(x), _ptr(y), x.numel(), _stream(stream)),
+           "moe_sigmoid_pinned")
+    return y
+
+
+def moe_route_topk(logits, k, gating="softmax", renormalize=True, n_groups=1, topk_groups=1,
+                   topk_ids=None, topk_w=None, stream=None):
+    """Top-k ids [T,k] int32 and gates [T,k] fp32 from fp32 logits [T,E]."""
+    torch = _torch()
+    _dev(logits, "logits", (torch.float32,))
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _dev(topk_ids, "topk_ids", (torch.int32,))
+    _dev(topk_w, "topk_w", (torch.float32,))
+    g = MOE_SOFTMAX if gating == "softmax" else MOE_SIGMOID if gating == "sigmoid" else -1
+    _check(load_library().moe_route_topk(_ptr(logits), T, E, k, g, int(bool(renormalize)),
+                                         n_groups, topk_groups, _ptr(topk_ids), _ptr(topk_w),
+                                         _stream(stream)), "moe_route_topk")
+    return topk_ids, topk_w
+
+
+def moe_send_counts(topk_ids, E, n_ep, send_counts=None, stream=None):
+    """Send-count matrix [n_ep, n_ep] int32 (row = source rank)."""
+    torch = _torch()
+    _dev(topk_ids, "topk_ids", (torch.int32,))
+    T, k = topk_ids.shape
+    if send_counts is None:
+        send_counts = torch.empty((n_ep, n_ep), dtype=torch.int32, device=topk_ids.device)
+    _dev(send_counts, "send_counts", (torch.int32,))
+    _check(load_library().moe_send_counts(_ptr(topk_ids), T, k, E, n_ep, _ptr(send_counts),
+                                          _stream(stream)), "moe_send_counts")
+    return send_counts
+
+
+def moe_permute_workspace_bytes(T, k, E) -> int:
+    return int(load_library().moe_permute_workspace_bytes(T, k, E))
+
+
+def moe_permute(x, topk_ids, E, counts=None, offsets=None, order=None, inv=None, x_perm=None,
+                workspace=None, stream=None):
+    """Returns (counts [E], offsets [E+1], order [Tk], inv [Tk], x_perm [Tk, d])."""
+    torch = _torch()
+    _dev(x, "x", _act_dtypes())
+    _dev(topk_ids, "topk_ids", (torch.int32,))
+    T, d = x.shape
+    k = topk_ids.shape[1]
+    dev = x.device
+    M = T * k
+    i32 = torch.int32
+    counts = torch.empty(E, dtype=i32, device=dev) if counts is None else counts
+    offsets = torch.empty(E + 1, dtype=i32, device=dev) if offsets is None else offsets
+    order = torch.empty(M, dtype=i32, device=dev) if order is None else order
+    inv = torch.empty(M, dtype=i32, device=dev) if inv is None else inv
+    x_perm = torch.empty((M, d), dtype=x.dtype, device=dev) if x_perm is None else x_perm
+    nbytes = moe_permute_workspace_bytes(T, k, E)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    for name, t in (("counts", counts), ("offsets", offsets), ("order", order), ("inv", inv)):
+        _dev(t, name, (i32,))
+    _dev(x_perm, "x_perm", (x.dtype,))
+    _check(load_library().moe_permute(
+        _ptr(x), _dtype_code(x), T, d, _ptr(topk_ids), k, E, _ptr(counts), _ptr(offsets),
+        _ptr(order), _ptr(inv), _ptr(x_perm), _ptr(workspace), workspace.numel(),
+        _stream(stream)), "moe_permute")
+    return counts, offsets, order, inv, x_perm
+
+
+def moe_grouped_swiglu(a, offsets, w13, w2, h=None, y=None, stream=None):
+    """y [M, d] = per-segment SwiGLU experts of the packed rows a [M, d]; h is scratch."""
+    torch = _torch()
+    _dev(a, "a", _act_dtypes())
+    _dev(offsets, "offsets", (torch.int32,))
+    _dev(w13, "w13", (a.dtype,))
+    _dev(w2, "w2", (a.dtype,))
+    M, d = a.shape
+    G, two, ffn, d2 = w13.shape
+    if two != 2 or d2 != d or tuple(w2.shape) != (G, d, ffn) or offsets.numel() != G + 1:
+        raise MoeError("moe_grouped_swiglu: inconsistent shapes")
+    h = torch.empty((M, ffn), dtype=a.dtype, device=a.device) if h is None else h
+    y = torch.empty((M, d), dtype=a.dtype, device=a.device) if y is None else y
+    _dev(h, "h", (a.dtype,))
+    _dev(y, "y", (a.dtype,))
+    _check(load_library().moe_grouped_swiglu(_ptr(a), _dtype_code(a), M, d, ffn, _ptr(offsets),
+                                             G, _ptr(w13), _ptr(w2), _ptr(h), _ptr(y),
+                                             _stream(stream)), "moe_grouped_swiglu")
+    return y
+
+
+def moe_unpermute_combine(y_perm, inv, topk_w, y_shared=None, y=None, stream=None):
+    """y [T, d] = sum_j topk_w[t,j] y_perm[inv[t k + j]] (+ y_shared[t])."""
+    torch = _torch()
+    _dev(y_perm, "y_perm", _act_dtypes())
+    _dev(inv, "inv", (torch.int32,))
+    _dev(topk_w, "topk_w", (torch.float32,))
+    T, k = topk_w.shape
+    d = y_perm.shape[1]
+    if y_shared is not None:
+        _dev(y_shared, "y_shared", (y_perm.dtype,))
+    y = torch.empty((T, d), dtype=y_perm.dtype, device=y_perm.device) if y is None else y
+    _dev(y, "y", (y_perm.dtype,))
+    _check(load_library().moe_unpermute_combine(_ptr(y_perm), _dtype_code(y_perm), T, k, d,
+                                                _ptr(inv), _ptr(topk_w), _ptr(y_shared), _ptr(y),
+                                                _stream(stream)), "moe_unpermute_combine")
+    return y

@@ -1,0 +1,120 @@
+// Unpermute and weight: y[t] = sum_j w[t,j] y_perm[inv[t k + j]] (+ y_shared[t]).
+//
+// Step 7 of the forward pass in "Expert parallelism" (zerotofrontier.app):
+// undo the sort and scatter-add each row into its token with its gate.  Here
+// the scatter-add is done in its gather form: one wave per token reads the
+// token's k packed rows through inv and writes the token once, so there are
+// no atomics and the fp32 sum order (slot 0..k-1, then the shared row) is
+// fixed.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <bool BF16>
+struct Vec;
+
+// 16 bytes = 8 bf16 values.
+template <>
+struct Vec<true> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void add(float *acc, float w, const uint4 &v) {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += w * bf16_lo(u[i]);
+      acc[2 * i + 1] += w * bf16_hi(u[i]);
+    }
+  }
+  static __device__ __forceinline__ uint4 pack(const float *acc) {
+    return make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                      pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+  }
+};
+
+// 16 bytes = 4 fp32 values.
+template <>
+struct Vec<false> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void add(float *acc, float w, const uint4 &v) {
+    acc[0] += w * __uint_as_float(v.x);
+    acc[1] += w * __uint_as_float(v.y);
+    acc[2] += w * __uint_as_float(v.z);
+    acc[3] += w * __uint_as_float(v.w);
+  }
+  static __device__ __forceinline__ uint4 pack(const float *acc) {
+    return make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                      __float_as_uint(acc[3]));
+  }
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_combine(const uint4 *__restrict__ y_perm, int T, int k,
+                                                      int nvec, const int32_t *__restrict__ inv,
+                                                      const float *__restrict__ w,
+                                                      const uint4 *__restrict__ y_sh, int64_t M,
+                                                      uint4 *__restrict__ y) {
+  using V = Vec<BF16>;
+  const int t = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = lane_id();
+  for (int v = lane; v < nvec; v += kWave) {
+    float acc[V::N];
+#pragma unroll
+    for (int i = 0; i < V::N; ++i) acc[i] = 0.0f;
+    int j = 0;
+    // Groups of four slots: issue the four loads, then accumulate in order.
+    for (; j + 4 <= k; j += 4) {
+      uint4 r[4];
+      float g[4];
+      bool ok[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = uniform(inv[(int64_t)t * k + j + u]);
+        g[u] = w[(int64_t)t * k + j + u];
+        ok[u] = p >= 0 && p < M;
+        if (ok[u]) r[u] = y_perm[(int64_t)p * nvec + v];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (ok[u]) V::add(acc, g[u], r[u]);
+    }
+    for (; j < k; ++j) {
+      const int p = uniform(inv[(int64_t)t * k + j]);
+      if (p >= 0 && p < M) V::add(acc, w[(int64_t)t * k + j], y_perm[(int64_t)p * nvec + v]);
+    }
+    if (y_sh) V::add(acc, 1.0f, y_sh[(int64_t)t * nvec + v]);
+    y[(int64_t)t * nvec + v] = V::pack(acc);
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_unpermute_combine(const void *y_perm, moe_dtype dt, int T, int k, int d,
+                                            const int32_t *inv, const float *topk_w,
+                                            const void *y_shared, void *y, hipStream_t stream) {
+  if (T < 0 || k < 1 || d < 1) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (d % 8 != 0 || k > 64 || (int64_t)T * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y_perm || !inv || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_perm) || !aligned16(y) || (y_shared && !aligned16(y_shared)))
+    return MOE_ERR_INVALID_ARG;
+  const int elem = dt == MOE_F32 ? 4 : 2;
+  const int nvec = (int)((int64_t)d * elem / 16);
+  const int64_t M = (int64_t)T * k;
+  const dim3 grid((T + 3) / 4), block(kThreads);
+  const uint4 *yp = static_cast<const uint4 *>(y_perm);
+  const uint4 *ys = static_cast<const uint4 *>(y_shared);
+  uint4 *out = static_cast<uint4 *>(y);
+  if (dt == MOE_BF16)
+    k_combine<true><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+  else
+    k_combine<false><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+  return launch_status();
+}

@@ -1,0 +1,244 @@
+// Permute: per-chunk expert histograms, one exclusive scan, a stable
+// wave-ballot multisplit that writes order and inv, and a row scatter that
+// reads every token row once and writes its k packed copies.
+//
+// "Token permutation and grouped GEMMs" (zerotofrontier.app, "Expert
+// parallelism"): order is the stable argsort of the expert ids, X[order] puts
+// rows in expert order, and inv (inv[order] = arange) undoes it.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;                // 4 waves per block
+constexpr int kMaxChunks = 1024;
+
+// Assignments per chunk: at least 2048, and few enough chunks that the scan's
+// per-expert walk over chunks stays short.
+inline int64_t chunk_size(int64_t M) {
+  int64_t c = 2048;
+  while ((M + c - 1) / c > kMaxChunks) c *= 2;
+  return c;
+}
+
+// hist[c][e] = number of assignments in chunk c with expert e.
+__global__ __launch_bounds__(kThreads) void k_hist(const int32_t *__restrict__ ids, int64_t M, int E,
+                                                   int64_t chunk, int32_t *__restrict__ hist) {
+  extern __shared__ int h[];
+  for (int e = threadIdx.x; e < E; e += kThreads) h[e] = 0;
+  __syncthreads();
+  const int64_t a0 = blockIdx.x * chunk;
+  const int64_t a1 = min(a0 + chunk, M);
+  for (int64_t a = a0 + threadIdx.x; a < a1; a += kThreads) {
+    const int e = ids[a];
+    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) hist[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// One block of 1024 threads, thread e owns expert e (E <= 1024).
+// counts[e] = sum over chunks; offsets = exclusive scan of counts;
+// hist[c][e] becomes the first packed position of chunk c's expert-e rows.
+__global__ __launch_bounds__(1024) void k_scan(int32_t *__restrict__ hist, int nchunks, int E,
+                                               int32_t *__restrict__ counts,
+                                               int32_t *__restrict__ offsets) {
+  __shared__ int wave_tot[16];
+  const int e = threadIdx.x;
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  int total = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = hist[(int64_t)c * E + e];
+      hist[(int64_t)c * E + e] = total;
+      total += v;
+    }
+    counts[e] = total;
+  }
+  // Block-wide exclusive scan of total over e.
+  int incl = total;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) wave_tot[wv] = incl;
+  __syncthreads();
+  if (wv == 0) {
+    int t = lane < 16 ? wave_tot[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int o = __shfl_up(t, off);
+      if (lane >= off) t += o;
+    }
+    if (lane < 16) wave_tot[lane] = t;  // inclusive totals per wave
+  }
+  __syncthreads();
+  const int excl = incl - total + (wv > 0 ? wave_tot[wv - 1] : 0);
+  if (e < E) {
+    offsets[e] = excl;
+    if (e == E - 1) offsets[E] = excl + total;
+    for (int c = 0; c < nchunks; ++c) hist[(int64_t)c * E + e] += excl;
+  }
+}
+
+// Stable ranks within a chunk.  The chunk is cut into 4 contiguous quarters,
+// one per wave.  Each wave walks its quarter 64 assignments at a time; lanes
+// with equal expert ids find each other with one ballot per id bit, and the
+// rank of a lane is the number of equal lanes below it.  Ranks therefore
+// follow assignment order, which makes the sort stable.
+__global__ __launch_bounds__(kThreads) void k_multisplit(const int32_t *__restrict__ ids, int64_t M,
+                                                         int E, int nbits, int64_t chunk,
+                                                         const int32_t *__restrict__ base,
+                                                         int32_t *__restrict__ order,
+                                                         int32_t *__restrict__ inv) {
+  extern __shared__ int cnt[];  // [4][E]
+  const int wv = uniform(threadIdx.x >> 6), lane = lane_id();
+  for (int i = threadIdx.x; i < 4 * E; i += kThreads) cnt[i] = 0;
+  __syncthreads();
+  const int64_t quarter = chunk / 4;
+  const int64_t c0 = blockIdx.x * chunk;
+  const int64_t q0 = min(c0 + wv * quarter, M), q1 = min(q0 + quarter, M);
+  int *mine = cnt + wv * E;
+  for (int64_t a = q0 + lane; a < q1; a += kWave) {
+    const int e = ids[a];
+    if (e >= 0 && e < E) atomicAdd(&mine[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    int run = base[(int64_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int v = cnt[w * E + e];
+      cnt[w * E + e] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int64_t s = q0; s < q1; s += kWave) {
+    const int64_t a = s + lane;
+    const int e = a < q1 ? ids[a] : -1;
+    const bool valid = e >= 0 && e < E;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    int pos = 0;
+    if (valid) {
+      pos = mine[e] + __popcll(peers & below);
+      order[pos] = (int32_t)a;
+      inv[a] = pos;
+    }
+    // All lanes have read mine[] above; now the lowest lane of each group of
+    // equal ids advances that expert's cursor.
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (peers & below) == 0) mine[e] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// One wave per token: read the row once (16-byte vectors), write k copies.
+__global__ __launch_bounds__(kThreads) void k_row_scatter(const uint4 *__restrict__ x, int T, int k,
+                                                          int nvec, const int32_t *__restrict__ inv,
+                                                          int64_t M, uint4 *__restrict__ x_perm) {
+  const int t = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = lane_id();
+  const uint4 *src = x + (int64_t)t * nvec;
+  int dst[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) dst[j] = j < k ? uniform(inv[(int64_t)t * k + j]) : -1;
+  for (int v0 = 0; v0 < nvec; v0 += 4 * kWave) {
+    uint4 r[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + u * kWave + lane;
+      if (v < nvec) r[u] = src[v];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j >= k) break;
+      const int p = dst[j];
+      if (p < 0 || p >= M) continue;
+      uint4 *out = x_perm + (int64_t)p * nvec;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int v = v0 + u * kWave + lane;
+        if (v < nvec) out[v] = r[u];
+      }
+    }
+  }
+}
+
+// Generic k (> 16): the same copy with inv read inside the loop.
+__global__ __launch_bounds__(kThreads) void k_row_scatter_anyk(const uint4 *__restrict__ x, int T,
+                                                               int k, int nvec,
+                                                               const int32_t *__restrict__ inv,
+                                                               int64_t M,
+                                                               uint4 *__restrict__ x_perm) {
+  const int t = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = lane_id();
+  for (int v = lane; v < nvec; v += kWave) {
+    const uint4 r = x[(int64_t)t * nvec + v];
+    for (int j = 0; j < k; ++j) {
+      const int p = uniform(inv[(int64_t)t * k + j]);
+      if (p >= 0 && p < M) x_perm[(int64_t)p * nvec + v] = r;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_permute_workspace_bytes(int T, int k, int E) {
+  if (T <= 0 || k <= 0 || E <= 0) return 16;
+  const int64_t M = (int64_t)T * k;
+  const int64_t nchunks = (M + chunk_size(M) - 1) / chunk_size(M);
+  return (size_t)nchunks * (size_t)E * sizeof(int32_t);
+}
+
+extern "C" moe_status moe_permute(const void *x, moe_dtype dt, int T, int d,
+                                  const int32_t *topk_ids, int k, int E, int32_t *counts,
+                                  int32_t *offsets, int32_t *order, int32_t *inv, void *x_perm,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T < 0 || k < 1 || E < 1 || d < 1) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (E > 1024 || d % 8 != 0 || (int64_t)T * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+  const int64_t M = (int64_t)T * k;
+  if (M > 0 && (!x || !topk_ids || !order || !inv || !x_perm || !workspace))
+    return MOE_ERR_INVALID_ARG;
+  if (M > 0 && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < moe_permute_workspace_bytes(T, k, E)) return MOE_ERR_INVALID_ARG;
+
+  const int64_t chunk = chunk_size(M > 0 ? M : 1);
+  const int nchunks = (int)((M + chunk - 1) / chunk);
+  int32_t *hist = static_cast<int32_t *>(workspace);
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+
+  if (nchunks > 0)
+    k_hist<<<dim3(nchunks), dim3(kThreads), sizeof(int) * E, stream>>>(topk_ids, M, E, chunk, hist);
+  // The scan also runs for M == 0 so that counts and offsets are written.
+  k_scan<<<dim3(1), dim3(1024), 0, stream>>>(hist, nchunks, E, counts, offsets);
+  if (M == 0) return launch_status();
+  k_multisplit<<<dim3(nchunks), dim3(kThreads), sizeof(int) * 4 * E, stream>>>(
+      topk_ids, M, E, nbits, chunk, hist, order, inv);
+  const int elem = dt == MOE_F32 ? 4 : 2;
+  const int nvec = (int)((int64_t)d * elem / 16);
+  const dim3 grid((T + 3) / 4);
+  if (k <= 16)
+    k_row_scatter<<<grid, dim3(kThreads), 0, stream>>>(static_cast<const uint4 *>(x), T, k, nvec,
+                                                        inv, M, static_cast<uint4 *>(x_perm));
+  else
+    k_row_scatter_anyk<<<grid, dim3(kThreads), 0, stream>>>(static_cast<const uint4 *>(x), T, k,
+                                                             nvec, inv, M,
+                                                             static_cast<uint4 *>(x_perm));
+  return launch_status();
+}

@@ -25,6 +25,7 @@ layer, DeepSeek-V3 decode and prefill layers, and one GPU's share of
 from __future__ import annotations
 
 import os
+import threading
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
@@ -109,6 +110,41 @@ def _normal(g: np.random.Generator, n: int, std: float, dtype: str) -> np.ndarra
     return a if dtype == "f32" else f32_to_bf16_bits(a)
 
 
+class _Scratch(threading.local):
+    f32 = None
+    u32 = None
+
+
+_scratch = _Scratch()
+
+
+def _normal_into(out: np.ndarray, g: np.random.Generator, std: float) -> None:
+    """Fill out (fp32, or uint16 bf16 bits) with N(0, std) draws.  Identical values
+    to _normal(); reuses per-thread scratch so no fresh pages are touched per call."""
+    n = out.size
+    flat = out.reshape(-1)
+    if out.dtype == np.float32:
+        g.standard_normal(n, dtype=np.float32, out=flat)
+        if std != 1.0:
+            flat *= np.float32(std)
+        return
+    if _scratch.f32 is None or _scratch.f32.size < n:
+        _scratch.f32 = np.empty(n, np.float32)
+        _scratch.u32 = np.empty(n, np.uint32)
+    a = _scratch.f32[:n]
+    g.standard_normal(n, dtype=np.float32, out=a)
+    if std != 1.0:
+        a *= np.float32(std)
+    u = a.view(np.uint32)
+    t = _scratch.u32[:n]
+    np.right_shift(u, np.uint32(16), out=t)          # round to nearest even:
+    np.bitwise_and(t, np.uint32(1), out=t)           # u + 0x7FFF + lsb(u >> 16)
+    np.add(t, np.uint32(0x7FFF), out=t)
+    np.add(t, u, out=t)
+    np.right_shift(t, np.uint32(16), out=t)
+    np.copyto(flat, t, casting="unsafe")
+
+
 def gen_logits(cfg: MoeConfig) -> np.ndarray:
     """Router logits [T, E], fp32 N(0,1)."""
     return rng(cfg, S_LOGITS).standard_normal((cfg.T, cfg.E), dtype=np.float32)
@@ -143,8 +179,8 @@ def gen_expert_weights(cfg: MoeConfig, experts=None, shared: bool = False):
 
     def one(i):
         e = ids[i]
-        w13[i] = _normal(rng(cfg, s13, e), 2 * ffn * d, cfg.w_std, cfg.dtype).reshape(2, ffn, d)
-        w2[i] = _normal(rng(cfg, s2, e), d * ffn, cfg.w_std, cfg.dtype).reshape(d, ffn)
+        _normal_into(w13[i], rng(cfg, s13, e), cfg.w_std)
+        _normal_into(w2[i], rng(cfg, s2, e), cfg.w_std)
 
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(one, range(G)))
