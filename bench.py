@@ -106,7 +106,7 @@ def main():
     log(f"workload {cfg.name}: generating inputs")
     t0 = time.perf_counter()
     x = inputs.gen_x(cfg)
-    w13, w2 = inputs.gen_expert_weights(cfg)
+    w13, w2 = inputs.gen_expert_weights(cfg, verbose=True)
     sh = inputs.gen_expert_weights(cfg, shared=True) if cfg.shared else (None, None)
     if cfg.gating == "given":
         logits = None

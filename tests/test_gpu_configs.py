@@ -50,7 +50,7 @@ def case(request):
     c.cfg = cfg
     log(f"{cfg.name}: generating inputs")
     c.x = inputs.gen_x(cfg)
-    c.w13, c.w2 = inputs.gen_expert_weights(cfg)
+    c.w13, c.w2 = inputs.gen_expert_weights(cfg, verbose=True)
     c.sh = inputs.gen_expert_weights(cfg, shared=True) if cfg.shared else (None, None)
     if cfg.gating == "given":
         c.logits = None

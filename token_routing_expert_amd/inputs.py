@@ -25,6 +25,7 @@ layer, DeepSeek-V3 decode and prefill layers, and one GPU's share of
 from __future__ import annotations
 
 import os
+import sys
 import threading
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
@@ -159,7 +160,7 @@ def _threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def gen_expert_weights(cfg: MoeConfig, experts=None, shared: bool = False):
+def gen_expert_weights(cfg: MoeConfig, experts=None, shared: bool = False, verbose: bool = False):
     """Expert weights, N(0, w_std).
 
     w13 [G, 2, ffn, d]: per expert the gate matrix then the up matrix, each row
@@ -181,6 +182,8 @@ def gen_expert_weights(cfg: MoeConfig, experts=None, shared: bool = False):
         e = ids[i]
         _normal_into(w13[i], rng(cfg, s13, e), cfg.w_std)
         _normal_into(w2[i], rng(cfg, s2, e), cfg.w_std)
+        if verbose and (i + 1) % 32 == 0:
+            print(f"  weights: {i + 1}/{G} experts", file=sys.stderr, flush=True)
 
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(one, range(G)))
