@@ -89,6 +89,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -129,6 +131,17 @@ def main():
             getattr(layer, name)()
             if evs is not None:
                 evs[i + 1].record(stream)
+
+    if args.copy_calibration:
+        # A plain device copy of known size: its FETCH_SIZE / WRITE_SIZE counter
+        # readings calibrate the counters of the path's kernels.
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 2, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read, {n} bytes written")
+        del src, dst
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):

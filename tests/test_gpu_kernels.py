@@ -220,6 +220,12 @@ GEMM_CASES = [
     ("bf16", 128, 128, [0, 0, 3]),
     ("bf16", 512, 256, [2, 5, 4, 3, 4, 4, 1, 0, 6, 2, 3, 4, 5, 4, 3, 3]),     # decode-like tiles
     ("f32", 128, 256, [4, 3, 0, 9, 1]),
+    # ping-pong tiles: medium (<= 288 rows per expert on average; 320-row
+    # tiles, here with experts of 321 and 640 rows that need two) and large
+    ("bf16", 512, 256, [250, 0, 321, 97, 640, 1]),
+    ("f32", 256, 256, [130, 300, 20]),
+    ("bf16", 256, 384, [700, 5, 1000, 0]),
+    ("f32", 256, 128, [513]),
 ]
 
 

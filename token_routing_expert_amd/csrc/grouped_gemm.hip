@@ -16,6 +16,8 @@
 // reads (32 rows, one chunk) hit distinct banks.  Each wave runs 32x32 MFMA
 // blocks: v_mfma_f32_32x32x16_bf16 for bf16, four v_mfma_f32_32x32x2f32 per
 // 16-byte chunk for fp32.  Accumulation is fp32.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -50,8 +52,13 @@ struct Mma<false> {
   }
 };
 
-// LDS index (in 16-byte chunks) of chunk cc of tile row r.
-__device__ __forceinline__ int swz(int r, int cc) { return r * 8 + (cc ^ (r & 7)); }
+// LDS layout of a staged tile: row r holds 8 16-byte chunks (one K slice of
+// 128 bytes: 64 bf16 or 32 fp32).  Chunk cc of row r is stored in slot
+// cc ^ key(r).  The key makes any 16 consecutive rows read at one logical
+// chunk -- an MFMA operand fetch reads 32 rows at one chunk -- cover every
+// bank of a 256-byte LDS bank row exactly once.
+__device__ __forceinline__ int swz_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r, int cc) { return r * 8 + (cc ^ swz_key(r)); }
 
 __device__ __forceinline__ int clamp_row(int v, int M) { return v < 0 ? 0 : (v > M ? M : v); }
 
@@ -59,10 +66,35 @@ struct Tile {
   int expert, lo, hi, m0, n_tile;
 };
 
-// Which expert and which (m, n) tile block L computes.  Tiles are numbered
+// MI355X dispatches workgroup i of a launch to XCD i % 8; each XCD has its own
+// L2.  The persistent kernels below give XCD x a contiguous band of tiles so
+// the tiles that share operands run on the same L2 at the same time.
+constexpr int kXcds = 8;
+
+// Total number of (m, n) tiles over all expert segments.  Every wave
+// computes the same value.
+template <int BM>
+__device__ __forceinline__ int count_tiles(const int32_t *__restrict__ offsets, int G, int M,
+                                           int ntiles) {
+  const int lane = lane_id();
+  int sum = 0;
+  for (int eb = 0; eb < G; eb += kWave) {
+    const int e = eb + lane;
+    if (e < G) {
+      const int a = clamp_row(offsets[e], M), b = clamp_row(offsets[e + 1], M);
+      const int n = b > a ? b - a : 0;
+      sum += ((n + BM - 1) / BM) * ntiles;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  return uniform(sum);
+}
+
+// Which expert and which (m, n) tile is tile number L.  Tiles are numbered
 // expert by expert; inside an expert n-tile major and m-tile minor, so the
-// m-tiles that share one weight tile are adjacent.  Every wave of the block
-// computes the same answer.  Returns false past the last real tile.
+// m-tiles that share one weight tile are adjacent and the n-tiles that share
+// the expert's rows follow each other.  Every wave computes the same answer.
 template <int BM>
 __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int G, int M,
                                           int ntiles, int L, Tile &t) {
@@ -101,174 +133,578 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
   return false;
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 63] (the count is an
+// immediate, so the value selects one of 64 waits through a branch tree).
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vmcnt_range(int n) {
+  if constexpr (LO == HI) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (LO & 15) | ((LO >> 4) << 14));
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (n <= MID) wait_vmcnt_range<LO, MID>(n);
+    else wait_vmcnt_range<MID + 1, HI>(n);
+  }
+}
+__device__ __forceinline__ void wait_vmcnt(int n) { wait_vmcnt_range<0, 63>(n < 63 ? n : 63); }
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-// Block tile BM x BN of the output (BN output columns of h or y), WM x WN
-// waves, each wave (BM/WM) x (BN/WN).  For SWIGLU the weight tile holds the
-// BN gate rows and then the BN matching up rows, and each wave keeps a gate
-// and an up accumulator per MFMA block.
+// Block tile: up to BM rows x BN output columns (of h or y), WM x WN waves.
+// Wave (wm, wn) owns row blocks wm, wm + WM, wm + 2 WM, ... (32 rows each,
+// interleaved so a short tile still spreads over all waves) and BN / WN
+// columns.  For SWIGLU the weight tile holds the BN gate rows and then the BN
+// matching up rows, and each wave keeps a gate and an up accumulator per MFMA
+// block.
 //
 //   A       [M, K] rows, kvec = K * elem / 16 chunks per row
 //   B       expert weights; expert g's first row at chunk g * b_expert_vec,
 //           up rows (SWIGLU) b_up_vec chunks after the gate rows
 //   C       [M, N] output, dtype of A
-template <bool BF16, int BM, int BN, int WM, int WN, bool SWIGLU>
+//
+// Persistent: the grid is a multiple of 8 workgroups sized to the resident
+// capacity; workgroup i serves XCD i % 8's band of tiles, so the tiles that
+// share operands run on one L2 at the same time.
+//
+// K loop: 128-byte K slices of the row tile and of the weight tile stream into
+// LDS with direct global-to-LDS loads (global_load_lds_dwordx4) that never
+// pass through registers.  The two operands have separate rings: the row
+// tile (shared by the workgroups of an expert, so mostly an L2 hit) SA
+// stages, SA - 1 slices ahead; the weight tile (read once from HBM) SB
+// stages, SB - 1 slices ahead.  One wave instruction fills 8 tile rows (1 KB of LDS,
+// contiguous); each lane fetches the global chunk that the swizzle puts at
+// its LDS slot.  Row groups wholly past the segment end are not loaded.  Each
+// wave waits (vmcnt) only for its own loads of the slice about to be used,
+// then one barrier makes the whole slice visible.
+template <bool BF16, int BM, int BN, int WM, int WN, bool SWIGLU, int SA, int SB>
 __global__ __launch_bounds__(WM *WN * 64) void k_grouped_gemm(
     const u32x4 *__restrict__ A, int M, int kvec, const int32_t *__restrict__ offsets, int G,
     const u32x4 *__restrict__ B, int64_t b_expert_vec, int64_t b_up_vec, int ntiles, int N,
     void *__restrict__ C) {
-  constexpr int NT = WM * WN * 64;
+  constexpr int NW = WM * WN;
   constexpr int BR = SWIGLU ? 2 * BN : BN;      // weight rows per tile
-  constexpr int A_PER = BM * 8 / NT;            // 16-byte chunks per thread per k-step
-  constexpr int B_PER = BR * 8 / NT;
-  constexpr int WMR = BM / WM, WNR = BN / WN;   // wave tile
-  constexpr int FM = WMR / 32, FN = WNR / 32;   // 32x32 MFMA blocks per wave
+  constexpr int NWA = NW / 2, NWB = NW - NWA;   // row-tile loaders, weight-tile loaders
+  constexpr int A_TOT = BM / 8, B_TOT = BR / 8;  // 8-row groups per slice
+  constexpr int A_PW = (A_TOT + NWA - 1) / NWA, B_PW = (B_TOT + NWB - 1) / NWB;
+  constexpr int MAXLD = A_PW > B_PW ? A_PW : B_PW;
+  constexpr int FM = BM / 32 / WM;              // row blocks per wave
+  constexpr int WNR = BN / WN, FN = WNR / 32;   // columns, column blocks per wave
   constexpr int NB = SWIGLU ? 2 * FN : FN;      // B fragments (gate, then up) per k-group
-  static_assert(A_PER * NT == BM * 8 && B_PER * NT == BR * 8, "tile / thread mismatch");
-  static_assert(FM >= 1 && FN >= 1, "wave tile too small");
+  constexpr int ASTAGE = BM * 8, BSTAGE = BR * 8;   // 16-byte chunks per stage
+  static_assert(NWA >= 1 && BM % 8 == 0 && BR % 8 == 0, "tile / wave mismatch");
+  static_assert(FM * WM * 32 == BM && FN >= 1, "wave tile");
+  static_assert(SA >= 2 && SB >= 2 && (SA - 2) * A_PW < 64 && (SB - 2) * B_PW < 64, "rings");
 
-  __shared__ u32x4 As[BM * 8];
-  __shared__ u32x4 Bs[BR * 8];
+  __shared__ u32x4 smem[SA * ASTAGE + SB * BSTAGE];
+  u32x4 *const a_ring = smem;
+  u32x4 *const b_ring = smem + SA * ASTAGE;
 
-  Tile tile;
-  if (!find_tile<BM>(offsets, G, M, ntiles, blockIdx.x, tile)) return;
-  const int m0 = tile.m0, hi = tile.hi, n0 = tile.n_tile * BN;
-
-  const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wave = uniform(tid >> 6);
+  const int wave = uniform(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  const int cc_ld = tid & 7;
-  const int row_ld = tid >> 3;
-
-  // Global chunk pointers for k-step 0.  Rows past the segment end re-read its
-  // last row (their results are never stored).
-  const u32x4 *pa[A_PER];
-#pragma unroll
-  for (int r = 0; r < A_PER; ++r) {
-    int row = m0 + row_ld + r * (NT / 8);
-    row = row < hi ? row : hi - 1;
-    pa[r] = A + (int64_t)row * kvec + cc_ld;
-  }
-  const u32x4 *bexp = B + (int64_t)tile.expert * b_expert_vec;
-  const u32x4 *pb[B_PER];
-#pragma unroll
-  for (int r = 0; r < B_PER; ++r) {
-    const int brow = row_ld + r * (NT / 8);
-    const u32x4 *base = bexp;
-    int n = n0 + brow;
-    if (SWIGLU && brow >= BN) {
-      base += b_up_vec;
-      n = n0 + brow - BN;
-    }
-    pb[r] = base + (int64_t)n * kvec + cc_ld;
-  }
-
-  // 32-row blocks of this wave that hold at least one live row.
-  const int wrow0 = m0 + wm * WMR;
-  int live = (hi - wrow0 + 31) / 32;
-  live = live < 0 ? 0 : (live > FM ? FM : live);
-
-  f32x16 acc[FM][NB];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  u32x4 ra[A_PER], rb[B_PER];
-#pragma unroll
-  for (int r = 0; r < A_PER; ++r) ra[r] = pa[r][0];
-#pragma unroll
-  for (int r = 0; r < B_PER; ++r) rb[r] = pb[r][0];
-
+  // DMA lane mapping: lane l fills row l / 8 of its 8-row group, LDS slot
+  // l % 8, which holds global chunk (l % 8) ^ key(row).
+  const int ld_row = lane >> 3;
+  const int ld_slot = lane & 7;
   const int KT = kvec / 8;
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt > 0) __syncthreads();
-#pragma unroll
-    for (int r = 0; r < A_PER; ++r) As[swz(row_ld + r * (NT / 8), cc_ld)] = ra[r];
-#pragma unroll
-    for (int r = 0; r < B_PER; ++r) Bs[swz(row_ld + r * (NT / 8), cc_ld)] = rb[r];
-    __syncthreads();
-    if (kt + 1 < KT) {
-      const int off = (kt + 1) * 8;
-#pragma unroll
-      for (int r = 0; r < A_PER; ++r) ra[r] = pa[r][off];
-#pragma unroll
-      for (int r = 0; r < B_PER; ++r) rb[r] = pb[r][off];
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int cc = 2 * q + (lane >> 5);
-      u32x4 fa[FM], fb[NB];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = As[swz(wm * WMR + i * 32 + (lane & 31), cc)];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        fb[j] = Bs[swz(wn * WNR + j * 32 + (lane & 31), cc)];
-        if (SWIGLU) fb[FN + j] = Bs[swz(BN + wn * WNR + j * 32 + (lane & 31), cc)];
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        if (i < live) {
-#pragma unroll
-          for (int j = 0; j < NB; ++j) Mma<BF16>::run(fa[i], fb[j], acc[i][j]);
+  const bool a_loader = wave < NWA;
+  const int lw = a_loader ? wave : wave - NWA;
+  const int lstride = a_loader ? NWA : NWB;
+  const int S = a_loader ? SA : SB;   // stages of this wave's ring
+
+  const int xcd = blockIdx.x % kXcds, nj = gridDim.x / kXcds;
+  const int total = count_tiles<BM>(offsets, G, M, ntiles);
+  const int band_end = (int)((int64_t)total * (xcd + 1) / kXcds);
+
+  for (int L = (int)((int64_t)total * xcd / kXcds) + (int)(blockIdx.x / kXcds); L < band_end;
+       L += nj) {
+    Tile tile;
+    find_tile<BM>(offsets, G, M, ntiles, L, tile);
+    const int m0 = tile.m0, hi = tile.hi, n0 = tile.n_tile * BN;
+    const int rows = hi - m0 < BM ? hi - m0 : BM;   // live rows of this tile
+
+    // DMA roles: waves 0 .. NWA-1 load the row tile, the other waves the
+    // weight tile, so each wave's vmcnt queue holds one operand's loads only
+    // and a weight slice issued SB - 1 steps ahead never holds up a row slice.
+    // Loader lw of an operand fills its 8-row groups lw, lw + stride, ...; a
+    // row group is loaded only if its first row is live, and its rows past
+    // the segment end re-read the last row (their results are never stored).
+    const int ngroups = a_loader ? ((rows + 7) / 8 < A_TOT ? (rows + 7) / 8 : A_TOT) : B_TOT;
+    const int nld = ngroups > lw ? (ngroups - lw + lstride - 1) / lstride : 0;
+    // Uniform base pointer plus a 32-bit per-lane chunk offset (the host
+    // checks that every offset fits), so the loads use the scalar-base form.
+    const u32x4 *lbase = a_loader ? A : B + (int64_t)tile.expert * b_expert_vec;
+    auto issue = [&](int kt) {
+      u32x4 *stage = a_loader ? a_ring + (kt % SA) * ASTAGE : b_ring + (kt % SB) * BSTAGE;
+      // A rolled loop: unrolled, the per-instruction offsets would be hoisted
+      // out of the K loop and held in registers the MFMA blocks need.
+#pragma unroll 1
+      for (int r = 0; r < nld; ++r) {
+        {
+          const int g = lw + r * lstride;
+          const uint32_t key = ld_row ^ (g & 1);   // swz_key(8 g + ld_row)
+          uint32_t off;
+          if (a_loader) {
+            int row = m0 + g * 8 + ld_row;
+            row = row < hi ? row : hi - 1;
+            off = (uint32_t)row * (uint32_t)kvec;
+          } else {
+            const int brow = g * 8 + ld_row;
+            off = SWIGLU && brow >= BN ? (uint32_t)b_up_vec + (uint32_t)(n0 + brow - BN) * kvec
+                                       : (uint32_t)(n0 + brow) * (uint32_t)kvec;
+          }
+          off += (uint32_t)kt * 8u + ((uint32_t)ld_slot ^ key);
+          __builtin_amdgcn_global_load_lds(
+              (const void *)(lbase + off),
+              (__attribute__((address_space(3))) void *)(stage + g * 64), 16, 0, 0);
         }
       }
-    }
-  }
+    };
 
-  // Epilogue.  MFMA 32x32 output layout: lane l holds column l % 32 and, in
-  // register v, row 8 (v / 4) + 4 (l / 32) + v % 4.
-  const int col_l = lane & 31, row_l = 4 * (lane >> 5);
+    // Row blocks of this wave that hold at least one live row: blocks
+    // wm, wm + WM, ... below ceil(rows / 32).
+    const int nblk = (rows + 31) / 32;
+    int live = (nblk - wm + WM - 1) / WM;
+    live = live < 0 ? 0 : (live > FM ? FM : live);
+
+    f32x16 acc[FM][NB];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    if (i >= live) continue;
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * WNR + j * 32 + col_l;
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wrow0 + i * 32 + 8 * (v >> 2) + row_l + (v & 3);
-        if (row < hi) {
-          const float val = SWIGLU ? silu(acc[i][j][v]) * acc[i][FN + j][v] : acc[i][j][v];
-          const int64_t idx = (int64_t)row * N + col;
-          if (BF16)
-            static_cast<uint16_t *>(C)[idx] = (uint16_t)f32_to_bf16_rne(val);
-          else
-            static_cast<float *>(C)[idx] = val;
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    // Prologue: each loader issues slices 0 .. S-2 of its ring; step j then
+    // issues slice j + S - 1.  At step kt the slices after kt that are
+    // already issued (up to S - 2 of them) may stay in flight.
+#pragma unroll
+    for (int s = 0; s < (SA > SB ? SA : SB) - 1; ++s)
+      if (s < S - 1 && s < KT) issue(s);
+
+    // The K loop, instantiated twice: FULL (every row block of this wave is
+    // live, the common case) issues all MFMAs unconditionally; the other
+    // variant skips dead blocks.  Fragments of k-group q + 1 are read from
+    // LDS while the MFMAs of k-group q run.
+    auto kloop = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      for (int kt = 0; kt < KT; ++kt) {
+        // This wave's loads of slice kt are done once no more than its loads
+        // of later slices remain in flight.
+        asm volatile("" ::: "memory");
+        wait_vmcnt(((kt + S - 2 < KT - 1 ? kt + S - 2 : KT - 1) - kt) * nld);
+        // Every wave's part of slice kt has landed, and every wave is done
+        // with the stages that row slice kt + SA - 1 and weight slice
+        // kt + SB - 1 overwrite (both were read in step kt - 1).
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+
+        const u32x4 *As = a_ring + (kt % SA) * ASTAGE;
+        const u32x4 *Bs = b_ring + (kt % SB) * BSTAGE;
+        u32x4 fa[2][FM], fb[2][NB];
+        auto fetch = [&](int q, int buf) {
+          const int cc = 2 * q + (lane >> 5);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            if (FULL || i < live) fa[buf][i] = As[swz((wm + i * WM) * 32 + (lane & 31), cc)];
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            fb[buf][j] = Bs[swz(wn * WNR + j * 32 + (lane & 31), cc)];
+            if (SWIGLU) fb[buf][FN + j] = Bs[swz(BN + wn * WNR + j * 32 + (lane & 31), cc)];
+          }
+        };
+        fetch(0, 0);
+        if (kt + S - 1 < KT) issue(kt + S - 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (q < 3) fetch(q + 1, (q + 1) & 1);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            if (FULL || i < live) {
+#pragma unroll
+              for (int j = 0; j < NB; ++j) Mma<BF16>::run(fa[q & 1][i], fb[q & 1][j], acc[i][j]);
+            }
+          }
+        }
+      }
+    };
+    if (live == FM)
+      kloop(std::true_type{});
+    else
+      kloop(std::false_type{});
+
+    // All waves are done reading LDS before the next tile's loads land in it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    // Epilogue.  MFMA 32x32 output layout: lane l holds column l % 32 and, in
+    // register v, row 8 (v / 4) + 4 (l / 32) + v % 4.
+    const int col_l = lane & 31, row_l = 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i >= live) continue;
+      const int rblk = m0 + (wm + i * WM) * 32;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * WNR + j * 32 + col_l;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = rblk + 8 * (v >> 2) + row_l + (v & 3);
+          if (row < hi) {
+            const float val = SWIGLU ? silu(acc[i][j][v]) * acc[i][FN + j][v] : acc[i][j][v];
+            const int64_t idx = (int64_t)row * N + col;
+            if (BF16)
+              static_cast<uint16_t *>(C)[idx] = (uint16_t)f32_to_bf16_rne(val);
+            else
+              static_cast<float *>(C)[idx] = val;
+          }
         }
       }
     }
   }
 }
 
-template <bool BF16, int BM, int BN, int WM, int WN>
+// Ping-pong variant for tiles with many rows: 8 waves, two per SIMD, in two
+// groups of 4.  The tile is up to BM rows x BR weight rows (SWIGLU: BR/2 gate
+// rows then the matching BR/2 up rows, i.e. BR/2 columns of h; otherwise BR
+// output columns).  Inside a group, wave (wm, wn) of WMG x WNG owns weight
+// rows [64 wn, 64 wn + 64) -- for SWIGLU 32 gate rows and their 32 up rows --
+// and the row blocks (32 rows each) g + 2 (wm + WMG i) of its group g.
+//
+// The two groups run the same program half a phase apart: each half K slice
+// (two k-groups) is a memory phase (LDS -> registers and issuing loads) and a
+// compute phase (MFMAs from registers), each closed by a barrier.  Group 1
+// starts one barrier late, so while one group issues MFMAs the other works
+// on memory, and the matrix cores of each SIMD stay busy.
+//
+// Direct global-to-LDS loads (global_load_lds_dwordx4) bring 128-byte K
+// slices; group 0 loads the row tile into a ring of 2 stages, one slice
+// ahead, group 1 the weight tile into a ring of SB stages, SB - 1 slices
+// ahead, so each wave's vmcnt queue holds one operand.  A slice is visible
+// to every wave after the first barrier that follows all its loaders' waits:
+// group 0 waits for row slice k + 1 at the end of its last compute phase of
+// slice k, group 1 for weight slice k + 1 at the end of its last memory phase
+// of slice k -- both right before the barrier after which group 0 reads slice
+// k + 1.  A stage is refilled only after both groups' last reads of it.
+template <bool BF16, int BM, int BR, int SB, bool SWIGLU>
+__global__ __launch_bounds__(512) void k_grouped_gemm_pp(
+    const u32x4 *__restrict__ A, int M, int kvec, const int32_t *__restrict__ offsets, int G,
+    const u32x4 *__restrict__ B, int64_t b_expert_vec, int64_t b_up_vec, int ntiles, int N,
+    void *__restrict__ C) {
+  constexpr int BN = SWIGLU ? BR / 2 : BR;       // output columns per tile
+  constexpr int WNG = BR / 64, WMG = 4 / WNG;    // waves of a group across N and M
+  constexpr int FM = (BM / 64 + WMG - 1) / WMG;  // row blocks per wave
+  constexpr int NB = 2;                          // B fragments per k-group
+  constexpr int ASTAGE = BM * 8, BSTAGE = BR * 8;   // 16-byte chunks per stage
+  constexpr int A_TOT = BM / 8, B_TOT = BR / 8;  // 8-row DMA groups per slice
+  constexpr int NLB = (B_TOT + 3) / 4;           // weight loads per group-1 wave per slice
+  static_assert(BM % 64 == 0 && (BR == 128 || BR == 256) && SB >= 2, "tile");
+  static_assert((2 * ASTAGE + SB * BSTAGE) * 16 <= 160 * 1024, "LDS");
+  static_assert(NLB * (SB - 1) < 64, "vmcnt");
+
+  __shared__ u32x4 smem[2 * ASTAGE + SB * BSTAGE];
+  u32x4 *const a_ring = smem;
+  u32x4 *const b_ring = smem + 2 * ASTAGE;
+
+  const int lane = lane_id();
+  const int wave = uniform(threadIdx.x >> 6);
+  const int grp = wave >> 2, wq = wave & 3;
+  const int wn = wq % WNG, wm = wq / WNG;
+  const int ld_row = lane >> 3, ld_slot = lane & 7;
+  const int KT = kvec / 8;
+
+  const int xcd = blockIdx.x % kXcds, nj = gridDim.x / kXcds;
+  const int total = count_tiles<BM>(offsets, G, M, ntiles);
+  const int band_end = (int)((int64_t)total * (xcd + 1) / kXcds);
+
+  for (int L = (int)((int64_t)total * xcd / kXcds) + (int)(blockIdx.x / kXcds); L < band_end;
+       L += nj) {
+    Tile tile;
+    find_tile<BM>(offsets, G, M, ntiles, L, tile);
+    const int m0 = tile.m0, hi = tile.hi, n0 = tile.n_tile * BN;
+    const int rows = hi - m0 < BM ? hi - m0 : BM;
+    const int nblk = (rows + 31) / 32;
+    // Row blocks g + 2 (wm + WMG i) below nblk.
+    int live = (nblk - grp - 2 * wm + 2 * WMG - 1) / (2 * WMG);
+    live = live < 0 ? 0 : (live > FM ? FM : live);
+
+    // Group 0: row groups wq, wq + 4, ... whose first row is live (rows past
+    // the segment end re-read its last row; their results are never stored).
+    // Group 1: weight groups wq, wq + 4, ...
+    const int a_groups = (rows + 7) / 8 < A_TOT ? (rows + 7) / 8 : A_TOT;
+    const u32x4 *bexp = B + (int64_t)tile.expert * b_expert_vec;
+    auto issue_a = [&](int kt) {
+      u32x4 *stage = a_ring + (kt & 1) * ASTAGE;
+#pragma unroll 1
+      for (int g = wq; g < a_groups; g += 4) {
+        int row = m0 + g * 8 + ld_row;
+        row = row < hi ? row : hi - 1;
+        const uint32_t key = ld_row ^ (g & 1);   // swz_key(8 g + ld_row)
+        __builtin_amdgcn_global_load_lds(
+            (const void *)(A + (int64_t)row * kvec + kt * 8 + (ld_slot ^ key)),
+            (__attribute__((address_space(3))) void *)(stage + g * 64), 16, 0, 0);
+      }
+    };
+    auto issue_b = [&](int kt) {
+      u32x4 *stage = b_ring + (kt % SB) * BSTAGE;
+#pragma unroll
+      for (int r = 0; r < NLB; ++r) {
+        const int g = wq + 4 * r;
+        if (g < B_TOT) {
+          const int brow = g * 8 + ld_row;
+          const uint32_t key = ld_row ^ (g & 1);
+          const u32x4 *src = bexp + (SWIGLU && brow >= BN ? b_up_vec + (int64_t)(n0 + brow - BN) * kvec
+                                                          : (int64_t)(n0 + brow) * kvec);
+          __builtin_amdgcn_global_load_lds(
+              (const void *)(src + kt * 8 + (ld_slot ^ key)),
+              (__attribute__((address_space(3))) void *)(stage + g * 64), 16, 0, 0);
+        }
+      }
+    };
+    // Group 1's wait for weight slice k: the weight slices after it that are
+    // already issued (k + 1 .. k + SB - 2) may stay in flight.
+    auto wait_b = [&](int k) {
+      const int last = k + SB - 2 < KT - 1 ? k + SB - 2 : KT - 1;
+      wait_vmcnt((last - k) * (B_TOT / 4));
+    };
+
+    f32x16 acc[FM][NB];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    // Slice 0 (and the first weight slices), then group 1 starts one barrier late.
+    asm volatile("" ::: "memory");
+    if (grp == 0) {
+      issue_a(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    } else {
+#pragma unroll
+      for (int s = 0; s < SB - 1; ++s)
+        if (s < KT) issue_b(s);
+      asm volatile("" ::: "memory");
+      wait_b(0);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (grp == 1) __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    // B fragment rows of this wave inside the weight tile.
+    const int brow0 = SWIGLU ? wn * 32 : wn * 64;
+    const int brow1 = SWIGLU ? BN + wn * 32 : wn * 64 + 32;
+
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // Memory phase.  First let the previous compute phase's MFMAs drain
+        // (they may still read the fragment registers the loads below
+        // overwrite): a use of every accumulator makes the compiler wait for
+        // the MFMA results.
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) asm volatile("" ::"v"(acc[i][j][0]));
+        const u32x4 *As = a_ring + (kt & 1) * ASTAGE;
+        const u32x4 *Bs = b_ring + (kt % SB) * BSTAGE;
+        u32x4 fa[2][FM], fb[2][NB];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int cc = 2 * (2 * h + q) + (lane >> 5);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            if (i < live) fa[q][i] = As[swz((grp + 2 * (wm + WMG * i)) * 32 + (lane & 31), cc)];
+          fb[q][0] = Bs[swz(brow0 + (lane & 31), cc)];
+          fb[q][1] = Bs[swz(brow1 + (lane & 31), cc)];
+        }
+        if (h == 0) {
+          if (grp == 0 && kt + 1 < KT) issue_a(kt + 1);
+          if (grp == 1 && kt + SB - 1 < KT) issue_b(kt + SB - 1);
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): reads done before the barrier
+        // Group 0 reads slice kt + 1 right after the next barrier but one.
+        if (grp == 1 && h == 1 && kt + 1 < KT) wait_b(kt + 1);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // Compute phase.
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            if (i < live)
+#pragma unroll
+              for (int j = 0; j < NB; ++j) Mma<BF16>::run(fa[q][i], fb[q][j], acc[i][j]);
+        asm volatile("" ::: "memory");
+        if (grp == 0 && h == 1 && kt + 1 < KT) __builtin_amdgcn_s_waitcnt(0x0F70);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+    }
+    if (grp == 0) __builtin_amdgcn_s_barrier();   // both groups leave the tile aligned
+    asm volatile("" ::: "memory");
+
+    // Epilogue.  MFMA 32x32 output layout: lane l holds column l % 32 and, in
+    // register v, row 8 (v / 4) + 4 (l / 32) + v % 4.
+    const int col_l = lane & 31, row_l = 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i >= live) continue;
+      const int rblk = m0 + (grp + 2 * (wm + WMG * i)) * 32;
+#pragma unroll
+      for (int j = 0; j < (SWIGLU ? 1 : 2); ++j) {
+        const int col = n0 + (SWIGLU ? wn * 32 : wn * 64 + j * 32) + col_l;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = rblk + 8 * (v >> 2) + row_l + (v & 3);
+          if (row < hi) {
+            const float val = SWIGLU ? silu(acc[i][0][v]) * acc[i][1][v] : acc[i][j][v];
+            const int64_t idx = (int64_t)row * N + col;
+            if (BF16)
+              static_cast<uint16_t *>(C)[idx] = (uint16_t)f32_to_bf16_rne(val);
+            else
+              static_cast<float *>(C)[idx] = val;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Compute units of the current device (cached per device id).
+inline int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Persistent grid: resident workgroups (CUs x blocks per CU), no more than
+// there can be tiles, rounded to a multiple of the XCD count.  per_cu caches
+// the occupancy query of one kernel instantiation.
+inline int persistent_grid(const void *kernel, int threads, int &per_cu, int64_t max_tiles) {
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  int64_t g = (int64_t)device_cus() * per_cu;
+  const int64_t cap = (max_tiles + kXcds - 1) / kXcds * kXcds;
+  if (g > cap) g = cap;
+  g = g / kXcds * kXcds;
+  return (int)(g < kXcds ? kXcds : g);
+}
+
+// One launch of the grouped GEMM with tile shape Cfg.
+template <int BM_, int BN_, int WM_, int WN_, int SA_, int SB_>
+struct TileCfg {
+  static constexpr bool PP = false;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, SA = SA_, SB = SB_;
+};
+// Ping-pong kernel: BM-row x BR-weight-row tiles, SB weight stages.
+template <int BM_, int BR_, int SB_>
+struct PpCfg {
+  static constexpr bool PP = true;
+  static constexpr int BM = BM_, BR = BR_, SB = SB_;
+};
+
+template <bool BF16, bool SWIGLU, typename Cfg>
+void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int G, const void *w,
+                void *out, hipStream_t stream) {
+  const int elem = BF16 ? 2 : 4;
+  const int kvec = K * elem / 16;
+  // w13 is [G, 2, N, K] (gate rows, then up rows); w2 is [G, N, K].
+  const int64_t b_expert = (int64_t)(SWIGLU ? 2 : 1) * N * kvec;
+  const int64_t b_up = SWIGLU ? (int64_t)N * kvec : 0;
+  if constexpr (Cfg::PP) {
+    constexpr int BN = SWIGLU ? Cfg::BR / 2 : Cfg::BR;
+    const int ntiles = N / BN;
+    const int64_t mtiles_max = (M + Cfg::BM - 1) / Cfg::BM + G;
+    auto kern = k_grouped_gemm_pp<BF16, Cfg::BM, Cfg::BR, Cfg::SB, SWIGLU>;
+    static int per_cu = 0;
+    const int grid = persistent_grid((const void *)kern, 512, per_cu, mtiles_max * ntiles);
+    kern<<<dim3(grid), dim3(512), 0, stream>>>(static_cast<const u32x4 *>(a), M, kvec, offsets, G,
+                                              static_cast<const u32x4 *>(w), b_expert, b_up,
+                                              ntiles, N, out);
+  } else {
+    const int ntiles = N / Cfg::BN;
+    const int64_t mtiles_max = (M + Cfg::BM - 1) / Cfg::BM + G;
+    auto kern = k_grouped_gemm<BF16, Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, SWIGLU, Cfg::SA, Cfg::SB>;
+    static int per_cu = 0;
+    const int threads = Cfg::WM * Cfg::WN * 64;
+    const int grid = persistent_grid((const void *)kern, threads, per_cu, mtiles_max * ntiles);
+    kern<<<dim3(grid), dim3(threads), 0, stream>>>(static_cast<const u32x4 *>(a), M, kvec, offsets,
+                                                  G, static_cast<const u32x4 *>(w), b_expert,
+                                                  b_up, ntiles, N, out);
+  }
+}
+
+// GEMM1 (gate/up + SwiGLU, K = d, N = ffn) then GEMM2 (down, K = ffn, N = d).
+template <bool BF16, typename C1, typename C2>
 moe_status launch_pair(const void *a, int M, int d, int ffn, const int32_t *offsets, int G,
                        const void *w13, const void *w2, void *h, void *y, hipStream_t stream) {
-  const int elem = BF16 ? 2 : 4;
-  const int mtiles_max = (M + BM - 1) / BM + G;
-  const dim3 block(WM * WN * 64);
-  // GEMM1: K = d, N = ffn, weights w13 [G, 2, ffn, d]
-  {
-    const int kvec = d * elem / 16;
-    const int ntiles = ffn / BN;
-    const int64_t b_expert = (int64_t)2 * ffn * kvec, b_up = (int64_t)ffn * kvec;
-    k_grouped_gemm<BF16, BM, BN, WM, WN, true><<<dim3(mtiles_max * ntiles), block, 0, stream>>>(
-        static_cast<const u32x4 *>(a), M, kvec, offsets, G, static_cast<const u32x4 *>(w13),
-        b_expert, b_up, ntiles, ffn, h);
-  }
-  // GEMM2: K = ffn, N = d, weights w2 [G, d, ffn]
-  {
-    const int kvec = ffn * elem / 16;
-    const int ntiles = d / BN;
-    const int64_t b_expert = (int64_t)d * kvec;
-    k_grouped_gemm<BF16, BM, BN, WM, WN, false><<<dim3(mtiles_max * ntiles), block, 0, stream>>>(
-        static_cast<const u32x4 *>(h), M, kvec, offsets, G, static_cast<const u32x4 *>(w2),
-        b_expert, 0, ntiles, d, y);
-  }
+  launch_one<BF16, true, C1>(a, M, d, ffn, offsets, G, w13, h, stream);
+  launch_one<BF16, false, C2>(h, M, ffn, d, offsets, G, w2, y, stream);
   return launch_status();
+}
+
+// Tile shapes.
+//   Small  (a few rows per expert, decode): 32-row tiles of the 4-wave kernel;
+//          the weights stream past once, three slices in flight.
+//   Medium (up to 320 rows per expert, e.g. 256 experts x 8192 tokens x top-8):
+//          ping-pong tiles of 320 rows, so one tile covers an expert's rows,
+//          each weight byte is read once and the workgroups of an XCD share
+//          the expert's rows through L2.
+//   Large  (many rows per expert): ping-pong tiles of 256 rows.
+#ifndef MOE_G1_SMALL
+#define MOE_G1_SMALL 32, 128, 1, 4, 2, 4
+#endif
+#ifndef MOE_G2_SMALL
+#define MOE_G2_SMALL 32, 128, 1, 4, 2, 4
+#endif
+#ifndef MOE_PP1_MEDIUM
+#define MOE_PP1_MEDIUM 320, 128, 4
+#endif
+#ifndef MOE_PP2_MEDIUM
+#define MOE_PP2_MEDIUM 320, 128, 4
+#endif
+#ifndef MOE_PP1_LARGE
+#define MOE_PP1_LARGE 256, 256, 3
+#endif
+#ifndef MOE_PP2_LARGE
+#define MOE_PP2_LARGE 256, 256, 3
+#endif
+using G1Small = TileCfg<MOE_G1_SMALL>;
+using G2Small = TileCfg<MOE_G2_SMALL>;
+using G1Medium = PpCfg<MOE_PP1_MEDIUM>;
+using G2Medium = PpCfg<MOE_PP2_MEDIUM>;
+using G1Large = PpCfg<MOE_PP1_LARGE>;
+using G2Large = PpCfg<MOE_PP2_LARGE>;
+
+template <bool BF16>
+moe_status launch_by_shape(const void *a, int M, int d, int ffn, const int32_t *offsets, int G,
+                           const void *w13, const void *w2, void *h, void *y, hipStream_t stream) {
+  const int64_t per_expert = (M + G - 1) / G;   // mean rows per expert
+  // The ping-pong tiles are up to 128 columns of h and 256 columns of y wide.
+  if (per_expert < 96 || d % 256 != 0)
+    return launch_pair<BF16, G1Small, G2Small>(a, M, d, ffn, offsets, G, w13, w2, h, y, stream);
+  if (per_expert <= 288)
+    return launch_pair<BF16, G1Medium, G2Medium>(a, M, d, ffn, offsets, G, w13, w2, h, y, stream);
+  return launch_pair<BF16, G1Large, G2Large>(a, M, d, ffn, offsets, G, w13, w2, h, y, stream);
 }
 
 }  // namespace
@@ -282,15 +718,18 @@ extern "C" moe_status moe_grouped_swiglu(const void *a, moe_dtype dt, int M, int
   if (M < 0 || G < 1 || d < 1 || ffn < 1) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (d % 128 != 0 || ffn % 128 != 0 || G > 4096) return MOE_ERR_UNSUPPORTED;
+  // 16-byte chunk offsets inside the row operands and inside one expert's
+  // weights are 32-bit in the kernels.
+  {
+    const int64_t elem = dt == MOE_F32 ? 4 : 2, big = (int64_t)1 << 31;
+    const int64_t krow = (int64_t)(d > ffn ? d : ffn) * elem / 16;
+    if ((int64_t)M * krow >= big || (int64_t)2 * ffn * d * elem / 16 >= big) return MOE_ERR_UNSUPPORTED;
+  }
   if (M == 0) return MOE_OK;
   if (!a || !offsets || !w13 || !w2 || !h || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(w13) || !aligned16(w2) || !aligned16(h) || !aligned16(y))
     return MOE_ERR_INVALID_ARG;
-  // Few rows per expert (decode): 32-row tiles, the weights stream past once.
-  const bool small = (int64_t)M < (int64_t)96 * G;
-  if (dt == MOE_BF16)
-    return small ? launch_pair<true, 32, 128, 1, 4>(a, M, d, ffn, offsets, G, w13, w2, h, y, stream)
-                 : launch_pair<true, 128, 128, 2, 2>(a, M, d, ffn, offsets, G, w13, w2, h, y, stream);
-  return small ? launch_pair<false, 32, 128, 1, 4>(a, M, d, ffn, offsets, G, w13, w2, h, y, stream)
-               : launch_pair<false, 128, 128, 2, 2>(a, M, d, ffn, offsets, G, w13, w2, h, y, stream);
+  return dt == MOE_BF16
+             ? launch_by_shape<true>(a, M, d, ffn, offsets, G, w13, w2, h, y, stream)
+             : launch_by_shape<false>(a, M, d, ffn, offsets, G, w13, w2, h, y, stream);
 }
