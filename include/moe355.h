@@ -174,6 +174,26 @@ moe_status moe_grouped_swiglu(const void *a, moe_dtype dt, int M, int d, int ffn
                               void *h, void *y, hipStream_t stream);
 
 /*
+ * The two halves of moe_grouped_swiglu as separate launches, so a caller can
+ * time, overlap or fuse around each product on its own.  Same arguments,
+ * layouts, precision and errors as moe_grouped_swiglu; the pair
+ * moe_grouped_gate_up then moe_grouped_down gives bit-identical h and y.
+ *
+ * moe_grouped_gate_up: h[p] = SiLU(a[p] W_gate,g^T) * (a[p] W_up,g^T) for
+ *   each packed row p of expert g's segment (4 d ffn FLOPs per row).
+ *   a [M, d] in, w13 [G, 2, ffn, d] in, h [M, ffn] out.
+ * moe_grouped_down: y[p] = h[p] W_down,g^T (2 d ffn FLOPs per row).
+ *   h [M, ffn] in, w2 [G, d, ffn] in, y [M, d] out.  Argument order follows
+ *   the product: M, then K = ffn, then N = d.
+ */
+moe_status moe_grouped_gate_up(const void *a, moe_dtype dt, int M, int d, int ffn,
+                               const int32_t *offsets, int G, const void *w13, void *h,
+                               hipStream_t stream);
+moe_status moe_grouped_down(const void *h, moe_dtype dt, int M, int ffn, int d,
+                            const int32_t *offsets, int G, const void *w2, void *y,
+                            hipStream_t stream);
+
+/*
  * Unpermute and weight (step 7; "Token permutation and grouped GEMMs":
  * Y_sorted[inv] restores the token order): for each token t,
  *     y[t] = sum_{j<k} topk_w[t, j] * y_perm[inv[t k + j]]  (+ y_shared[t]),

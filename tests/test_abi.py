@@ -105,6 +105,20 @@ def test_grouped_swiglu_validation(lib):
     assert f(a, 1, 0, 128, 256, NULL, 4, NULL, NULL, NULL, NULL, NULL) == 0  # M = 0: no-op
 
 
+def test_grouped_halves_validation(lib):
+    a = ctypes.c_void_p(16)
+    for f, args in ((lib.moe_grouped_gate_up, lambda M, d, ffn, off, G, p: (a, 1, M, d, ffn, off, G, a, p, NULL)),
+                    (lib.moe_grouped_down, lambda M, d, ffn, off, G, p: (a, 1, M, ffn, d, off, G, a, p, NULL))):
+        assert f(*args(64, 96, 256, a, 4, a)) == UNSUPPORTED       # d % 128
+        assert f(*args(64, 128, 200, a, 4, a)) == UNSUPPORTED      # ffn % 128
+        assert f(*args(64, 128, 256, a, 5000, a)) == UNSUPPORTED   # G > 4096
+        assert f(*args(64, 128, 256, a, 0, a)) == INVALID          # G < 1
+        assert f(*args(64, 128, 256, NULL, 4, a)) == INVALID       # null offsets
+        assert f(*args(64, 128, 256, a, 4, NULL)) == INVALID       # null output
+        assert f(*args(64, 128, 256, a, 4, ctypes.c_void_p(24))) == INVALID   # misaligned output
+        assert f(*args(0, 128, 256, NULL, 4, NULL)) == 0           # M = 0: no-op
+
+
 def test_combine_validation(lib):
     f = lib.moe_unpermute_combine
     a = ctypes.c_void_p(16)

@@ -226,6 +226,11 @@ GEMM_CASES = [
     ("f32", 256, 256, [130, 300, 20]),
     ("bf16", 256, 384, [700, 5, 1000, 0]),
     ("f32", 256, 128, [513]),
+    # wider shapes: several K slices per ring stage cycle, tails of 65, 97,
+    # 128 and 1 rows, a single large segment
+    ("bf16", 512, 512, [250, 0, 321, 97, 640, 1]),
+    ("bf16", 768, 640, [300, 40, 513]),
+    ("bf16", 512, 1024, [1000]),
 ]
 
 
@@ -243,6 +248,25 @@ def test_grouped_swiglu(lib, case):
     y = lib.moe_grouped_swiglu(dev(a), dev(offsets), dev(w13), dev(w2))
     torch.cuda.synchronize()
     rows_close(as_f64(host(y)), ref, 1e-4 if dt == "f32" else 2e-2)
+
+
+@pytest.mark.parametrize("case", [GEMM_CASES[0], GEMM_CASES[4], GEMM_CASES[6], GEMM_CASES[10]])
+def test_grouped_halves_match_the_fused_call(lib, case):
+    """moe_grouped_gate_up then moe_grouped_down give h and y bit for bit as moe_grouped_swiglu."""
+    dt, d, ffn, sizes = case
+    G, M = len(sizes), sum(sizes)
+    cfg = inputs.MoeConfig("t", 4, T=M, E=G, k=1, d=d, ffn=ffn, dtype=dt, gating="softmax",
+                           w_std=0.05)
+    a = dev(inputs.gen_x(cfg))
+    w13, w2 = (dev(w) for w in inputs.gen_expert_weights(cfg))
+    offsets = dev(np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32))
+    h1 = torch.empty((M, ffn), dtype=a.dtype, device=a.device)
+    y1 = lib.moe_grouped_swiglu(a, offsets, w13, w2, h=h1)
+    h2 = lib.moe_grouped_gate_up(a, offsets, w13)
+    y2 = lib.moe_grouped_down(h2, offsets, w2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(h1).view(np.uint8), host(h2).view(np.uint8))
+    assert np.array_equal(host(y1).view(np.uint8), host(y2).view(np.uint8))
 
 
 def test_grouped_swiglu_shared_expert_form(lib):

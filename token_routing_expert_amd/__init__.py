@@ -21,7 +21,7 @@ MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 # Every symbol include/moe355.h declares.
 EXPORTS = ("moe_status_string", "moe_route_topk", "moe_sigmoid_pinned", "moe_send_counts",
            "moe_permute_workspace_bytes", "moe_permute", "moe_grouped_swiglu",
-           "moe_unpermute_combine")
+           "moe_grouped_gate_up", "moe_grouped_down", "moe_unpermute_combine")
 
 
 class MoeError(RuntimeError):
@@ -49,9 +49,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_permute_workspace_bytes.restype = sz
     lib.moe_permute.argtypes = [P, i32, i32, i32, P, i32, i32, P, P, P, P, P, P, sz, P]
     lib.moe_grouped_swiglu.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P, P, P]
+    lib.moe_grouped_gate_up.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P]
+    lib.moe_grouped_down.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P]
     lib.moe_unpermute_combine.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P]
     for name in ("moe_route_topk", "moe_sigmoid_pinned", "moe_send_counts", "moe_permute",
-                 "moe_grouped_swiglu", "moe_unpermute_combine"):
+                 "moe_grouped_swiglu", "moe_grouped_gate_up", "moe_grouped_down",
+                 "moe_unpermute_combine"):
         getattr(lib, name).restype = i32
     if path == LIB_PATH:
         _lib = lib
@@ -191,6 +194,50 @@ def moe_grouped_swiglu(a, offsets, w13, w2, h=None, y=None, stream=None):
     _check(load_library().moe_grouped_swiglu(_ptr(a), _dtype_code(a), M, d, ffn, _ptr(offsets),
                                              G, _ptr(w13), _ptr(w2), _ptr(h), _ptr(y),
                                              _stream(stream)), "moe_grouped_swiglu")
+    return y
+
+
+def _expert_shapes(name, a, offsets, w13=None, w2=None):
+    torch = _torch()
+    _dev(a, "a", _act_dtypes())
+    _dev(offsets, "offsets", (torch.int32,))
+    for wname, w in (("w13", w13), ("w2", w2)):
+        if w is not None:
+            _dev(w, wname, (a.dtype,))
+    G = offsets.numel() - 1
+    if w13 is not None and (w13.dim() != 4 or w13.shape[0] != G or w13.shape[1] != 2):
+        raise MoeError(f"{name}: w13 must be [G, 2, ffn, d] with G = offsets.numel() - 1")
+    if w2 is not None and (w2.dim() != 3 or w2.shape[0] != G):
+        raise MoeError(f"{name}: w2 must be [G, d, ffn] with G = offsets.numel() - 1")
+    return G
+
+
+def moe_grouped_gate_up(a, offsets, w13, h=None, stream=None):
+    """h [M, ffn] = SiLU(a W_gate^T) * (a W_up^T) per expert segment of the packed rows a [M, d]."""
+    G = _expert_shapes("moe_grouped_gate_up", a, offsets, w13=w13)
+    M, d = a.shape
+    ffn = w13.shape[2]
+    if w13.shape[3] != d:
+        raise MoeError("moe_grouped_gate_up: inconsistent shapes")
+    h = _torch().empty((M, ffn), dtype=a.dtype, device=a.device) if h is None else h
+    _dev(h, "h", (a.dtype,))
+    _check(load_library().moe_grouped_gate_up(_ptr(a), _dtype_code(a), M, d, ffn, _ptr(offsets),
+                                              G, _ptr(w13), _ptr(h), _stream(stream)),
+           "moe_grouped_gate_up")
+    return h
+
+
+def moe_grouped_down(h, offsets, w2, y=None, stream=None):
+    """y [M, d] = h W_down^T per expert segment of h [M, ffn]."""
+    G = _expert_shapes("moe_grouped_down", h, offsets, w2=w2)
+    M, ffn = h.shape
+    d = w2.shape[1]
+    if w2.shape[2] != ffn:
+        raise MoeError("moe_grouped_down: inconsistent shapes")
+    y = _torch().empty((M, d), dtype=h.dtype, device=h.device) if y is None else y
+    _dev(y, "y", (h.dtype,))
+    _check(load_library().moe_grouped_down(_ptr(h), _dtype_code(h), M, ffn, d, _ptr(offsets), G,
+                                           _ptr(w2), _ptr(y), _stream(stream)), "moe_grouped_down")
     return y
 
 

@@ -653,15 +653,6 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
   }
 }
 
-// GEMM1 (gate/up + SwiGLU, K = d, N = ffn) then GEMM2 (down, K = ffn, N = d).
-template <bool BF16, typename C1, typename C2>
-moe_status launch_pair(const void *a, int M, int d, int ffn, const int32_t *offsets, int G,
-                       const void *w13, const void *w2, void *h, void *y, hipStream_t stream) {
-  launch_one<BF16, true, C1>(a, M, d, ffn, offsets, G, w13, h, stream);
-  launch_one<BF16, false, C2>(h, M, ffn, d, offsets, G, w2, y, stream);
-  return launch_status();
-}
-
 // Tile shapes.
 //   Small  (a few rows per expert, decode): 32-row tiles of the 4-wave kernel;
 //          the weights stream past once, three slices in flight.
@@ -695,16 +686,52 @@ using G2Medium = PpCfg<MOE_PP2_MEDIUM>;
 using G1Large = PpCfg<MOE_PP1_LARGE>;
 using G2Large = PpCfg<MOE_PP2_LARGE>;
 
+// Which tile family serves a call: by the mean rows per expert.  Both halves
+// of an expert MLP use the same family.  The ping-pong tiles are up to 128
+// columns of h and 256 columns of y wide.
+enum class Family { Small, Medium, Large };
+inline Family family_of(int M, int G, int d) {
+  const int64_t per_expert = ((int64_t)M + G - 1) / G;
+  if (per_expert < 96 || d % 256 != 0) return Family::Small;
+  return per_expert <= 288 ? Family::Medium : Family::Large;
+}
+
+// GEMM1: gate/up + SwiGLU, K = d, N = ffn.
 template <bool BF16>
-moe_status launch_by_shape(const void *a, int M, int d, int ffn, const int32_t *offsets, int G,
-                           const void *w13, const void *w2, void *h, void *y, hipStream_t stream) {
-  const int64_t per_expert = (M + G - 1) / G;   // mean rows per expert
-  // The ping-pong tiles are up to 128 columns of h and 256 columns of y wide.
-  if (per_expert < 96 || d % 256 != 0)
-    return launch_pair<BF16, G1Small, G2Small>(a, M, d, ffn, offsets, G, w13, w2, h, y, stream);
-  if (per_expert <= 288)
-    return launch_pair<BF16, G1Medium, G2Medium>(a, M, d, ffn, offsets, G, w13, w2, h, y, stream);
-  return launch_pair<BF16, G1Large, G2Large>(a, M, d, ffn, offsets, G, w13, w2, h, y, stream);
+void launch_gate_up(Family f, const void *a, int M, int d, int ffn, const int32_t *offsets, int G,
+                    const void *w13, void *h, hipStream_t stream) {
+  if (f == Family::Small)
+    launch_one<BF16, true, G1Small>(a, M, d, ffn, offsets, G, w13, h, stream);
+  else if (f == Family::Medium)
+    launch_one<BF16, true, G1Medium>(a, M, d, ffn, offsets, G, w13, h, stream);
+  else
+    launch_one<BF16, true, G1Large>(a, M, d, ffn, offsets, G, w13, h, stream);
+}
+
+// GEMM2: down, K = ffn, N = d.
+template <bool BF16>
+void launch_down(Family f, const void *h, int M, int ffn, int d, const int32_t *offsets, int G,
+                 const void *w2, void *y, hipStream_t stream) {
+  if (f == Family::Small)
+    launch_one<BF16, false, G2Small>(h, M, ffn, d, offsets, G, w2, y, stream);
+  else if (f == Family::Medium)
+    launch_one<BF16, false, G2Medium>(h, M, ffn, d, offsets, G, w2, y, stream);
+  else
+    launch_one<BF16, false, G2Large>(h, M, ffn, d, offsets, G, w2, y, stream);
+}
+
+// Argument checks shared by the three entry points (pointers are checked by
+// each).  Returns MOE_OK when the call may launch.
+moe_status check_shape(moe_dtype dt, int M, int d, int ffn, int G) {
+  if (M < 0 || G < 1 || d < 1 || ffn < 1) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (d % 128 != 0 || ffn % 128 != 0 || G > 4096) return MOE_ERR_UNSUPPORTED;
+  // 16-byte chunk offsets inside the row operands and inside one expert's
+  // weights are 32-bit in the kernels.
+  const int64_t elem = dt == MOE_F32 ? 4 : 2, big = (int64_t)1 << 31;
+  const int64_t krow = (int64_t)(d > ffn ? d : ffn) * elem / 16;
+  if ((int64_t)M * krow >= big || (int64_t)2 * ffn * d * elem / 16 >= big) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
 }
 
 }  // namespace
@@ -712,24 +739,51 @@ moe_status launch_by_shape(const void *a, int M, int d, int ffn, const int32_t *
 
 using namespace moe;
 
+extern "C" moe_status moe_grouped_gate_up(const void *a, moe_dtype dt, int M, int d, int ffn,
+                                          const int32_t *offsets, int G, const void *w13, void *h,
+                                          hipStream_t stream) {
+  const moe_status st = check_shape(dt, M, d, ffn, G);
+  if (st != MOE_OK || M == 0) return st;
+  if (!a || !offsets || !w13 || !h) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(w13) || !aligned16(h)) return MOE_ERR_INVALID_ARG;
+  const Family f = family_of(M, G, d);
+  if (dt == MOE_BF16)
+    launch_gate_up<true>(f, a, M, d, ffn, offsets, G, w13, h, stream);
+  else
+    launch_gate_up<false>(f, a, M, d, ffn, offsets, G, w13, h, stream);
+  return launch_status();
+}
+
+extern "C" moe_status moe_grouped_down(const void *h, moe_dtype dt, int M, int ffn, int d,
+                                       const int32_t *offsets, int G, const void *w2, void *y,
+                                       hipStream_t stream) {
+  const moe_status st = check_shape(dt, M, d, ffn, G);
+  if (st != MOE_OK || M == 0) return st;
+  if (!h || !offsets || !w2 || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w2) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  const Family f = family_of(M, G, d);
+  if (dt == MOE_BF16)
+    launch_down<true>(f, h, M, ffn, d, offsets, G, w2, y, stream);
+  else
+    launch_down<false>(f, h, M, ffn, d, offsets, G, w2, y, stream);
+  return launch_status();
+}
+
 extern "C" moe_status moe_grouped_swiglu(const void *a, moe_dtype dt, int M, int d, int ffn,
                                          const int32_t *offsets, int G, const void *w13,
                                          const void *w2, void *h, void *y, hipStream_t stream) {
-  if (M < 0 || G < 1 || d < 1 || ffn < 1) return MOE_ERR_INVALID_ARG;
-  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (d % 128 != 0 || ffn % 128 != 0 || G > 4096) return MOE_ERR_UNSUPPORTED;
-  // 16-byte chunk offsets inside the row operands and inside one expert's
-  // weights are 32-bit in the kernels.
-  {
-    const int64_t elem = dt == MOE_F32 ? 4 : 2, big = (int64_t)1 << 31;
-    const int64_t krow = (int64_t)(d > ffn ? d : ffn) * elem / 16;
-    if ((int64_t)M * krow >= big || (int64_t)2 * ffn * d * elem / 16 >= big) return MOE_ERR_UNSUPPORTED;
-  }
-  if (M == 0) return MOE_OK;
+  const moe_status st = check_shape(dt, M, d, ffn, G);
+  if (st != MOE_OK || M == 0) return st;
   if (!a || !offsets || !w13 || !w2 || !h || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(w13) || !aligned16(w2) || !aligned16(h) || !aligned16(y))
     return MOE_ERR_INVALID_ARG;
-  return dt == MOE_BF16
-             ? launch_by_shape<true>(a, M, d, ffn, offsets, G, w13, w2, h, y, stream)
-             : launch_by_shape<false>(a, M, d, ffn, offsets, G, w13, w2, h, y, stream);
+  const Family f = family_of(M, G, d);
+  if (dt == MOE_BF16) {
+    launch_gate_up<true>(f, a, M, d, ffn, offsets, G, w13, h, stream);
+    launch_down<true>(f, h, M, ffn, d, offsets, G, w2, y, stream);
+  } else {
+    launch_gate_up<false>(f, a, M, d, ffn, offsets, G, w13, h, stream);
+    launch_down<false>(f, h, M, ffn, d, offsets, G, w2, y, stream);
+  }
+  return launch_status();
 }

@@ -10,8 +10,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (moe_grouped_swiglu, moe_permute, moe_permute_workspace_bytes, moe_route_topk,
-               moe_send_counts, moe_unpermute_combine)
+from . import (moe_grouped_down, moe_grouped_gate_up, moe_grouped_swiglu, moe_permute,
+               moe_permute_workspace_bytes, moe_route_topk, moe_send_counts,
+               moe_unpermute_combine)
 from .inputs import MoeConfig
 
 
@@ -92,6 +93,14 @@ class MoeLayer:
     def experts_routed(self, stream=None):
         moe_grouped_swiglu(self.x_perm, self.offsets, self.w13, self.w2, self.h, self.y_perm,
                            stream=stream)
+
+    def gate_up(self, stream=None):
+        """The routed experts' first product alone (the same launch experts_routed makes)."""
+        moe_grouped_gate_up(self.x_perm, self.offsets, self.w13, self.h, stream=stream)
+
+    def down(self, stream=None):
+        """The routed experts' second product alone."""
+        moe_grouped_down(self.h, self.offsets, self.w2, self.y_perm, stream=stream)
 
     def experts_shared(self, stream=None):
         if self.cfg.shared:
