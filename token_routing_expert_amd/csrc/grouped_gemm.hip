@@ -95,12 +95,15 @@ __device__ __forceinline__ int count_tiles(const int32_t *__restrict__ offsets, 
 // expert by expert; inside an expert n-tile major and m-tile minor, so the
 // m-tiles that share one weight tile are adjacent and the n-tiles that share
 // the expert's rows follow each other.  Every wave computes the same answer.
+// A workgroup asks for increasing L, so the search resumes at the expert
+// (e0) and tile number (base) of the previous answer: one 64-expert window
+// per call in the usual case instead of a scan from expert 0.
 template <int BM>
 __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int G, int M,
-                                          int ntiles, int L, Tile &t) {
+                                          int ntiles, int L, Tile &t, int &e0, int &base) {
   const int lane = lane_id();
-  int running = 0;
-  for (int eb = 0; eb < G; eb += kWave) {
+  int running = base;
+  for (int eb = e0; eb < G; eb += kWave) {
     const int e = eb + lane;
     int a = 0, b = 0, tiles = 0;
     if (e < G) {
@@ -122,10 +125,13 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
       t.expert = eb + src;
       t.lo = uniform(__shfl(a, src));
       t.hi = uniform(__shfl(b, src));
-      const int local = L - uniform(__shfl(excl, src));
+      const int first = uniform(__shfl(excl, src));
+      const int local = L - first;
       const int mtiles = (t.hi - t.lo + BM - 1) / BM;
       t.m0 = t.lo + (local % mtiles) * BM;
       t.n_tile = local / mtiles;
+      e0 = t.expert;
+      base = first;
       return true;
     }
     running += __shfl(incl, kWave - 1);
@@ -215,10 +221,11 @@ __global__ __launch_bounds__(WM *WN * 64) void k_grouped_gemm(
   const int total = count_tiles<BM>(offsets, G, M, ntiles);
   const int band_end = (int)((int64_t)total * (xcd + 1) / kXcds);
 
+  int cur_e = 0, cur_base = 0;   // search cursor of find_tile
   for (int L = (int)((int64_t)total * xcd / kXcds) + (int)(blockIdx.x / kXcds); L < band_end;
        L += nj) {
     Tile tile;
-    find_tile<BM>(offsets, G, M, ntiles, L, tile);
+    find_tile<BM>(offsets, G, M, ntiles, L, tile, cur_e, cur_base);
     const int m0 = tile.m0, hi = tile.hi, n0 = tile.n_tile * BN;
     const int rows = hi - m0 < BM ? hi - m0 : BM;   // live rows of this tile
 
@@ -417,10 +424,11 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
   const int total = count_tiles<BM>(offsets, G, M, ntiles);
   const int band_end = (int)((int64_t)total * (xcd + 1) / kXcds);
 
+  int cur_e = 0, cur_base = 0;   // search cursor of find_tile
   for (int L = (int)((int64_t)total * xcd / kXcds) + (int)(blockIdx.x / kXcds); L < band_end;
        L += nj) {
     Tile tile;
-    find_tile<BM>(offsets, G, M, ntiles, L, tile);
+    find_tile<BM>(offsets, G, M, ntiles, L, tile, cur_e, cur_base);
     const int m0 = tile.m0, hi = tile.hi, n0 = tile.n_tile * BN;
     const int rows = hi - m0 < BM ? hi - m0 : BM;
     const int nblk = (rows + 31) / 32;
@@ -657,9 +665,11 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
 //   Small  (a few rows per expert, decode): 32-row tiles of the 4-wave kernel;
 //          the weights stream past once, three slices in flight.
 //   Medium (up to 320 rows per expert, e.g. 256 experts x 8192 tokens x top-8):
-//          ping-pong tiles of 320 rows, so one tile covers an expert's rows,
-//          each weight byte is read once and the workgroups of an XCD share
-//          the expert's rows through L2.
+//          ping-pong tiles of 320 rows x 256 weight rows, so one tile covers
+//          an expert's rows, each weight byte is read once and the
+//          workgroups of an XCD share the expert's rows through L2.  The
+//          wide weight tile halves how often the rows are re-read; LDS then
+//          holds two weight stages.
 //   Large  (many rows per expert): ping-pong tiles of 256 rows.
 #ifndef MOE_G1_SMALL
 #define MOE_G1_SMALL 32, 128, 1, 4, 2, 4
@@ -668,10 +678,10 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
 #define MOE_G2_SMALL 32, 128, 1, 4, 2, 4
 #endif
 #ifndef MOE_PP1_MEDIUM
-#define MOE_PP1_MEDIUM 320, 128, 4
+#define MOE_PP1_MEDIUM 320, 256, 2
 #endif
 #ifndef MOE_PP2_MEDIUM
-#define MOE_PP2_MEDIUM 320, 128, 4
+#define MOE_PP2_MEDIUM 320, 256, 2
 #endif
 #ifndef MOE_PP1_LARGE
 #define MOE_PP1_LARGE 256, 256, 3
