@@ -12,6 +12,21 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+#ifndef MOE_COMBINE_NV
+#define MOE_COMBINE_NV 2   // 16-byte vectors per lane per round
+#endif
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Loads and stores of rows that are touched once: nontemporal, so the
+// streams do not displace cached data.
+__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
+  const v4u q = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+  return make_uint4(q[0], q[1], q[2], q[3]);
+}
+__device__ __forceinline__ void store_stream(uint4 *p, const uint4 &v) {
+  __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u *>(p));
+}
 
 template <bool BF16>
 struct Vec;
@@ -50,7 +65,14 @@ struct Vec<false> {
   }
 };
 
-template <bool BF16>
+// One wave per token.  The token's k slots (packed positions and gates) are
+// read once into scalar registers; each lane then handles NV vectors of the
+// row per round, issuing the loads of all k rows (and the shared row) for all
+// NV vectors before the first add, so a round keeps NV (k + 1) loads in
+// flight.  The adds keep the fixed order slot 0 .. k-1, then the shared row.
+// The expert rows are read once and the output written once: both stream
+// with nontemporal accesses.
+template <bool BF16, int KMAX, int NV>
 __global__ __launch_bounds__(kThreads) void k_combine(const uint4 *__restrict__ y_perm, int T, int k,
                                                       int nvec, const int32_t *__restrict__ inv,
                                                       const float *__restrict__ w,
@@ -60,12 +82,64 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint4 *__restrict__ 
   const int t = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = lane_id();
+  int p[KMAX];
+  float g[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    p[j] = -1;
+    g[j] = 0.0f;
+    if (j < k) {
+      const int q = uniform(inv[(int64_t)t * k + j]);
+      p[j] = q >= 0 && q < M ? q : -1;
+      g[j] = __uint_as_float(uniform(__float_as_uint(w[(int64_t)t * k + j])));
+    }
+  }
+  for (int v0 = lane; v0 < nvec; v0 += NV * kWave) {
+    uint4 r[NV][KMAX + 1];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int v = v0 + u * kWave;
+      if (v < nvec) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if (p[j] >= 0) r[u][j] = load_stream(y_perm + (int64_t)p[j] * nvec + v);
+        if (y_sh) r[u][KMAX] = y_sh[(int64_t)t * nvec + v];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int v = v0 + u * kWave;
+      if (v < nvec) {
+        float acc[V::N];
+#pragma unroll
+        for (int i = 0; i < V::N; ++i) acc[i] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if (p[j] >= 0) V::add(acc, g[j], r[u][j]);
+        if (y_sh) V::add(acc, 1.0f, r[u][KMAX]);
+        store_stream(y + (int64_t)t * nvec + v, V::pack(acc));
+      }
+    }
+  }
+}
+
+// Any k up to 64: the slots are read inside the loop, four loads at a time.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_combine_anyk(const uint4 *__restrict__ y_perm, int T,
+                                                           int k, int nvec,
+                                                           const int32_t *__restrict__ inv,
+                                                           const float *__restrict__ w,
+                                                           const uint4 *__restrict__ y_sh, int64_t M,
+                                                           uint4 *__restrict__ y) {
+  using V = Vec<BF16>;
+  const int t = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = lane_id();
   for (int v = lane; v < nvec; v += kWave) {
     float acc[V::N];
 #pragma unroll
     for (int i = 0; i < V::N; ++i) acc[i] = 0.0f;
     int j = 0;
-    // Groups of four slots: issue the four loads, then accumulate in order.
     for (; j + 4 <= k; j += 4) {
       uint4 r[4];
       float g[4];
@@ -112,9 +186,29 @@ extern "C" moe_status moe_unpermute_combine(const void *y_perm, moe_dtype dt, in
   const uint4 *yp = static_cast<const uint4 *>(y_perm);
   const uint4 *ys = static_cast<const uint4 *>(y_shared);
   uint4 *out = static_cast<uint4 *>(y);
-  if (dt == MOE_BF16)
-    k_combine<true><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
-  else
-    k_combine<false><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+  constexpr int NV = MOE_COMBINE_NV;
+  if (dt == MOE_BF16) {
+    if (k == 1)
+      k_combine<true, 1, NV><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+    else if (k == 2)
+      k_combine<true, 2, NV><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+    else if (k <= 4)
+      k_combine<true, 4, NV><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+    else if (k <= 8)
+      k_combine<true, 8, NV><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+    else
+      k_combine_anyk<true><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+  } else {
+    if (k == 1)
+      k_combine<false, 1, NV><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+    else if (k == 2)
+      k_combine<false, 2, NV><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+    else if (k <= 4)
+      k_combine<false, 4, NV><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+    else if (k <= 8)
+      k_combine<false, 8, NV><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+    else
+      k_combine_anyk<false><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+  }
   return launch_status();
 }

@@ -10,7 +10,10 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;                // 4 waves per block
+constexpr int kThreads = 256;
+#ifndef MOE_SCATTER_NV
+#define MOE_SCATTER_NV 8   // 16-byte vectors per lane per round of the row scatter
+#endif                // 4 waves per block
 constexpr int kMaxChunks = 1024;
 
 // Assignments per chunk: at least 2048, and few enough chunks that the scan's
@@ -40,18 +43,23 @@ __global__ __launch_bounds__(kThreads) void k_hist(const int32_t *__restrict__ i
 // One block of 1024 threads, thread e owns expert e (E <= 1024).
 // counts[e] = sum over chunks; offsets = exclusive scan of counts;
 // hist[c][e] becomes the first packed position of chunk c's expert-e rows.
+// The chunk walks read kBatch chunks' counts at a time, so their loads are in
+// flight together instead of one L2 round trip per chunk.
 __global__ __launch_bounds__(1024) void k_scan(int32_t *__restrict__ hist, int nchunks, int E,
                                                int32_t *__restrict__ counts,
                                                int32_t *__restrict__ offsets) {
+  constexpr int kBatch = 8;
   __shared__ int wave_tot[16];
   const int e = threadIdx.x;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   int total = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = hist[(int64_t)c * E + e];
-      hist[(int64_t)c * E + e] = total;
-      total += v;
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = c0 + i < nchunks ? hist[(int64_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) total += v[i];
     }
     counts[e] = total;
   }
@@ -78,7 +86,17 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t *__restrict__ hist, int n
   if (e < E) {
     offsets[e] = excl;
     if (e == E - 1) offsets[E] = excl + total;
-    for (int c = 0; c < nchunks; ++c) hist[(int64_t)c * E + e] += excl;
+    int run = excl;
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = c0 + i < nchunks ? hist[(int64_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (c0 + i < nchunks) hist[(int64_t)(c0 + i) * E + e] = run;
+        run += v[i];
+      }
+    }
   }
 }
 
@@ -140,7 +158,18 @@ __global__ __launch_bounds__(kThreads) void k_multisplit(const int32_t *__restri
   }
 }
 
+// A store of data that is not read again soon (nontemporal: it does not
+// displace cached data on its way to HBM).
+__device__ __forceinline__ void store_stream(uint4 *p, const uint4 &v) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u *>(p));
+}
+
 // One wave per token: read the row once (16-byte vectors), write k copies.
+// Up to 64 NV vectors of the row are loaded into registers before the first
+// store, so those loads are in flight at once; the k copies then stream out
+// with nontemporal stores.  Longer rows take several rounds.
+template <int NV>
 __global__ __launch_bounds__(kThreads) void k_row_scatter(const uint4 *__restrict__ x, int T, int k,
                                                           int nvec, const int32_t *__restrict__ inv,
                                                           int64_t M, uint4 *__restrict__ x_perm) {
@@ -151,10 +180,10 @@ __global__ __launch_bounds__(kThreads) void k_row_scatter(const uint4 *__restric
   int dst[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) dst[j] = j < k ? uniform(inv[(int64_t)t * k + j]) : -1;
-  for (int v0 = 0; v0 < nvec; v0 += 4 * kWave) {
-    uint4 r[4];
+  for (int v0 = 0; v0 < nvec; v0 += NV * kWave) {
+    uint4 r[NV];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NV; ++u) {
       const int v = v0 + u * kWave + lane;
       if (v < nvec) r[u] = src[v];
     }
@@ -165,9 +194,9 @@ __global__ __launch_bounds__(kThreads) void k_row_scatter(const uint4 *__restric
       if (p < 0 || p >= M) continue;
       uint4 *out = x_perm + (int64_t)p * nvec;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < NV; ++u) {
         const int v = v0 + u * kWave + lane;
-        if (v < nvec) out[v] = r[u];
+        if (v < nvec) store_stream(out + v, r[u]);
       }
     }
   }
@@ -234,8 +263,8 @@ extern "C" moe_status moe_permute(const void *x, moe_dtype dt, int T, int d,
   const int nvec = (int)((int64_t)d * elem / 16);
   const dim3 grid((T + 3) / 4);
   if (k <= 16)
-    k_row_scatter<<<grid, dim3(kThreads), 0, stream>>>(static_cast<const uint4 *>(x), T, k, nvec,
-                                                        inv, M, static_cast<uint4 *>(x_perm));
+    k_row_scatter<MOE_SCATTER_NV><<<grid, dim3(kThreads), 0, stream>>>(
+        static_cast<const uint4 *>(x), T, k, nvec, inv, M, static_cast<uint4 *>(x_perm));
   else
     k_row_scatter_anyk<<<grid, dim3(kThreads), 0, stream>>>(static_cast<const uint4 *>(x), T, k,
                                                              nvec, inv, M,
