@@ -393,7 +393,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_grouped_gemm(
 // slice k, group 1 for weight slice k + 1 at the end of its last memory phase
 // of slice k -- both right before the barrier after which group 0 reads slice
 // k + 1.  A stage is refilled only after both groups' last reads of it.
-template <bool BF16, int BM, int BR, int SB, bool SWIGLU>
+template <bool BF16, int BM, int BR, int SB, bool SWIGLU, bool SPLIT>
 __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     const u32x4 *__restrict__ A, int M, int kvec, const int32_t *__restrict__ offsets, int G,
     const u32x4 *__restrict__ B, int64_t b_expert_vec, int64_t b_up_vec, int ntiles, int N,
@@ -408,6 +408,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
   static_assert(BM % 64 == 0 && (BR == 128 || BR == 256) && SB >= 2, "tile");
   static_assert((2 * ASTAGE + SB * BSTAGE) * 16 <= 160 * 1024, "LDS");
   static_assert(NLB * (SB - 1) < 64, "vmcnt");
+  static_assert(FM <= 5, "row blocks per wave");
 
   __shared__ u32x4 smem[2 * ASTAGE + SB * BSTAGE];
   u32x4 *const a_ring = smem;
@@ -476,9 +477,17 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
       wait_vmcnt((last - k) * (B_TOT / 4));
     };
 
-    f32x16 acc[FM][NB];
+    // The rest of the tile.  SPLIT: instantiated per number of live row
+    // blocks NL of this wave (the waves of a tile may differ), so the MFMA
+    // and epilogue code has no per-block branches -- for tiles that are
+    // often partly live.  Otherwise one body skips dead blocks at run time.
+    auto run_tile = [&](auto nl_tag, auto dyn_tag) {
+    constexpr int NL = decltype(nl_tag)::value;
+    constexpr bool DYN = decltype(dyn_tag)::value;   // NL = FM, blocks below live only
+    constexpr int NLM = NL > 0 ? NL : 1;
+    f32x16 acc[NLM][NB];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < NL; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -515,18 +524,18 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
         // overwrite): a use of every accumulator makes the compiler wait for
         // the MFMA results.
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < NL; ++i)
 #pragma unroll
           for (int j = 0; j < NB; ++j) asm volatile("" ::"v"(acc[i][j][0]));
         const u32x4 *As = a_ring + (kt & 1) * ASTAGE;
         const u32x4 *Bs = b_ring + (kt % SB) * BSTAGE;
-        u32x4 fa[2][FM], fb[2][NB];
+        u32x4 fa[2][NLM], fb[2][NB];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int cc = 2 * (2 * h + q) + (lane >> 5);
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-            if (i < live) fa[q][i] = As[swz((grp + 2 * (wm + WMG * i)) * 32 + (lane & 31), cc)];
+          for (int i = 0; i < NL; ++i)
+            if (!DYN || i < live) fa[q][i] = As[swz((grp + 2 * (wm + WMG * i)) * 32 + (lane & 31), cc)];
           fb[q][0] = Bs[swz(brow0 + (lane & 31), cc)];
           fb[q][1] = Bs[swz(brow1 + (lane & 31), cc)];
         }
@@ -545,8 +554,8 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-            if (i < live)
+          for (int i = 0; i < NL; ++i)
+            if (!DYN || i < live)
 #pragma unroll
               for (int j = 0; j < NB; ++j) Mma<BF16>::run(fa[q][i], fb[q][j], acc[i][j]);
         asm volatile("" ::: "memory");
@@ -563,8 +572,8 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     // register v, row 8 (v / 4) + 4 (l / 32) + v % 4.
     const int col_l = lane & 31, row_l = 4 * (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if (i >= live) continue;
+    for (int i = 0; i < NL; ++i) {
+      if (DYN && i >= live) continue;
       const int rblk = m0 + (grp + 2 * (wm + WMG * i)) * 32;
 #pragma unroll
       for (int j = 0; j < (SWIGLU ? 1 : 2); ++j) {
@@ -581,6 +590,21 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
               static_cast<float *>(C)[idx] = val;
           }
         }
+      }
+    }
+    };
+    using Dyn = std::true_type;
+    using Fixed = std::false_type;
+    if constexpr (!SPLIT) {
+      run_tile(std::integral_constant<int, FM>{}, Dyn{});
+    } else {
+      switch (live) {
+        case 5: if constexpr (FM >= 5) run_tile(std::integral_constant<int, 5>{}, Fixed{}); break;
+        case 4: if constexpr (FM >= 4) run_tile(std::integral_constant<int, 4>{}, Fixed{}); break;
+        case 3: if constexpr (FM >= 3) run_tile(std::integral_constant<int, 3>{}, Fixed{}); break;
+        case 2: if constexpr (FM >= 2) run_tile(std::integral_constant<int, 2>{}, Fixed{}); break;
+        case 1: run_tile(std::integral_constant<int, 1>{}, Fixed{}); break;
+        default: run_tile(std::integral_constant<int, 0>{}, Fixed{}); break;
       }
     }
   }
@@ -623,11 +647,13 @@ struct TileCfg {
   static constexpr bool PP = false;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, SA = SA_, SB = SB_;
 };
-// Ping-pong kernel: BM-row x BR-weight-row tiles, SB weight stages.
-template <int BM_, int BR_, int SB_>
+// Ping-pong kernel: BM-row x BR-weight-row tiles, SB weight stages; SPLIT: one
+// kernel body per live row-block count.
+template <int BM_, int BR_, int SB_, bool SPLIT_ = false>
 struct PpCfg {
   static constexpr bool PP = true;
   static constexpr int BM = BM_, BR = BR_, SB = SB_;
+  static constexpr bool SPLIT = SPLIT_;
 };
 
 template <bool BF16, bool SWIGLU, typename Cfg>
@@ -642,7 +668,7 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
     constexpr int BN = SWIGLU ? Cfg::BR / 2 : Cfg::BR;
     const int ntiles = N / BN;
     const int64_t mtiles_max = (M + Cfg::BM - 1) / Cfg::BM + G;
-    auto kern = k_grouped_gemm_pp<BF16, Cfg::BM, Cfg::BR, Cfg::SB, SWIGLU>;
+    auto kern = k_grouped_gemm_pp<BF16, Cfg::BM, Cfg::BR, Cfg::SB, SWIGLU, Cfg::SPLIT>;
     static int per_cu = 0;
     const int grid = persistent_grid((const void *)kern, 512, per_cu, mtiles_max * ntiles);
     kern<<<dim3(grid), dim3(512), 0, stream>>>(static_cast<const u32x4 *>(a), M, kvec, offsets, G,
@@ -678,10 +704,10 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
 #define MOE_G2_SMALL 32, 128, 1, 4, 2, 4
 #endif
 #ifndef MOE_PP1_MEDIUM
-#define MOE_PP1_MEDIUM 320, 256, 2
+#define MOE_PP1_MEDIUM 320, 256, 2, true
 #endif
 #ifndef MOE_PP2_MEDIUM
-#define MOE_PP2_MEDIUM 320, 256, 2
+#define MOE_PP2_MEDIUM 320, 256, 2, true
 #endif
 #ifndef MOE_PP1_LARGE
 #define MOE_PP1_LARGE 256, 256, 3
