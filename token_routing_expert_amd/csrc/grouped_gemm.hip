@@ -473,15 +473,20 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     // Group 1's wait for weight slice k: the weight slices after it that are
     // already issued (k + 1 .. k + SB - 2) may stay in flight.
     auto wait_b = [&](int k) {
-      const int last = k + SB - 2 < KT - 1 ? k + SB - 2 : KT - 1;
-      wait_vmcnt((last - k) * (B_TOT / 4));
+      constexpr int kSteady = (SB - 2) * (B_TOT / 4);
+      if (k + SB - 2 <= KT - 1) {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (kSteady & 15) | ((kSteady >> 4) << 14));
+      } else {
+        wait_vmcnt((KT - 1 - k) * (B_TOT / 4));
+      }
     };
 
     // The rest of the tile.  SPLIT: instantiated per number of live row
     // blocks NL of this wave (the waves of a tile may differ), so the MFMA
     // and epilogue code has no per-block branches -- for tiles that are
     // often partly live.  Otherwise one body skips dead blocks at run time.
-    auto run_tile = [&](auto nl_tag, auto dyn_tag) {
+    auto run_tile = [&](auto nl_tag, auto dyn_tag, auto grp_tag) {
+    constexpr int GRP = decltype(grp_tag)::value;   // this wave's group, as a constant
     constexpr int NL = decltype(nl_tag)::value;
     constexpr bool DYN = decltype(dyn_tag)::value;   // NL = FM, blocks below live only
     constexpr int NLM = NL > 0 ? NL : 1;
@@ -495,7 +500,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
 
     // Slice 0 (and the first weight slices), then group 1 starts one barrier late.
     asm volatile("" ::: "memory");
-    if (grp == 0) {
+    if (GRP == 0) {
       issue_a(0);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -509,7 +514,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (grp == 1) __builtin_amdgcn_s_barrier();
+    if (GRP == 1) __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
     // B fragment rows of this wave inside the weight tile.
@@ -535,18 +540,18 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
           const int cc = 2 * (2 * h + q) + (lane >> 5);
 #pragma unroll
           for (int i = 0; i < NL; ++i)
-            if (!DYN || i < live) fa[q][i] = As[swz((grp + 2 * (wm + WMG * i)) * 32 + (lane & 31), cc)];
+            if (!DYN || i < live) fa[q][i] = As[swz((GRP + 2 * (wm + WMG * i)) * 32 + (lane & 31), cc)];
           fb[q][0] = Bs[swz(brow0 + (lane & 31), cc)];
           fb[q][1] = Bs[swz(brow1 + (lane & 31), cc)];
         }
         if (h == 0) {
-          if (grp == 0 && kt + 1 < KT) issue_a(kt + 1);
-          if (grp == 1 && kt + SB - 1 < KT) issue_b(kt + SB - 1);
+          if (GRP == 0 && kt + 1 < KT) issue_a(kt + 1);
+          if (GRP == 1 && kt + SB - 1 < KT) issue_b(kt + SB - 1);
         }
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): reads done before the barrier
         // Group 0 reads slice kt + 1 right after the next barrier but one.
-        if (grp == 1 && h == 1 && kt + 1 < KT) wait_b(kt + 1);
+        if (GRP == 1 && h == 1 && kt + 1 < KT) wait_b(kt + 1);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -559,13 +564,13 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
 #pragma unroll
               for (int j = 0; j < NB; ++j) Mma<BF16>::run(fa[q][i], fb[q][j], acc[i][j]);
         asm volatile("" ::: "memory");
-        if (grp == 0 && h == 1 && kt + 1 < KT) __builtin_amdgcn_s_waitcnt(0x0F70);
+        if (GRP == 0 && h == 1 && kt + 1 < KT) __builtin_amdgcn_s_waitcnt(0x0F70);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       }
     }
-    if (grp == 0) __builtin_amdgcn_s_barrier();   // both groups leave the tile aligned
+    if (GRP == 0) __builtin_amdgcn_s_barrier();   // both groups leave the tile aligned
     asm volatile("" ::: "memory");
 
     // Epilogue.  MFMA 32x32 output layout: lane l holds column l % 32 and, in
@@ -574,7 +579,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       if (DYN && i >= live) continue;
-      const int rblk = m0 + (grp + 2 * (wm + WMG * i)) * 32;
+      const int rblk = m0 + (GRP + 2 * (wm + WMG * i)) * 32;
 #pragma unroll
       for (int j = 0; j < (SWIGLU ? 1 : 2); ++j) {
         const int col = n0 + (SWIGLU ? wn * 32 : wn * 64 + j * 32) + col_l;
@@ -595,18 +600,26 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     };
     using Dyn = std::true_type;
     using Fixed = std::false_type;
-    if constexpr (!SPLIT) {
-      run_tile(std::integral_constant<int, FM>{}, Dyn{});
-    } else {
-      switch (live) {
-        case 5: if constexpr (FM >= 5) run_tile(std::integral_constant<int, 5>{}, Fixed{}); break;
-        case 4: if constexpr (FM >= 4) run_tile(std::integral_constant<int, 4>{}, Fixed{}); break;
-        case 3: if constexpr (FM >= 3) run_tile(std::integral_constant<int, 3>{}, Fixed{}); break;
-        case 2: if constexpr (FM >= 2) run_tile(std::integral_constant<int, 2>{}, Fixed{}); break;
-        case 1: run_tile(std::integral_constant<int, 1>{}, Fixed{}); break;
-        default: run_tile(std::integral_constant<int, 0>{}, Fixed{}); break;
+    auto by_live = [&](auto g) {
+      if constexpr (!SPLIT) {
+        run_tile(std::integral_constant<int, FM>{}, Dyn{}, g);
+      } else {
+        switch (live) {
+          case 5: if constexpr (FM >= 5) run_tile(std::integral_constant<int, 5>{}, Fixed{}, g); break;
+          case 4: if constexpr (FM >= 4) run_tile(std::integral_constant<int, 4>{}, Fixed{}, g); break;
+          case 3: if constexpr (FM >= 3) run_tile(std::integral_constant<int, 3>{}, Fixed{}, g); break;
+          case 2: if constexpr (FM >= 2) run_tile(std::integral_constant<int, 2>{}, Fixed{}, g); break;
+          case 1: run_tile(std::integral_constant<int, 1>{}, Fixed{}, g); break;
+          default: run_tile(std::integral_constant<int, 0>{}, Fixed{}, g); break;
+        }
       }
-    }
+    };
+    // Each group runs its own copy of the tile code: the loads it issues and
+    // the waits it makes are fixed per group, so they need no branches.
+    if (grp == 0)
+      by_live(std::integral_constant<int, 0>{});
+    else
+      by_live(std::integral_constant<int, 1>{});
   }
 }
 
