@@ -165,7 +165,8 @@ moe_status moe_permute(const void *x, moe_dtype dt, int T, int d, const int32_t 
  * always-active shared expert is the same call with G = 1 and offsets {0, M}
  * ("Fine-grained vs coarse experts").
  * Errors: INVALID_ARG for null pointers, M < 0, G < 1, misalignment;
- * UNSUPPORTED for d or ffn not a multiple of 128, G > 4096, M >= 2^31.
+ * UNSUPPORTED for d or ffn not a multiple of 128, G > 4096, M >= 2^31, or
+ * one expert's gate and up matrices of 4 GiB or more (2 ffn d elem >= 2^32).
  * An offsets array that breaks its precondition is clamped to [0, M] and
  * never causes an out-of-bounds access.
  */

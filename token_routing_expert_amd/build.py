@@ -48,8 +48,21 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    _check_no_missing_kernels(LIB + ".tmp")
     os.replace(LIB + ".tmp", LIB)
     return LIB
+
+
+def _check_no_missing_kernels(path: str) -> None:
+    """Fail if the library references a symbol of its own namespace that it
+    does not define: the host side of a kernel can be left out without a
+    compile error, and the library would then fail to load."""
+    nm = "/opt/rocm/llvm/bin/llvm-nm" if os.path.exists("/opt/rocm/llvm/bin/llvm-nm") else "nm"
+    out = subprocess.run([nm, "-D", "--undefined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    missing = [line.split()[-1] for line in out.splitlines() if "_ZN3moe" in line]
+    if missing:
+        raise RuntimeError(f"{path}: undefined library symbols (kernel host stubs missing): {missing[:4]}")
 
 
 if __name__ == "__main__":

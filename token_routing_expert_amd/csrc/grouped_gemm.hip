@@ -378,22 +378,49 @@ __global__ __launch_bounds__(WM *WN * 64) void k_grouped_gemm(
 // rows [64 wn, 64 wn + 64) -- for SWIGLU 32 gate rows and their 32 up rows --
 // and the row blocks (32 rows each) g + 2 (wm + WMG i) of its group g.
 //
-// The two groups run the same program half a phase apart: each half K slice
-// (two k-groups) is a memory phase (LDS -> registers and issuing loads) and a
-// compute phase (MFMAs from registers), each closed by a barrier.  Group 1
+// The two groups run the same program half a phase apart: every two k-groups
+// (64 bytes of K) are a memory phase (LDS -> registers and issuing loads) and
+// a compute phase (MFMAs from registers), each closed by a barrier.  Group 1
 // starts one barrier late, so while one group issues MFMAs the other works
 // on memory, and the matrix cores of each SIMD stay busy.
 //
-// Direct global-to-LDS loads (global_load_lds_dwordx4) bring 128-byte K
-// slices; group 0 loads the row tile into a ring of 2 stages, one slice
-// ahead, group 1 the weight tile into a ring of SB stages, SB - 1 slices
-// ahead, so each wave's vmcnt queue holds one operand.  A slice is visible
-// to every wave after the first barrier that follows all its loaders' waits:
-// group 0 waits for row slice k + 1 at the end of its last compute phase of
-// slice k, group 1 for weight slice k + 1 at the end of its last memory phase
-// of slice k -- both right before the barrier after which group 0 reads slice
-// k + 1.  A stage is refilled only after both groups' last reads of it.
-template <bool BF16, int BM, int BR, int SB, bool SWIGLU, bool SPLIT>
+// K is staged in slices of 16 CPR bytes per row (CPR = 8: 128 bytes, two
+// phase pairs per slice; CPR = 4: 64 bytes, one).  Narrow slices make the
+// ring stages small, so more of them fit: the weight tile, streamed from HBM,
+// can then be requested several phases before it is read.  Direct
+// global-to-LDS loads (one wave instruction = 1 KB = 64 / CPR rows); group 0
+// loads the row tile into a ring of SA stages, SA - 1 slices ahead, group 1
+// the weight tile into a ring of SB stages, SB - 1 slices ahead, so each
+// wave's vmcnt queue holds one operand.  A slice is visible to every wave
+// after the first barrier that follows all its loaders' waits: group 0 waits
+// for row slice k + 1 at the end of its last compute phase of slice k, group
+// 1 for weight slice k + 1 at the end of its last memory phase of slice k --
+// both right before the barrier after which group 0 reads slice k + 1.  A
+// stage is refilled only after both groups' last reads of it.
+// Fourth word of a raw buffer resource on gfx9-class GPUs: 32-bit data
+// format, no swizzle, no stride; accesses at or past the byte count return 0.
+constexpr int kBufferFlags = 0x00020000;
+
+// One wave's 16-byte-per-lane buffer load straight into LDS: lane l's data
+// lands at lds + 16 l.  base/bytes describe the buffer; voff is the lane's
+// byte offset, soff a wave-uniform byte offset added to it.
+__device__ __forceinline__ void buffer_load_lds16(const void *base, uint32_t bytes, u32x4 *lds,
+                                                  uint32_t voff, uint32_t soff) {
+  const __amdgpu_buffer_rsrc_t res =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (__attribute__((address_space(3))) void *)lds, 16,
+                                           voff, soff, 0, 0);
+}
+
+template <int CPR>
+__device__ __forceinline__ int swz_c(int r, int cc) {
+  if constexpr (CPR == 8)
+    return swz(r, cc);
+  else
+    return r * 4 + (cc ^ ((r >> 2) & 3));   // 16 consecutive rows at one chunk: all banks once
+}
+
+template <bool BF16, int BM, int BR, int SA, int SB, int CPR, bool SWIGLU, bool SPLIT>
 __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     const u32x4 *__restrict__ A, int M, int kvec, const int32_t *__restrict__ offsets, int G,
     const u32x4 *__restrict__ B, int64_t b_expert_vec, int64_t b_up_vec, int ntiles, int N,
@@ -402,24 +429,31 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
   constexpr int WNG = BR / 64, WMG = 4 / WNG;    // waves of a group across N and M
   constexpr int FM = (BM / 64 + WMG - 1) / WMG;  // row blocks per wave
   constexpr int NB = 2;                          // B fragments per k-group
-  constexpr int ASTAGE = BM * 8, BSTAGE = BR * 8;   // 16-byte chunks per stage
-  constexpr int A_TOT = BM / 8, B_TOT = BR / 8;  // 8-row DMA groups per slice
-  constexpr int NLB = (B_TOT + 3) / 4;           // weight loads per group-1 wave per slice
-  static_assert(BM % 64 == 0 && (BR == 128 || BR == 256) && SB >= 2, "tile");
-  static_assert((2 * ASTAGE + SB * BSTAGE) * 16 <= 160 * 1024, "LDS");
-  static_assert(NLB * (SB - 1) < 64, "vmcnt");
+  constexpr int NH = CPR / 4;                    // phase pairs per slice
+  constexpr int RPI = 64 / CPR;                  // rows per DMA instruction
+  constexpr int ASTAGE = BM * CPR, BSTAGE = BR * CPR;   // 16-byte chunks per stage
+  constexpr int A_TOT = BM / RPI, B_TOT = BR / RPI;     // DMA groups per slice
+  constexpr int NLB = B_TOT / 4;                 // weight loads per group-1 wave per slice
+  static_assert(CPR == 4 || CPR == 8, "slice width");
+  static_assert(BM % 64 == 0 && BM % RPI == 0 && (BR == 128 || BR == 256) && B_TOT % 4 == 0, "tile");
+  static_assert(SA >= 2 && SB >= 2, "rings");
+  static_assert((SA * ASTAGE + SB * BSTAGE) * 16 <= 160 * 1024, "LDS");
+  static_assert(NLB * (SB - 2) < 64 && ((A_TOT + 3) / 4) * (SA - 2) < 64, "vmcnt");
   static_assert(FM <= 5, "row blocks per wave");
 
-  __shared__ u32x4 smem[2 * ASTAGE + SB * BSTAGE];
+  __shared__ u32x4 smem[SA * ASTAGE + SB * BSTAGE];
   u32x4 *const a_ring = smem;
-  u32x4 *const b_ring = smem + 2 * ASTAGE;
+  u32x4 *const b_ring = smem + SA * ASTAGE;
 
   const int lane = lane_id();
   const int wave = uniform(threadIdx.x >> 6);
   const int grp = wave >> 2, wq = wave & 3;
   const int wn = wq % WNG, wm = wq / WNG;
-  const int ld_row = lane >> 3, ld_slot = lane & 7;
-  const int KT = kvec / 8;
+  // DMA lane mapping: lane l fills row l / CPR of its group, LDS slot l % CPR,
+  // which holds global chunk (l % CPR) ^ key(row); the key of a group's rows
+  // depends on the group only through its parity (CPR = 8) or not at all.
+  const int ld_row = lane / CPR, ld_slot = lane % CPR;
+  const int KT = kvec / CPR;
 
   const int xcd = blockIdx.x % kXcds, nj = gridDim.x / kXcds;
   const int total = count_tiles<BM>(offsets, G, M, ntiles);
@@ -438,47 +472,65 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     live = live < 0 ? 0 : (live > FM ? FM : live);
 
     // Group 0: row groups wq, wq + 4, ... whose first row is live (rows past
-    // the segment end re-read its last row; their results are never stored).
-    // Group 1: weight groups wq, wq + 4, ...
-    const int a_groups = (rows + 7) / 8 < A_TOT ? (rows + 7) / 8 : A_TOT;
-    const u32x4 *bexp = B + (int64_t)tile.expert * b_expert_vec;
-    auto issue_a = [&](int kt) {
-      u32x4 *stage = a_ring + (kt & 1) * ASTAGE;
-#pragma unroll 1
-      for (int g = wq; g < a_groups; g += 4) {
-        int row = m0 + g * 8 + ld_row;
-        row = row < hi ? row : hi - 1;
-        const uint32_t key = ld_row ^ (g & 1);   // swz_key(8 g + ld_row)
-        __builtin_amdgcn_global_load_lds(
-            (const void *)(A + (int64_t)row * kvec + kt * 8 + (ld_slot ^ key)),
-            (__attribute__((address_space(3))) void *)(stage + g * 64), 16, 0, 0);
+    // the segment end re-read its last row; their results are never stored);
+    // na of them per slice.  Group 1: weight groups wq, wq + 4, ...
+    const int a_groups = (rows + RPI - 1) / RPI < A_TOT ? (rows + RPI - 1) / RPI : A_TOT;
+    const int na = a_groups > wq ? (a_groups - wq + 3) / 4 : 0;
+    auto key_of = [&](int g) -> uint32_t {
+      return CPR == 8 ? (uint32_t)(ld_row ^ (g & 1)) : (uint32_t)((ld_row >> 2) & 3);
+    };
+    // Buffer-to-LDS loads: a resource per operand tile (the row tile from row
+    // m0, the expert's weights), a per-lane 32-bit byte offset fixed for the
+    // tile, and the K position as the scalar offset -- a K step costs no
+    // address arithmetic.
+    constexpr int NLA = (A_TOT + 3) / 4;           // row loads per group-0 wave per slice, at most
+    const u32x4 *a_base = A + (int64_t)m0 * kvec;
+    const uint32_t a_bytes = (uint32_t)((int64_t)rows * kvec * 16);
+    const u32x4 *b_base = B + (int64_t)tile.expert * b_expert_vec;
+    const uint32_t b_bytes = (uint32_t)(b_expert_vec * 16);
+    auto a_offsets = [&](uint32_t (&off)[NLA]) {
+#pragma unroll
+      for (int r = 0; r < NLA; ++r) {
+        const int g = wq + 4 * r;
+        int row = g * RPI + ld_row;
+        row = row < rows ? row : rows - 1;
+        off[r] = ((uint32_t)row * (uint32_t)kvec + ((uint32_t)ld_slot ^ key_of(g))) * 16u;
       }
     };
-    auto issue_b = [&](int kt) {
-      u32x4 *stage = b_ring + (kt % SB) * BSTAGE;
+    auto b_offsets = [&](uint32_t (&off)[NLB]) {
 #pragma unroll
       for (int r = 0; r < NLB; ++r) {
         const int g = wq + 4 * r;
-        if (g < B_TOT) {
-          const int brow = g * 8 + ld_row;
-          const uint32_t key = ld_row ^ (g & 1);
-          const u32x4 *src = bexp + (SWIGLU && brow >= BN ? b_up_vec + (int64_t)(n0 + brow - BN) * kvec
-                                                          : (int64_t)(n0 + brow) * kvec);
-          __builtin_amdgcn_global_load_lds(
-              (const void *)(src + kt * 8 + (ld_slot ^ key)),
-              (__attribute__((address_space(3))) void *)(stage + g * 64), 16, 0, 0);
-        }
+        const int brow = g * RPI + ld_row;
+        off[r] = ((SWIGLU && brow >= BN ? (uint32_t)b_up_vec + (uint32_t)(n0 + brow - BN) * kvec
+                                        : (uint32_t)(n0 + brow) * (uint32_t)kvec) +
+                  ((uint32_t)ld_slot ^ key_of(g))) * 16u;
       }
     };
-    // Group 1's wait for weight slice k: the weight slices after it that are
-    // already issued (k + 1 .. k + SB - 2) may stay in flight.
+    auto issue_a = [&](int kt, const uint32_t (&off)[NLA]) {
+      u32x4 *stage = a_ring + (kt % SA) * ASTAGE;
+#pragma unroll
+      for (int r = 0; r < NLA; ++r)
+        if (r < na) buffer_load_lds16(a_base, a_bytes, stage + (wq + 4 * r) * 64, off[r], kt * CPR * 16);
+    };
+    auto issue_b = [&](int kt, const uint32_t (&off)[NLB]) {
+      u32x4 *stage = b_ring + (kt % SB) * BSTAGE;
+#pragma unroll
+      for (int r = 0; r < NLB; ++r)
+        buffer_load_lds16(b_base, b_bytes, stage + (wq + 4 * r) * 64, off[r], kt * CPR * 16);
+    };
+    // Waits for slice k of this wave's operand: the slices after it that are
+    // already issued (up to k + S - 2) may stay in flight.
     auto wait_b = [&](int k) {
-      constexpr int kSteady = (SB - 2) * (B_TOT / 4);
-      if (k + SB - 2 <= KT - 1) {
+      constexpr int kSteady = (SB - 2) * NLB;
+      if (k + SB - 2 <= KT - 1)
         __builtin_amdgcn_s_waitcnt(0x0F70 | (kSteady & 15) | ((kSteady >> 4) << 14));
-      } else {
-        wait_vmcnt((KT - 1 - k) * (B_TOT / 4));
-      }
+      else
+        wait_vmcnt((KT - 1 - k) * NLB);
+    };
+    auto wait_a = [&](int k) {
+      const int last = k + SA - 2 < KT - 1 ? k + SA - 2 : KT - 1;
+      wait_vmcnt((last - k) * na);
     };
 
     // The rest of the tile.  SPLIT: instantiated per number of live row
@@ -498,16 +550,24 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    // Slice 0 (and the first weight slices), then group 1 starts one barrier late.
+    // Slices 0 .. S - 2 of this wave's operand, wait for slice 0, then group
+    // 1 starts one barrier late.
+    uint32_t off[GRP == 0 ? NLA : NLB];
+    if constexpr (GRP == 0)
+      a_offsets(off);
+    else
+      b_offsets(off);
     asm volatile("" ::: "memory");
-    if (GRP == 0) {
-      issue_a(0);
+    if constexpr (GRP == 0) {
+#pragma unroll
+      for (int s = 0; s < SA - 1; ++s)
+        if (s < KT) issue_a(s, off);
       asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+      wait_a(0);
     } else {
 #pragma unroll
       for (int s = 0; s < SB - 1; ++s)
-        if (s < KT) issue_b(s);
+        if (s < KT) issue_b(s, off);
       asm volatile("" ::: "memory");
       wait_b(0);
     }
@@ -523,7 +583,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
 
     for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < NH; ++h) {
         // Memory phase.  First let the previous compute phase's MFMAs drain
         // (they may still read the fragment registers the loads below
         // overwrite): a use of every accumulator makes the compiler wait for
@@ -532,7 +592,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
         for (int i = 0; i < NL; ++i)
 #pragma unroll
           for (int j = 0; j < NB; ++j) asm volatile("" ::"v"(acc[i][j][0]));
-        const u32x4 *As = a_ring + (kt & 1) * ASTAGE;
+        const u32x4 *As = a_ring + (kt % SA) * ASTAGE;
         const u32x4 *Bs = b_ring + (kt % SB) * BSTAGE;
         u32x4 fa[2][NLM], fb[2][NB];
 #pragma unroll
@@ -540,18 +600,22 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
           const int cc = 2 * (2 * h + q) + (lane >> 5);
 #pragma unroll
           for (int i = 0; i < NL; ++i)
-            if (!DYN || i < live) fa[q][i] = As[swz((GRP + 2 * (wm + WMG * i)) * 32 + (lane & 31), cc)];
-          fb[q][0] = Bs[swz(brow0 + (lane & 31), cc)];
-          fb[q][1] = Bs[swz(brow1 + (lane & 31), cc)];
+            if (!DYN || i < live)
+              fa[q][i] = As[swz_c<CPR>((GRP + 2 * (wm + WMG * i)) * 32 + (lane & 31), cc)];
+          fb[q][0] = Bs[swz_c<CPR>(brow0 + (lane & 31), cc)];
+          fb[q][1] = Bs[swz_c<CPR>(brow1 + (lane & 31), cc)];
         }
         if (h == 0) {
-          if (GRP == 0 && kt + 1 < KT) issue_a(kt + 1);
-          if (GRP == 1 && kt + SB - 1 < KT) issue_b(kt + SB - 1);
+          if constexpr (GRP == 0) {
+            if (kt + SA - 1 < KT) issue_a(kt + SA - 1, off);
+          } else {
+            if (kt + SB - 1 < KT) issue_b(kt + SB - 1, off);
+          }
         }
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): reads done before the barrier
         // Group 0 reads slice kt + 1 right after the next barrier but one.
-        if (GRP == 1 && h == 1 && kt + 1 < KT) wait_b(kt + 1);
+        if (GRP == 1 && h == NH - 1 && kt + 1 < KT) wait_b(kt + 1);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -564,7 +628,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
 #pragma unroll
               for (int j = 0; j < NB; ++j) Mma<BF16>::run(fa[q][i], fb[q][j], acc[i][j]);
         asm volatile("" ::: "memory");
-        if (GRP == 0 && h == 1 && kt + 1 < KT) __builtin_amdgcn_s_waitcnt(0x0F70);
+        if (GRP == 0 && h == NH - 1 && kt + 1 < KT) wait_a(kt + 1);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -660,12 +724,13 @@ struct TileCfg {
   static constexpr bool PP = false;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, SA = SA_, SB = SB_;
 };
-// Ping-pong kernel: BM-row x BR-weight-row tiles, SB weight stages; SPLIT: one
-// kernel body per live row-block count.
-template <int BM_, int BR_, int SB_, bool SPLIT_ = false>
+// Ping-pong kernel: BM-row x BR-weight-row tiles, K slices of 16 CPR bytes,
+// SA row-tile and SB weight-tile ring stages; SPLIT: one kernel body per live
+// row-block count.
+template <int BM_, int BR_, int SA_, int SB_, int CPR_, bool SPLIT_>
 struct PpCfg {
   static constexpr bool PP = true;
-  static constexpr int BM = BM_, BR = BR_, SB = SB_;
+  static constexpr int BM = BM_, BR = BR_, SA = SA_, SB = SB_, CPR = CPR_;
   static constexpr bool SPLIT = SPLIT_;
 };
 
@@ -681,7 +746,7 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
     constexpr int BN = SWIGLU ? Cfg::BR / 2 : Cfg::BR;
     const int ntiles = N / BN;
     const int64_t mtiles_max = (M + Cfg::BM - 1) / Cfg::BM + G;
-    auto kern = k_grouped_gemm_pp<BF16, Cfg::BM, Cfg::BR, Cfg::SB, SWIGLU, Cfg::SPLIT>;
+    auto kern = k_grouped_gemm_pp<BF16, Cfg::BM, Cfg::BR, Cfg::SA, Cfg::SB, Cfg::CPR, SWIGLU, Cfg::SPLIT>;
     static int per_cu = 0;
     const int grid = persistent_grid((const void *)kern, 512, per_cu, mtiles_max * ntiles);
     kern<<<dim3(grid), dim3(512), 0, stream>>>(static_cast<const u32x4 *>(a), M, kvec, offsets, G,
@@ -707,8 +772,8 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
 //          ping-pong tiles of 320 rows x 256 weight rows, so one tile covers
 //          an expert's rows, each weight byte is read once and the
 //          workgroups of an XCD share the expert's rows through L2.  The
-//          wide weight tile halves how often the rows are re-read; LDS then
-//          holds two weight stages.
+//          wide weight tile halves how often the rows are re-read; 64-byte K
+//          slices let LDS hold 6 weight stages, 5 slices ahead.
 //   Large  (many rows per expert): ping-pong tiles of 256 rows.
 #ifndef MOE_G1_SMALL
 #define MOE_G1_SMALL 32, 128, 1, 4, 2, 4
@@ -717,16 +782,16 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
 #define MOE_G2_SMALL 32, 128, 1, 4, 2, 4
 #endif
 #ifndef MOE_PP1_MEDIUM
-#define MOE_PP1_MEDIUM 320, 256, 2, true
+#define MOE_PP1_MEDIUM 320, 256, 3, 6, 4, true
 #endif
 #ifndef MOE_PP2_MEDIUM
-#define MOE_PP2_MEDIUM 320, 256, 2, true
+#define MOE_PP2_MEDIUM 320, 256, 3, 6, 4, true
 #endif
 #ifndef MOE_PP1_LARGE
-#define MOE_PP1_LARGE 256, 256, 3
+#define MOE_PP1_LARGE 256, 256, 2, 3, 8, false
 #endif
 #ifndef MOE_PP2_LARGE
-#define MOE_PP2_LARGE 256, 256, 3
+#define MOE_PP2_LARGE 256, 256, 2, 3, 8, false
 #endif
 using G1Small = TileCfg<MOE_G1_SMALL>;
 using G2Small = TileCfg<MOE_G2_SMALL>;
@@ -780,6 +845,8 @@ moe_status check_shape(moe_dtype dt, int M, int d, int ffn, int G) {
   const int64_t elem = dt == MOE_F32 ? 4 : 2, big = (int64_t)1 << 31;
   const int64_t krow = (int64_t)(d > ffn ? d : ffn) * elem / 16;
   if ((int64_t)M * krow >= big || (int64_t)2 * ffn * d * elem / 16 >= big) return MOE_ERR_UNSUPPORTED;
+  // Byte offsets inside one expert's weights are 32-bit in the ping-pong kernel.
+  if ((int64_t)2 * ffn * d * elem >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
