@@ -638,8 +638,12 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     asm volatile("" ::: "memory");
 
     // Epilogue.  MFMA 32x32 output layout: lane l holds column l % 32 and, in
-    // register v, row 8 (v / 4) + 4 (l / 32) + v % 4.
+    // register v, row 8 (v / 4) + 4 (l / 32) + v % 4.  bf16 output: adjacent
+    // lanes (columns c, c + 1) trade values so each holds two columns of one
+    // row, and one 4-byte store writes the pair -- even lanes rows t = 0, 2 of
+    // each group of four rows, odd lanes rows t = 1, 3.
     const int col_l = lane & 31, row_l = 4 * (lane >> 5);
+    const bool odd = lane & 1;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       if (DYN && i >= live) continue;
@@ -647,16 +651,31 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
 #pragma unroll
       for (int j = 0; j < (SWIGLU ? 1 : 2); ++j) {
         const int col = n0 + (SWIGLU ? wn * 32 : wn * 64 + j * 32) + col_l;
+        float val[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = rblk + 8 * (v >> 2) + row_l + (v & 3);
-          if (row < hi) {
-            const float val = SWIGLU ? silu(acc[i][0][v]) * acc[i][1][v] : acc[i][j][v];
-            const int64_t idx = (int64_t)row * N + col;
-            if (BF16)
-              static_cast<uint16_t *>(C)[idx] = (uint16_t)f32_to_bf16_rne(val);
-            else
-              static_cast<float *>(C)[idx] = val;
+        for (int v = 0; v < 16; ++v) val[v] = SWIGLU ? silu(acc[i][0][v]) * acc[i][1][v] : acc[i][j][v];
+        if constexpr (BF16) {
+          uint32_t *out = static_cast<uint32_t *>(C);
+          const int c0 = col & ~1;
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {
+            // Rows t = v % 4 (even lanes keep it) and t + 1 (odd lanes).
+            const float mine = odd ? val[v + 1] : val[v];
+            const float give = odd ? val[v] : val[v + 1];
+            const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0xB1, 0xF, 0xF, false));
+            const float lo = odd ? got : mine, hi2 = odd ? mine : got;   // columns c0, c0 + 1
+            const int row = rblk + 8 * (v >> 2) + row_l + (v & 3) + (odd ? 1 : 0);
+            if (row < hi) {
+              typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+              const bf16x2 pk = {(__bf16)lo, (__bf16)hi2};
+              out[((int64_t)row * N + c0) >> 1] = __builtin_bit_cast(uint32_t, pk);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = rblk + 8 * (v >> 2) + row_l + (v & 3);
+            if (row < hi) static_cast<float *>(C)[(int64_t)row * N + col] = val[v];
           }
         }
       }
