@@ -26,11 +26,12 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def stage_bytes(cfg):
-    """Algorithmic HBM bytes of the permute and combine stages (per layer)."""
+def stage_bytes(cfg, gather=False):
+    """Algorithmic HBM bytes of the permute and combine stages (per layer).
+    With gather the permute computes indices only (ids in, order and inv out)."""
     s = cfg.elem_bytes
     T, k, d = cfg.T, cfg.k, cfg.d
-    permute = T * (d * s + k * d * s + 12 * k)     # read x once, write k copies, ids/order/inv
+    permute = T * 12 * k if gather else T * (d * s + k * d * s + 12 * k)   # x once, k copies
     combine = T * (k * d * s + d * s + 8 * k + (d * s if cfg.shared else 0))
     return permute, combine
 
@@ -44,13 +45,15 @@ def expert_flops(cfg):
     return gate_up, down, shared
 
 
-def gate_up_bytes(cfg, counts):
+def gate_up_bytes(cfg, counts, gather=False):
     """Algorithmic HBM bytes of the routed gate/up launch: the gate and up
-    weights of every expert that has rows, the packed rows once, h written."""
+    weights of every expert that has rows, each packed row once (with gather
+    read from x through order), h written."""
     s = cfg.elem_bytes
     touched = int((counts > 0).sum())
     M = cfg.T * cfg.k
-    return touched * 2 * cfg.ffn * cfg.d * s + M * cfg.d * s + M * cfg.ffn * s
+    return (touched * 2 * cfg.ffn * cfg.d * s + M * cfg.d * s + M * cfg.ffn * s
+            + (4 * M if gather else 0))
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -123,6 +126,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=("gather", "packed"), default="gather",
+                    help="gather: the first expert product reads token rows through the "
+                         "permutation; packed: the permute writes the packed copy X[order]")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -152,7 +158,7 @@ def main():
         ids_in = w_in = None
     log(f"generated in {time.perf_counter() - t0:.1f} s; uploading")
     layer = MoeLayer(cfg, x, w13, w2, logits=logits, sh_w13=sh[0], sh_w2=sh[1],
-                     topk_ids=ids_in, topk_w=w_in)
+                     topk_ids=ids_in, topk_w=w_in, fused_gather=args.path == "gather")
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -199,8 +205,9 @@ def main():
     counts = to_host(layer.counts)
     f_gate_up, f_down, f_shared = expert_flops(cfg)
     peak = PEAK_MFMA[cfg.dtype]
-    b_perm, b_comb = stage_bytes(cfg)
-    b_gate_up = gate_up_bytes(cfg, counts)
+    gather = args.path == "gather"
+    b_perm, b_comb = stage_bytes(cfg, gather)
+    b_gate_up = gate_up_bytes(cfg, counts, gather)
     stage_info = {}
     for name in stages:
         ms = stage_ms[name]
@@ -234,10 +241,11 @@ def main():
         "config": {
             "workload": cfg.name, "T": cfg.T, "E": cfg.E, "k": cfg.k, "d": cfg.d, "ffn": cfg.ffn,
             "gating": cfg.gating, "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups,
-            "shared_experts": int(cfg.shared), "n_ep_simulated": cfg.n_ep,
+            "shared_experts": int(cfg.shared), "n_ep_simulated": cfg.n_ep, "path": args.path,
         },
         "roofline": {
-            "kernel": "moe_grouped_gate_up: routed gate/up products + SwiGLU (one launch)",
+            "kernel": ("moe_grouped_gate_up_gather" if gather else "moe_grouped_gate_up")
+                      + ": routed gate/up products + SwiGLU (one launch)",
             "bound": "mfma",
             "achieved": round(achieved / 1e12, 2),
             "peak": peak / 1e12,

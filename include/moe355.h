@@ -133,9 +133,12 @@ size_t moe_permute_workspace_bytes(int T, int k, int E);
  *   x_perm     [M, d] out, dtype dt.
  *   workspace  at least moe_permute_workspace_bytes(T, k, E) bytes of device
  *              scratch owned by the caller; its contents on entry do not matter.
- * Errors: INVALID_ARG for null pointers, T < 0, k < 1, E < 1, workspace too
- * small, misaligned x / x_perm; UNSUPPORTED for E > 1024, d % 8 != 0, or
- * T k >= 2^31.
+ * Index-only mode: x and x_perm both NULL computes counts, offsets, order and
+ * inv and copies no rows (for moe_grouped_gate_up_gather, which reads the rows
+ * of x through order itself).
+ * Errors: INVALID_ARG for null pointers (exactly one of x, x_perm NULL
+ * included), T < 0, k < 1, E < 1, workspace too small, misaligned x / x_perm;
+ * UNSUPPORTED for E > 1024, d % 8 != 0, or T k >= 2^31.
  */
 moe_status moe_permute(const void *x, moe_dtype dt, int T, int d, const int32_t *topk_ids,
                        int k, int E, int32_t *counts, int32_t *offsets, int32_t *order,
@@ -193,6 +196,28 @@ moe_status moe_grouped_gate_up(const void *a, moe_dtype dt, int M, int d, int ff
 moe_status moe_grouped_down(const void *h, moe_dtype dt, int M, int ffn, int d,
                             const int32_t *offsets, int G, const void *w2, void *y,
                             hipStream_t stream);
+
+/*
+ * moe_grouped_gate_up with the permute's row copy folded into the product's
+ * loads ("Token permutation and grouped GEMMs": X[order] is only ever read by
+ * the first expert product, so the rows can be gathered where they are
+ * consumed).  Packed row p is token order[p] / k of x; the result is
+ * bit-identical to moe_permute's x_perm followed by moe_grouped_gate_up.
+ *
+ *   x        [T, d] activations in token order, dtype dt.
+ *   k        assignments per token (M = T k packed rows).
+ *   order    [M] int32 from moe_permute (its index-only mode suffices); every
+ *            entry must lie in [0, M).
+ *   offsets, w13, h, G, d, ffn as in moe_grouped_gate_up.
+ * Errors: those of moe_grouped_gate_up with M = T k, and INVALID_ARG for
+ * k < 1 or a null order; UNSUPPORTED also for x of 4 GiB or more
+ * (T d elem >= 2^32) or T k >= 2^31.  An order entry outside [0, M) is outside
+ * the contract: the read it steers is bounded by x's extent, the row it
+ * produces is undefined.
+ */
+moe_status moe_grouped_gate_up_gather(const void *x, moe_dtype dt, int T, int k, int d,
+                                      int ffn, const int32_t *order, const int32_t *offsets,
+                                      int G, const void *w13, void *h, hipStream_t stream);
 
 /*
  * Unpermute and weight (step 7; "Token permutation and grouped GEMMs":

@@ -119,6 +119,28 @@ def test_grouped_halves_validation(lib):
         assert f(*args(0, 128, 256, NULL, 4, NULL)) == 0           # M = 0: no-op
 
 
+def test_gate_up_gather_validation(lib):
+    f = lib.moe_grouped_gate_up_gather
+    a = ctypes.c_void_p(16)
+    #       x  dt T  k  d    ffn  order off G  w13 h  stream
+    assert f(a, 1, 8, 0, 128, 256, a, a, 4, a, a, NULL) == INVALID          # k < 1
+    assert f(a, 1, 8, 2, 96, 256, a, a, 4, a, a, NULL) == UNSUPPORTED       # d % 128
+    assert f(a, 1, 8, 2, 128, 256, NULL, a, 4, a, a, NULL) == INVALID       # null order
+    assert f(a, 1, 8, 2, 128, 256, a, a, 4, a, ctypes.c_void_p(24), NULL) == INVALID
+    assert f(a, 1, 1 << 20, 2, 4096, 256, a, a, 4, a, a, NULL) == UNSUPPORTED  # x >= 4 GiB
+    assert f(a, 1, 1 << 30, 2, 128, 256, a, a, 4, a, a, NULL) == UNSUPPORTED   # T k >= 2^31
+    assert f(NULL, 1, 0, 2, 128, 256, NULL, NULL, 4, NULL, NULL, NULL) == 0  # T = 0: no-op
+
+
+def test_permute_index_only_validation(lib):
+    f = lib.moe_permute
+    a = ctypes.c_void_p(16)
+    ws = lib.moe_permute_workspace_bytes(8, 2, 4)
+    #       x     dt T  d   ids k  E  counts off order inv x_perm ws  bytes
+    assert f(a, 1, 8, 16, a, 2, 4, a, a, a, a, NULL, a, ws, NULL) == INVALID   # x without x_perm
+    assert f(NULL, 1, 8, 16, a, 2, 4, a, a, a, a, a, a, ws, NULL) == INVALID   # x_perm without x
+
+
 def test_combine_validation(lib):
     f = lib.moe_unpermute_combine
     a = ctypes.c_void_p(16)

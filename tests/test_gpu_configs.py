@@ -1,6 +1,9 @@
 """GPU parity at the five full-size workloads, through the same MoeLayer chain
-that bench.py times.  Routing ids, send counts, counts, offsets, order and inv
-are compared bit for bit over every token; packed rows bitwise; expert outputs
+that bench.py times (the fused-gather path: index-only permute, first expert
+product reading token rows through order).  Routing ids, send counts, counts,
+offsets, order and inv are compared bit for bit over every token; packed rows
+of the row-copying permute bitwise, and the row-copying path's layer output
+bitwise against the fused path's; expert outputs
 and layer outputs against the oracle's fp64 evaluation, on every token for the
 small fp32 layer and the decode batch and on a seeded 256-token sample for the
 large ones.  Tolerances: fp32 per-row max |gpu - oracle| <= 1e-4 max |oracle|;
@@ -60,7 +63,7 @@ def case(request):
         c.ids_in = c.w_in = None
     log(f"{cfg.name}: uploading")
     layer = MoeLayer(cfg, c.x, c.w13, c.w2, logits=c.logits, sh_w13=c.sh[0], sh_w2=c.sh[1],
-                     topk_ids=c.ids_in, topk_w=c.w_in)
+                     topk_ids=c.ids_in, topk_w=c.w_in, fused_gather=True)
     log(f"{cfg.name}: forward")
     layer.forward()
     torch.cuda.synchronize()
@@ -121,12 +124,34 @@ def test_permute_indices(case):
 
 
 def test_packed_rows(case):
-    cfg = case.cfg
+    """The row-copying permute on the same ids: X[order] bitwise on 4096 sampled rows."""
+    from token_routing_expert_amd import moe_permute
+    cfg, lay = case.cfg, case.layer
+    x_perm = moe_permute(lay.x, lay.topk_ids, cfg.E)[4]
+    torch.cuda.synchronize()
     r = np.random.default_rng(0)
     p = np.arange(cfg.M) if cfg.M <= 4096 else np.sort(r.choice(cfg.M, 4096, replace=False))
     ref = oracle.gather_rows(case.x, case.order[p], cfg.k)
-    got = _host_rows(case.layer.x_perm, p)
+    got = _host_rows(x_perm, p)
+    del x_perm
     assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
+
+
+def test_row_copy_path_is_bit_identical(case):
+    """The layer with the packed copy X[order] (row-copying permute, then the
+    plain grouped product) gives the fused-gather layer's output bit for bit."""
+    from token_routing_expert_amd.layer import MoeLayer, to_host
+    cfg, lay = case.cfg, case.layer
+    other = MoeLayer(cfg, lay.x, lay.w13, lay.w2, logits=lay.logits,
+                     sh_w13=getattr(lay, "sh_w13", None), sh_w2=getattr(lay, "sh_w2", None),
+                     topk_ids=lay.topk_ids if cfg.gating == "given" else None,
+                     topk_w=lay.topk_w if cfg.gating == "given" else None, fused_gather=False)
+    other.forward()
+    torch.cuda.synchronize()
+    y = to_host(other.y)
+    del other
+    torch.cuda.empty_cache()
+    assert np.array_equal(y.view(np.uint8), case.g["y"].view(np.uint8))
 
 
 def _host_rows(t, idx):

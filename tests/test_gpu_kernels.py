@@ -188,6 +188,20 @@ def test_permute(lib, case):
     assert np.array_equal(gxp.view(np.uint8), xp_ref.view(np.uint8))
 
 
+def test_permute_index_only(lib):
+    """x = x_perm = NULL gives the same indices as the full call and copies no rows."""
+    T, k, E = 3001, 5, 7
+    r = np.random.default_rng(11)
+    ids = _ids("hot", T, k, E, r)
+    counts, offsets, order, inv = oracle.permute_index(ids, E)
+    x = torch.zeros((T, 16), dtype=torch.float32, device="cuda")
+    gc, go, gord, ginv, gxp = lib.moe_permute(x, dev(ids), E, rows=False)
+    torch.cuda.synchronize()
+    assert gxp is None
+    for got, ref in ((gc, counts), (go, offsets), (gord, order), (ginv, inv)):
+        assert np.array_equal(host(got), ref)
+
+
 def test_permute_empty(lib):
     x = torch.zeros((0, 16), dtype=torch.float32, device="cuda")
     ids = torch.zeros((0, 2), dtype=torch.int32, device="cuda")
@@ -267,6 +281,60 @@ def test_grouped_halves_match_the_fused_call(lib, case):
     torch.cuda.synchronize()
     assert np.array_equal(host(h1).view(np.uint8), host(h2).view(np.uint8))
     assert np.array_equal(host(y1).view(np.uint8), host(y2).view(np.uint8))
+
+
+GATHER_CASES = [
+    # dtype, T, k, E, d, ffn, ids kind: one case per tile family (mean rows
+    # per expert below 96, up to 288, above), with empty experts and ragged tails
+    ("bf16", 300, 2, 16, 256, 256, "random"),
+    ("bf16", 1000, 2, 8, 512, 256, "random"),
+    ("bf16", 1500, 2, 4, 256, 384, "hot"),
+    ("f32", 333, 3, 16, 128, 256, "hot"),
+    ("f32", 1200, 1, 2, 256, 128, "random"),
+    ("bf16", 257, 4, 3, 512, 512, "one"),
+]
+
+
+@pytest.mark.parametrize("case", GATHER_CASES)
+def test_gate_up_gather_matches_the_packed_rows(lib, case):
+    """The gathered first product equals moe_permute's x_perm through
+    moe_grouped_gate_up bit for bit, and the oracle to the dtype's bar."""
+    dt, T, k, E, d, ffn, kind = case
+    r = np.random.default_rng(T + 31 * E)
+    ids = _ids(kind, T, k, E, r)
+    cfg = inputs.MoeConfig("t", 6, T=T, E=E, k=k, d=d, ffn=ffn, dtype=dt, gating="softmax",
+                           w_std=0.05)
+    x = inputs.gen_x(cfg)
+    w13, w2 = inputs.gen_expert_weights(cfg)
+    xd, w13d = dev(x), dev(w13)
+    _, offsets, order, _, x_perm = lib.moe_permute(xd, dev(ids), E)
+    h_ref = lib.moe_grouped_gate_up(x_perm, offsets, w13d)
+    h = lib.moe_grouped_gate_up_gather(xd, order, k, offsets, w13d)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(h).view(np.uint8), host(h_ref).view(np.uint8))
+    # oracle on a sample of packed rows: row p is token order[p] // k under expert ids[order[p]]
+    p = np.unique(np.concatenate([np.arange(0, T * k, max(1, T * k // 48)), [T * k - 1]]))
+    o = oracle.permute_index(ids, E)[2]
+    tok, ex = o[p] // k, ids.reshape(-1)[o[p]]
+    xr = as_f64(x)[tok]
+    wf = as_f64(w13)
+    gate = np.einsum("pd,pfd->pf", xr, wf[ex, 0])
+    up = np.einsum("pd,pfd->pf", xr, wf[ex, 1])
+    h_or = gate / (1.0 + np.exp(-gate)) * up
+    rows_close(as_f64(host(h)[p]), h_or, 1e-4 if dt == "f32" else 2e-2)
+
+
+def test_gate_up_gather_errors(lib):
+    x = torch.zeros((4, 128), dtype=torch.bfloat16, device="cuda")
+    w13 = torch.zeros((1, 2, 128, 128), dtype=torch.bfloat16, device="cuda")
+    off = torch.tensor([0, 8], dtype=torch.int32, device="cuda")
+    order = torch.zeros(8, dtype=torch.int32, device="cuda")
+    with pytest.raises(lib.MoeError):
+        lib.moe_grouped_gate_up_gather(x, order[:7], 2, off, w13)   # order of the wrong size
+    h = lib.moe_grouped_gate_up_gather(x[:0], order[:0], 2, torch.zeros(2, dtype=torch.int32,
+                                                                         device="cuda"), w13)
+    torch.cuda.synchronize()
+    assert tuple(h.shape) == (0, 128)
 
 
 def test_grouped_swiglu_shared_expert_form(lib):

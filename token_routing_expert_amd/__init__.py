@@ -21,7 +21,8 @@ MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 # Every symbol include/moe355.h declares.
 EXPORTS = ("moe_status_string", "moe_route_topk", "moe_sigmoid_pinned", "moe_send_counts",
            "moe_permute_workspace_bytes", "moe_permute", "moe_grouped_swiglu",
-           "moe_grouped_gate_up", "moe_grouped_down", "moe_unpermute_combine")
+           "moe_grouped_gate_up", "moe_grouped_gate_up_gather", "moe_grouped_down",
+           "moe_unpermute_combine")
 
 
 class MoeError(RuntimeError):
@@ -50,11 +51,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_permute.argtypes = [P, i32, i32, i32, P, i32, i32, P, P, P, P, P, P, sz, P]
     lib.moe_grouped_swiglu.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P, P, P]
     lib.moe_grouped_gate_up.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P]
+    lib.moe_grouped_gate_up_gather.argtypes = [P, i32, i32, i32, i32, i32, P, P, i32, P, P, P]
     lib.moe_grouped_down.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P]
     lib.moe_unpermute_combine.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P]
     for name in ("moe_route_topk", "moe_sigmoid_pinned", "moe_send_counts", "moe_permute",
-                 "moe_grouped_swiglu", "moe_grouped_gate_up", "moe_grouped_down",
-                 "moe_unpermute_combine"):
+                 "moe_grouped_swiglu", "moe_grouped_gate_up", "moe_grouped_gate_up_gather",
+                 "moe_grouped_down", "moe_unpermute_combine"):
         getattr(lib, name).restype = i32
     if path == LIB_PATH:
         _lib = lib
@@ -148,8 +150,12 @@ def moe_permute_workspace_bytes(T, k, E) -> int:
 
 
 def moe_permute(x, topk_ids, E, counts=None, offsets=None, order=None, inv=None, x_perm=None,
-                workspace=None, stream=None):
-    """Returns (counts [E], offsets [E+1], order [Tk], inv [Tk], x_perm [Tk, d])."""
+                workspace=None, stream=None, rows=True):
+    """Returns (counts [E], offsets [E+1], order [Tk], inv [Tk], x_perm [Tk, d]).
+
+    rows=False is the index-only mode: x only gives T and d, no row is copied
+    and x_perm is returned as None.
+    """
     torch = _torch()
     _dev(x, "x", _act_dtypes())
     _dev(topk_ids, "topk_ids", (torch.int32,))
@@ -162,16 +168,20 @@ def moe_permute(x, topk_ids, E, counts=None, offsets=None, order=None, inv=None,
     offsets = torch.empty(E + 1, dtype=i32, device=dev) if offsets is None else offsets
     order = torch.empty(M, dtype=i32, device=dev) if order is None else order
     inv = torch.empty(M, dtype=i32, device=dev) if inv is None else inv
-    x_perm = torch.empty((M, d), dtype=x.dtype, device=dev) if x_perm is None else x_perm
+    if rows:
+        x_perm = torch.empty((M, d), dtype=x.dtype, device=dev) if x_perm is None else x_perm
+    elif x_perm is not None:
+        raise MoeError("moe_permute: x_perm given in index-only mode")
     nbytes = moe_permute_workspace_bytes(T, k, E)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     for name, t in (("counts", counts), ("offsets", offsets), ("order", order), ("inv", inv)):
         _dev(t, name, (i32,))
-    _dev(x_perm, "x_perm", (x.dtype,))
+    if rows:
+        _dev(x_perm, "x_perm", (x.dtype,))
     _check(load_library().moe_permute(
-        _ptr(x), _dtype_code(x), T, d, _ptr(topk_ids), k, E, _ptr(counts), _ptr(offsets),
-        _ptr(order), _ptr(inv), _ptr(x_perm), _ptr(workspace), workspace.numel(),
+        _ptr(x) if rows else None, _dtype_code(x), T, d, _ptr(topk_ids), k, E, _ptr(counts),
+        _ptr(offsets), _ptr(order), _ptr(inv), _ptr(x_perm), _ptr(workspace), workspace.numel(),
         _stream(stream)), "moe_permute")
     return counts, offsets, order, inv, x_perm
 
@@ -224,6 +234,27 @@ def moe_grouped_gate_up(a, offsets, w13, h=None, stream=None):
     _check(load_library().moe_grouped_gate_up(_ptr(a), _dtype_code(a), M, d, ffn, _ptr(offsets),
                                               G, _ptr(w13), _ptr(h), _stream(stream)),
            "moe_grouped_gate_up")
+    return h
+
+
+def moe_grouped_gate_up_gather(x, order, k, offsets, w13, h=None, stream=None):
+    """moe_grouped_gate_up on the rows x[order // k] without materialising them.
+
+    x [T, d] in token order, order [T k] from moe_permute; returns h [T k, ffn].
+    """
+    torch = _torch()
+    G = _expert_shapes("moe_grouped_gate_up_gather", x, offsets, w13=w13)
+    _dev(order, "order", (torch.int32,))
+    T, d = x.shape
+    M = T * k
+    ffn = w13.shape[2]
+    if w13.shape[3] != d or order.numel() != M:
+        raise MoeError("moe_grouped_gate_up_gather: inconsistent shapes")
+    h = torch.empty((M, ffn), dtype=x.dtype, device=x.device) if h is None else h
+    _dev(h, "h", (x.dtype,))
+    _check(load_library().moe_grouped_gate_up_gather(
+        _ptr(x), _dtype_code(x), T, k, d, ffn, _ptr(order), _ptr(offsets), G, _ptr(w13), _ptr(h),
+        _stream(stream)), "moe_grouped_gate_up_gather")
     return h
 
 

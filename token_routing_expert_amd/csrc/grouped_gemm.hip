@@ -155,6 +155,13 @@ __device__ __forceinline__ void wait_vmcnt(int n) { wait_vmcnt_range<0, 63>(n < 
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// Source row of packed row p under a gather: token gather[p] / gk, clamped to
+// [0, a_rows) so a corrupt index can only steer a read inside A.
+__device__ __forceinline__ uint32_t gather_row(const int32_t *gather, int p, int gk, int a_rows) {
+  const uint32_t src = (uint32_t)gather[p] / (uint32_t)gk;
+  return src < (uint32_t)a_rows ? src : (uint32_t)a_rows - 1u;
+}
+
 // Block tile: up to BM rows x BN output columns (of h or y), WM x WN waves.
 // Wave (wm, wn) owns row blocks wm, wm + WM, wm + 2 WM, ... (32 rows each,
 // interleaved so a short tile still spreads over all waves) and BN / WN
@@ -185,7 +192,7 @@ template <bool BF16, int BM, int BN, int WM, int WN, bool SWIGLU, int SA, int SB
 __global__ __launch_bounds__(WM *WN * 64) void k_grouped_gemm(
     const u32x4 *__restrict__ A, int M, int kvec, const int32_t *__restrict__ offsets, int G,
     const u32x4 *__restrict__ B, int64_t b_expert_vec, int64_t b_up_vec, int ntiles, int N,
-    void *__restrict__ C) {
+    void *__restrict__ C, const int32_t *__restrict__ gather, int gk, int a_rows) {
   constexpr int NW = WM * WN;
   constexpr int BR = SWIGLU ? 2 * BN : BN;      // weight rows per tile
   constexpr int NWA = NW / 2, NWB = NW - NWA;   // row-tile loaders, weight-tile loaders
@@ -240,30 +247,47 @@ __global__ __launch_bounds__(WM *WN * 64) void k_grouped_gemm(
     // Uniform base pointer plus a 32-bit per-lane chunk offset (the host
     // checks that every offset fits), so the loads use the scalar-base form.
     const u32x4 *lbase = a_loader ? A : B + (int64_t)tile.expert * b_expert_vec;
+    // Row loaders: the source row of each of their groups, found once per
+    // tile (with gather, packed row p is row gather[p] / gk of A, clamped to
+    // A's a_rows rows).
+    uint32_t arow[A_PW];
+    if (a_loader) {
+#pragma unroll
+      for (int r = 0; r < A_PW; ++r) {
+        int row = m0 + (lw + r * lstride) * 8 + ld_row;
+        row = row < hi ? row : hi - 1;
+        arow[r] = gather ? gather_row(gather, row, gk, a_rows) : (uint32_t)row;
+      }
+    }
     auto issue = [&](int kt) {
       u32x4 *stage = a_loader ? a_ring + (kt % SA) * ASTAGE : b_ring + (kt % SB) * BSTAGE;
+      if (a_loader) {
+#pragma unroll
+        for (int r = 0; r < A_PW; ++r) {
+          if (r < nld) {
+            const int g = lw + r * lstride;
+            const uint32_t key = ld_row ^ (g & 1);   // swz_key(8 g + ld_row)
+            const uint32_t off = arow[r] * (uint32_t)kvec + (uint32_t)kt * 8u + ((uint32_t)ld_slot ^ key);
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(lbase + off),
+                (__attribute__((address_space(3))) void *)(stage + g * 64), 16, 0, 0);
+          }
+        }
+        return;
+      }
       // A rolled loop: unrolled, the per-instruction offsets would be hoisted
       // out of the K loop and held in registers the MFMA blocks need.
 #pragma unroll 1
       for (int r = 0; r < nld; ++r) {
-        {
-          const int g = lw + r * lstride;
-          const uint32_t key = ld_row ^ (g & 1);   // swz_key(8 g + ld_row)
-          uint32_t off;
-          if (a_loader) {
-            int row = m0 + g * 8 + ld_row;
-            row = row < hi ? row : hi - 1;
-            off = (uint32_t)row * (uint32_t)kvec;
-          } else {
-            const int brow = g * 8 + ld_row;
-            off = SWIGLU && brow >= BN ? (uint32_t)b_up_vec + (uint32_t)(n0 + brow - BN) * kvec
-                                       : (uint32_t)(n0 + brow) * (uint32_t)kvec;
-          }
-          off += (uint32_t)kt * 8u + ((uint32_t)ld_slot ^ key);
-          __builtin_amdgcn_global_load_lds(
-              (const void *)(lbase + off),
-              (__attribute__((address_space(3))) void *)(stage + g * 64), 16, 0, 0);
-        }
+        const int g = lw + r * lstride;
+        const uint32_t key = ld_row ^ (g & 1);   // swz_key(8 g + ld_row)
+        const int brow = g * 8 + ld_row;
+        uint32_t off = SWIGLU && brow >= BN ? (uint32_t)b_up_vec + (uint32_t)(n0 + brow - BN) * kvec
+                                            : (uint32_t)(n0 + brow) * (uint32_t)kvec;
+        off += (uint32_t)kt * 8u + ((uint32_t)ld_slot ^ key);
+        __builtin_amdgcn_global_load_lds(
+            (const void *)(lbase + off),
+            (__attribute__((address_space(3))) void *)(stage + g * 64), 16, 0, 0);
       }
     };
 
@@ -424,7 +448,7 @@ template <bool BF16, int BM, int BR, int SA, int SB, int CPR, bool SWIGLU, bool 
 __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     const u32x4 *__restrict__ A, int M, int kvec, const int32_t *__restrict__ offsets, int G,
     const u32x4 *__restrict__ B, int64_t b_expert_vec, int64_t b_up_vec, int ntiles, int N,
-    void *__restrict__ C) {
+    void *__restrict__ C, const int32_t *__restrict__ gather, int gk, int a_rows) {
   constexpr int BN = SWIGLU ? BR / 2 : BR;       // output columns per tile
   constexpr int WNG = BR / 64, WMG = 4 / WNG;    // waves of a group across N and M
   constexpr int FM = (BM / 64 + WMG - 1) / WMG;  // row blocks per wave
@@ -484,8 +508,10 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     // tile, and the K position as the scalar offset -- a K step costs no
     // address arithmetic.
     constexpr int NLA = (A_TOT + 3) / 4;           // row loads per group-0 wave per slice, at most
-    const u32x4 *a_base = A + (int64_t)m0 * kvec;
-    const uint32_t a_bytes = (uint32_t)((int64_t)rows * kvec * 16);
+    // Without gather the resource starts at the tile's first row; with
+    // gather (packed row p is row gather[p] / gk of A) it spans A's a_rows rows.
+    const u32x4 *a_base = gather ? A : A + (int64_t)m0 * kvec;
+    const uint32_t a_bytes = (uint32_t)((int64_t)(gather ? a_rows : rows) * kvec * 16);
     const u32x4 *b_base = B + (int64_t)tile.expert * b_expert_vec;
     const uint32_t b_bytes = (uint32_t)(b_expert_vec * 16);
     auto a_offsets = [&](uint32_t (&off)[NLA]) {
@@ -494,7 +520,8 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
         const int g = wq + 4 * r;
         int row = g * RPI + ld_row;
         row = row < rows ? row : rows - 1;
-        off[r] = ((uint32_t)row * (uint32_t)kvec + ((uint32_t)ld_slot ^ key_of(g))) * 16u;
+        const uint32_t src = gather ? gather_row(gather, m0 + row, gk, a_rows) : (uint32_t)row;
+        off[r] = (src * (uint32_t)kvec + ((uint32_t)ld_slot ^ key_of(g))) * 16u;
       }
     };
     auto b_offsets = [&](uint32_t (&off)[NLB]) {
@@ -753,9 +780,12 @@ struct PpCfg {
   static constexpr bool SPLIT = SPLIT_;
 };
 
+// gather (optional): packed row p of the product is row gather[p] / gk of a,
+// which then has a_rows rows.
 template <bool BF16, bool SWIGLU, typename Cfg>
 void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int G, const void *w,
-                void *out, hipStream_t stream) {
+                void *out, hipStream_t stream, const int32_t *gather = nullptr, int gk = 1,
+                int a_rows = 0) {
   const int elem = BF16 ? 2 : 4;
   const int kvec = K * elem / 16;
   // w13 is [G, 2, N, K] (gate rows, then up rows); w2 is [G, N, K].
@@ -770,7 +800,7 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
     const int grid = persistent_grid((const void *)kern, 512, per_cu, mtiles_max * ntiles);
     kern<<<dim3(grid), dim3(512), 0, stream>>>(static_cast<const u32x4 *>(a), M, kvec, offsets, G,
                                               static_cast<const u32x4 *>(w), b_expert, b_up,
-                                              ntiles, N, out);
+                                              ntiles, N, out, gather, gk, a_rows);
   } else {
     const int ntiles = N / Cfg::BN;
     const int64_t mtiles_max = (M + Cfg::BM - 1) / Cfg::BM + G;
@@ -780,7 +810,7 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
     const int grid = persistent_grid((const void *)kern, threads, per_cu, mtiles_max * ntiles);
     kern<<<dim3(grid), dim3(threads), 0, stream>>>(static_cast<const u32x4 *>(a), M, kvec, offsets,
                                                   G, static_cast<const u32x4 *>(w), b_expert,
-                                                  b_up, ntiles, N, out);
+                                                  b_up, ntiles, N, out, gather, gk, a_rows);
   }
 }
 
@@ -832,13 +862,14 @@ inline Family family_of(int M, int G, int d) {
 // GEMM1: gate/up + SwiGLU, K = d, N = ffn.
 template <bool BF16>
 void launch_gate_up(Family f, const void *a, int M, int d, int ffn, const int32_t *offsets, int G,
-                    const void *w13, void *h, hipStream_t stream) {
+                    const void *w13, void *h, hipStream_t stream, const int32_t *gather = nullptr,
+                    int gk = 1, int a_rows = 0) {
   if (f == Family::Small)
-    launch_one<BF16, true, G1Small>(a, M, d, ffn, offsets, G, w13, h, stream);
+    launch_one<BF16, true, G1Small>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows);
   else if (f == Family::Medium)
-    launch_one<BF16, true, G1Medium>(a, M, d, ffn, offsets, G, w13, h, stream);
+    launch_one<BF16, true, G1Medium>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows);
   else
-    launch_one<BF16, true, G1Large>(a, M, d, ffn, offsets, G, w13, h, stream);
+    launch_one<BF16, true, G1Large>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows);
 }
 
 // GEMM2: down, K = ffn, N = d.
@@ -886,6 +917,28 @@ extern "C" moe_status moe_grouped_gate_up(const void *a, moe_dtype dt, int M, in
     launch_gate_up<true>(f, a, M, d, ffn, offsets, G, w13, h, stream);
   else
     launch_gate_up<false>(f, a, M, d, ffn, offsets, G, w13, h, stream);
+  return launch_status();
+}
+
+extern "C" moe_status moe_grouped_gate_up_gather(const void *x, moe_dtype dt, int T, int k, int d,
+                                                 int ffn, const int32_t *order,
+                                                 const int32_t *offsets, int G, const void *w13,
+                                                 void *h, hipStream_t stream) {
+  if (T < 0 || k < 1) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)T * k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  const int M = T * k;
+  const moe_status st = check_shape(dt, M, d, ffn, G);
+  if (st != MOE_OK || M == 0) return st;
+  // Byte offsets inside x are 32-bit in the kernels.
+  const int64_t elem = dt == MOE_F32 ? 4 : 2;
+  if ((int64_t)T * d * elem >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  if (!x || !order || !offsets || !w13 || !h) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w13) || !aligned16(h)) return MOE_ERR_INVALID_ARG;
+  const Family f = family_of(M, G, d);
+  if (dt == MOE_BF16)
+    launch_gate_up<true>(f, x, M, d, ffn, offsets, G, w13, h, stream, order, k, T);
+  else
+    launch_gate_up<false>(f, x, M, d, ffn, offsets, G, w13, h, stream, order, k, T);
   return launch_status();
 }
 

@@ -241,9 +241,11 @@ extern "C" moe_status moe_permute(const void *x, moe_dtype dt, int T, int d,
   if (E > 1024 || d % 8 != 0 || (int64_t)T * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
   const int64_t M = (int64_t)T * k;
-  if (M > 0 && (!x || !topk_ids || !order || !inv || !x_perm || !workspace))
-    return MOE_ERR_INVALID_ARG;
-  if (M > 0 && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
+  // x and x_perm both NULL: index-only mode (counts, offsets, order, inv).
+  const bool rows = x || x_perm;
+  if (M > 0 && (!topk_ids || !order || !inv || !workspace)) return MOE_ERR_INVALID_ARG;
+  if (M > 0 && rows && (!x || !x_perm)) return MOE_ERR_INVALID_ARG;
+  if (M > 0 && rows && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < moe_permute_workspace_bytes(T, k, E)) return MOE_ERR_INVALID_ARG;
 
   const int64_t chunk = chunk_size(M > 0 ? M : 1);
@@ -259,6 +261,7 @@ extern "C" moe_status moe_permute(const void *x, moe_dtype dt, int T, int d,
   if (M == 0) return launch_status();
   k_multisplit<<<dim3(nchunks), dim3(kThreads), sizeof(int) * 4 * E, stream>>>(
       topk_ids, M, E, nbits, chunk, hist, order, inv);
+  if (!rows) return launch_status();
   const int elem = dt == MOE_F32 ? 4 : 2;
   const int nvec = (int)((int64_t)d * elem / 16);
   const dim3 grid((T + 3) / 4);

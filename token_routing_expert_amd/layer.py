@@ -10,9 +10,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (moe_grouped_down, moe_grouped_gate_up, moe_grouped_swiglu, moe_permute,
-               moe_permute_workspace_bytes, moe_route_topk, moe_send_counts,
-               moe_unpermute_combine)
+from . import (moe_grouped_down, moe_grouped_gate_up, moe_grouped_gate_up_gather,
+               moe_grouped_swiglu, moe_permute, moe_permute_workspace_bytes, moe_route_topk,
+               moe_send_counts, moe_unpermute_combine)
 from .inputs import MoeConfig
 
 
@@ -35,12 +35,18 @@ def to_host(t) -> np.ndarray:
 
 
 class MoeLayer:
-    """Device-resident inputs, weights and every intermediate buffer of one layer."""
+    """Device-resident inputs, weights and every intermediate buffer of one layer.
+
+    fused_gather=True skips the packed copy X[order]: the permute computes
+    indices only and the first expert product reads the token rows through
+    order itself (moe_grouped_gate_up_gather).  Both paths give the same bits.
+    """
 
     def __init__(self, cfg: MoeConfig, x, w13, w2, logits=None, sh_w13=None, sh_w2=None,
-                 topk_ids=None, topk_w=None, device="cuda"):
+                 topk_ids=None, topk_w=None, device="cuda", fused_gather=False):
         import torch
         self.cfg = cfg
+        self.fused_gather = fused_gather
         dev = torch.device(device)
         self.device = dev
         self.x = x if isinstance(x, torch.Tensor) else to_device(x, dev)
@@ -63,7 +69,7 @@ class MoeLayer:
         self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
         self.order = torch.empty(M, dtype=i32, device=dev)
         self.inv = torch.empty(M, dtype=i32, device=dev)
-        self.x_perm = torch.empty((M, d), dtype=act, device=dev)
+        self.x_perm = None if fused_gather else torch.empty((M, d), dtype=act, device=dev)
         self.workspace = torch.empty(max(16, moe_permute_workspace_bytes(T, k, E)), dtype=torch.uint8,
                                      device=dev)
         self.h = torch.empty((M, ffn), dtype=act, device=dev)
@@ -88,15 +94,24 @@ class MoeLayer:
 
     def permute(self, stream=None):
         moe_permute(self.x, self.topk_ids, self.cfg.E, self.counts, self.offsets, self.order,
-                    self.inv, self.x_perm, self.workspace, stream=stream)
+                    self.inv, self.x_perm, self.workspace, stream=stream,
+                    rows=not self.fused_gather)
 
     def experts_routed(self, stream=None):
-        moe_grouped_swiglu(self.x_perm, self.offsets, self.w13, self.w2, self.h, self.y_perm,
-                           stream=stream)
+        if self.fused_gather:
+            self.gate_up(stream)
+            self.down(stream)
+        else:
+            moe_grouped_swiglu(self.x_perm, self.offsets, self.w13, self.w2, self.h, self.y_perm,
+                               stream=stream)
 
     def gate_up(self, stream=None):
         """The routed experts' first product alone (the same launch experts_routed makes)."""
-        moe_grouped_gate_up(self.x_perm, self.offsets, self.w13, self.h, stream=stream)
+        if self.fused_gather:
+            moe_grouped_gate_up_gather(self.x, self.order, self.cfg.k, self.offsets, self.w13,
+                                       self.h, stream=stream)
+        else:
+            moe_grouped_gate_up(self.x_perm, self.offsets, self.w13, self.h, stream=stream)
 
     def down(self, stream=None):
         """The routed experts' second product alone."""
