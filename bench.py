@@ -222,9 +222,21 @@ def main():
                         hbm_frac=round(nbytes / (ms * 1e-3) / PEAK_HBM, 4))
         stage_info[name] = info
 
-    # Dominant kernel: the routed gate/up launch (about 2/3 of the FLOPs).
+    # Dominant kernel: the routed gate/up launch (about 2/3 of the FLOPs).  Its
+    # bound is the roofline's: HBM when its arithmetic intensity (algorithmic
+    # FLOPs per algorithmic byte) lies below the ridge peak FLOP/s / peak B/s.
     gu_ms = stage_ms["gate_up"]
-    achieved = f_gate_up / (gu_ms * 1e-3)
+    flop_rate = f_gate_up / (gu_ms * 1e-3)
+    byte_rate = b_gate_up / (gu_ms * 1e-3)
+    intensity = f_gate_up / b_gate_up
+    ridge = peak / PEAK_HBM
+    hbm_bound = intensity < ridge
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(byte_rate / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": round(byte_rate / PEAK_HBM, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flop_rate / 1e12, 2), "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": round(flop_rate / peak, 4)}
     result = {
         "metric": METRIC,
         "value": cfg.T / (ms_step * 1e-3),
@@ -246,14 +258,15 @@ def main():
         "roofline": {
             "kernel": ("moe_grouped_gate_up_gather" if gather else "moe_grouped_gate_up")
                       + ": routed gate/up products + SwiGLU (one launch)",
-            "bound": "mfma",
-            "achieved": round(achieved / 1e12, 2),
-            "peak": peak / 1e12,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
+            **roof,
             "traffic": measured_traffic(cfg.name),
             "algorithmic_bytes": b_gate_up,
-            "hbm_frac": round(b_gate_up / (gu_ms * 1e-3) / PEAK_HBM, 4),
+            "algorithmic_flops": f_gate_up,
+            "intensity_flop_per_byte": round(intensity, 1),
+            "ridge_flop_per_byte": round(ridge, 1),
+            "mfma_frac": round(flop_rate / peak, 4),
+            "hbm_frac": round(byte_rate / PEAK_HBM, 4),
+            "launch_ms": round(gu_ms, 4),
         },
         "stages": stage_info,
         "device": torch.cuda.get_device_name(0),
