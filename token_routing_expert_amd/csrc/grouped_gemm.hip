@@ -406,14 +406,17 @@ __global__ __launch_bounds__(WM *WN * 64) void k_grouped_gemm(
 // (64 bytes of K) are a memory phase (LDS -> registers and issuing loads) and
 // a compute phase (MFMAs from registers), each closed by a barrier.  Group 1
 // starts one barrier late, so while one group issues MFMAs the other works
-// on memory, and the matrix cores of each SIMD stay busy.
+// on memory, and the matrix cores of each SIMD stay busy.  A memory phase
+// need not wait for its LDS reads: they finish under the wave's next compute
+// phase while the other group's reads already queue, which keeps the LDS
+// busy across the barrier.
 //
 // K is staged in slices of 16 CPR bytes per row (CPR = 8: 128 bytes, two
 // phase pairs per slice; CPR = 4: 64 bytes, one).  Narrow slices make the
 // ring stages small, so more of them fit: the weight tile, streamed from HBM,
 // can then be requested several phases before it is read.  Direct
 // global-to-LDS loads (one wave instruction = 1 KB = 64 / CPR rows); group 0
-// loads the row tile into a ring of SA stages, SA - 1 slices ahead, group 1
+// loads the row tile into a ring of SA stages, DA slices ahead, group 1
 // the weight tile into a ring of SB stages, SB - 1 slices ahead, so each
 // wave's vmcnt queue holds one operand.  A slice is visible to every wave
 // after the first barrier that follows all its loaders' waits: group 0 waits
@@ -424,6 +427,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_grouped_gemm(
 // Fourth word of a raw buffer resource on gfx9-class GPUs: 32-bit data
 // format, no swizzle, no stride; accesses at or past the byte count return 0.
 constexpr int kBufferFlags = 0x00020000;
+
 
 // One wave's 16-byte-per-lane buffer load straight into LDS: lane l's data
 // lands at lds + 16 l.  base/bytes describe the buffer; voff is the lane's
@@ -436,6 +440,15 @@ __device__ __forceinline__ void buffer_load_lds16(const void *base, uint32_t byt
                                            voff, soff, 0, 0);
 }
 
+// A workgroup barrier that is also a scheduling fence: without the fences the
+// compiler may move MFMAs (register-only instructions) across s_barrier, which
+// would pull one group's compute phase into the other group's window.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int CPR>
 __device__ __forceinline__ int swz_c(int r, int cc) {
   if constexpr (CPR == 8)
@@ -444,7 +457,7 @@ __device__ __forceinline__ int swz_c(int r, int cc) {
     return r * 4 + (cc ^ ((r >> 2) & 3));   // 16 consecutive rows at one chunk: all banks once
 }
 
-template <bool BF16, int BM, int BR, int SA, int SB, int CPR, bool SWIGLU, bool SPLIT>
+template <bool BF16, int BM, int BR, int SA, int SB, int CPR, int DA, bool SWIGLU, bool SPLIT>
 __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     const u32x4 *__restrict__ A, int M, int kvec, const int32_t *__restrict__ offsets, int G,
     const u32x4 *__restrict__ B, int64_t b_expert_vec, int64_t b_up_vec, int ntiles, int N,
@@ -460,9 +473,18 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
   constexpr int NLB = B_TOT / 4;                 // weight loads per group-1 wave per slice
   static_assert(CPR == 4 || CPR == 8, "slice width");
   static_assert(BM % 64 == 0 && BM % RPI == 0 && (BR == 128 || BR == 256) && B_TOT % 4 == 0, "tile");
-  static_assert(SA >= 2 && SB >= 2, "rings");
+  static_assert(SA >= 2 && SB >= 2 && DA >= 1 && DA <= SA - 1, "rings");
   static_assert((SA * ASTAGE + SB * BSTAGE) * 16 <= 160 * 1024, "LDS");
-  static_assert(NLB * (SB - 2) < 64 && ((A_TOT + 3) / 4) * (SA - 2) < 64, "vmcnt");
+  static_assert(NLB * (SB - 2) < 64 && ((A_TOT + 3) / 4) * (DA - 1) < 64, "vmcnt");
+  // A memory phase ends with its LDS reads still in flight (they complete
+  // under the next compute phase) unless a stage they read may be refilled
+  // in the very next phase: group 0 refills the row stage of slice
+  // kt + DA - SA at its first memory phase of slice kt, one phase after
+  // group 1's last read of slice kt - 1.  With DA = SA - 1 that is the same
+  // stage, so group 1 drains its reads at its last memory phase of a slice.
+  // Every other refill targets a stage whose last reads were consumed by
+  // MFMAs at least one phase earlier.
+  constexpr bool kDrainLast = DA == SA - 1;
   static_assert(FM <= 5, "row blocks per wave");
 
   __shared__ u32x4 smem[SA * ASTAGE + SB * BSTAGE];
@@ -547,7 +569,8 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
         buffer_load_lds16(b_base, b_bytes, stage + (wq + 4 * r) * 64, off[r], kt * CPR * 16);
     };
     // Waits for slice k of this wave's operand: the slices after it that are
-    // already issued (up to k + S - 2) may stay in flight.
+    // already issued (up to k + SB - 2, or k + DA - 1 for the row tile) may
+    // stay in flight.
     auto wait_b = [&](int k) {
       constexpr int kSteady = (SB - 2) * NLB;
       if (k + SB - 2 <= KT - 1)
@@ -556,7 +579,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
         wait_vmcnt((KT - 1 - k) * NLB);
     };
     auto wait_a = [&](int k) {
-      const int last = k + SA - 2 < KT - 1 ? k + SA - 2 : KT - 1;
+      const int last = k + DA - 1 < KT - 1 ? k + DA - 1 : KT - 1;
       wait_vmcnt((last - k) * na);
     };
 
@@ -577,8 +600,8 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    // Slices 0 .. S - 2 of this wave's operand, wait for slice 0, then group
-    // 1 starts one barrier late.
+    // Slices 0 .. DA - 1 (row tile) or 0 .. SB - 2 (weight tile) of this
+    // wave's operand, wait for slice 0, then group 1 starts one barrier late.
     uint32_t off[GRP == 0 ? NLA : NLB];
     if constexpr (GRP == 0)
       a_offsets(off);
@@ -587,7 +610,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     asm volatile("" ::: "memory");
     if constexpr (GRP == 0) {
 #pragma unroll
-      for (int s = 0; s < SA - 1; ++s)
+      for (int s = 0; s < DA; ++s)
         if (s < KT) issue_a(s, off);
       asm volatile("" ::: "memory");
       wait_a(0);
@@ -599,9 +622,9 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
       wait_b(0);
     }
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
+    phase_barrier();
     asm volatile("" ::: "memory");
-    if (GRP == 1) __builtin_amdgcn_s_barrier();
+    if (GRP == 1) phase_barrier();
     asm volatile("" ::: "memory");
 
     // B fragment rows of this wave inside the weight tile.
@@ -634,17 +657,18 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
         }
         if (h == 0) {
           if constexpr (GRP == 0) {
-            if (kt + SA - 1 < KT) issue_a(kt + SA - 1, off);
+            if (kt + DA < KT) issue_a(kt + DA, off);
           } else {
             if (kt + SB - 1 < KT) issue_b(kt + SB - 1, off);
           }
         }
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): reads done before the barrier
+        if (GRP == 1 && kDrainLast && h == NH - 1)
+          __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0): reads done before the barrier
         // Group 0 reads slice kt + 1 right after the next barrier but one.
         if (GRP == 1 && h == NH - 1 && kt + 1 < KT) wait_b(kt + 1);
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
+        phase_barrier();
         asm volatile("" ::: "memory");
         // Compute phase.
 #pragma unroll
@@ -657,11 +681,11 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
         asm volatile("" ::: "memory");
         if (GRP == 0 && h == NH - 1 && kt + 1 < KT) wait_a(kt + 1);
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
+        phase_barrier();
         asm volatile("" ::: "memory");
       }
     }
-    if (GRP == 0) __builtin_amdgcn_s_barrier();   // both groups leave the tile aligned
+    if (GRP == 0) phase_barrier();   // both groups leave the tile aligned
     asm volatile("" ::: "memory");
 
     // Epilogue.  MFMA 32x32 output layout: lane l holds column l % 32 and, in
@@ -773,10 +797,10 @@ struct TileCfg {
 // Ping-pong kernel: BM-row x BR-weight-row tiles, K slices of 16 CPR bytes,
 // SA row-tile and SB weight-tile ring stages; SPLIT: one kernel body per live
 // row-block count.
-template <int BM_, int BR_, int SA_, int SB_, int CPR_, bool SPLIT_>
+template <int BM_, int BR_, int SA_, int SB_, int CPR_, bool SPLIT_, int DA_>
 struct PpCfg {
   static constexpr bool PP = true;
-  static constexpr int BM = BM_, BR = BR_, SA = SA_, SB = SB_, CPR = CPR_;
+  static constexpr int BM = BM_, BR = BR_, SA = SA_, SB = SB_, CPR = CPR_, DA = DA_;
   static constexpr bool SPLIT = SPLIT_;
 };
 
@@ -795,7 +819,8 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
     constexpr int BN = SWIGLU ? Cfg::BR / 2 : Cfg::BR;
     const int ntiles = N / BN;
     const int64_t mtiles_max = (M + Cfg::BM - 1) / Cfg::BM + G;
-    auto kern = k_grouped_gemm_pp<BF16, Cfg::BM, Cfg::BR, Cfg::SA, Cfg::SB, Cfg::CPR, SWIGLU, Cfg::SPLIT>;
+    auto kern = k_grouped_gemm_pp<BF16, Cfg::BM, Cfg::BR, Cfg::SA, Cfg::SB, Cfg::CPR, Cfg::DA, SWIGLU,
+                                  Cfg::SPLIT>;
     static int per_cu = 0;
     const int grid = persistent_grid((const void *)kern, 512, per_cu, mtiles_max * ntiles);
     kern<<<dim3(grid), dim3(512), 0, stream>>>(static_cast<const u32x4 *>(a), M, kvec, offsets, G,
@@ -831,16 +856,16 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
 #define MOE_G2_SMALL 32, 128, 1, 4, 2, 4
 #endif
 #ifndef MOE_PP1_MEDIUM
-#define MOE_PP1_MEDIUM 320, 256, 3, 6, 4, true
+#define MOE_PP1_MEDIUM 320, 256, 4, 5, 4, true, 2
 #endif
 #ifndef MOE_PP2_MEDIUM
-#define MOE_PP2_MEDIUM 320, 256, 3, 6, 4, true
+#define MOE_PP2_MEDIUM 320, 256, 4, 5, 4, true, 2
 #endif
 #ifndef MOE_PP1_LARGE
-#define MOE_PP1_LARGE 256, 256, 2, 3, 8, false
+#define MOE_PP1_LARGE 256, 256, 2, 3, 8, true, 1
 #endif
 #ifndef MOE_PP2_LARGE
-#define MOE_PP2_LARGE 256, 256, 2, 3, 8, false
+#define MOE_PP2_LARGE 256, 256, 2, 3, 8, true, 1
 #endif
 using G1Small = TileCfg<MOE_G1_SMALL>;
 using G2Small = TileCfg<MOE_G2_SMALL>;
