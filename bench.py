@@ -56,6 +56,28 @@ def gate_up_bytes(cfg, counts, gather=False):
             + (4 * M if gather else 0))
 
 
+def load_accounting(cfg, counts, send_counts):
+    """Load and padding statistics of the batch: rows per expert, the rows the
+    GEMM tiles compute beyond the real ones (tile padding), and the imbalance
+    of the simulated EP ranks (most-loaded receiving rank over the mean, from
+    the send-count matrix's column sums)."""
+    import numpy as np
+    counts = np.asarray(counts, np.int64)
+    M = int(counts.sum())
+    per_expert = -(-M // cfg.E) if cfg.E else 0
+    bm = 32 if per_expert < 96 or cfg.d % 256 else (320 if per_expert <= 288 else 256)
+    tiled = int((-(-counts // bm) * bm).sum())
+    blocks = int((-(-counts // 32) * 32).sum())   # MFMAs run on 32-row blocks with a live row
+    out = {"rows": M, "rows_per_expert_min": int(counts.min()), "rows_per_expert_max": int(counts.max()),
+           "empty_experts": int((counts == 0).sum()), "tile_rows": bm,
+           "tile_padding_frac": round((tiled - M) / max(M, 1), 4),
+           "mfma_padding_frac": round((blocks - M) / max(M, 1), 4), "dropped_rows": 0}
+    if send_counts is not None:
+        recv = np.asarray(send_counts, np.int64).sum(axis=0)
+        out["ep_recv_imbalance"] = round(float(recv.max() / max(recv.mean(), 1e-9)), 4)
+    return out
+
+
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "dsv3_prefill_gate_up_traffic.json")
 GEMM_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "token_routing_expert_amd",
@@ -200,6 +222,10 @@ def main():
     ms_step = wall * 1e3 / K
     stage_ms = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K
                 for j, name in enumerate(stages)}
+    step_ev = sorted(evs[i][0].elapsed_time(evs[i][-1]) for i in range(K))
+
+    def pct(q):
+        return round(step_ev[min(K - 1, int(q * (K - 1) + 0.5))], 4)
 
     from token_routing_expert_amd.layer import to_host
     counts = to_host(layer.counts)
@@ -269,6 +295,9 @@ def main():
             "launch_ms": round(gu_ms, 4),
         },
         "stages": stage_info,
+        "step_ms_events": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
+        "load": load_accounting(cfg, counts,
+                                to_host(layer.send_counts) if cfg.n_ep else None),
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
