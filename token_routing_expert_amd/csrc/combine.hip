@@ -194,8 +194,8 @@ extern "C" moe_status moe_unpermute_combine(const void *y_perm, moe_dtype dt, in
       k_combine<true, 2, NV><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
     else if (k <= 4)
       k_combine<true, 4, NV><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
-    else if (k <= 8)
-      k_combine<true, 8, NV><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+    else if (k <= 8)   // k + 1 rows per vector already keep enough loads in flight
+      k_combine<true, 8, 1><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
     else
       k_combine_anyk<true><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
   } else {
@@ -206,7 +206,7 @@ extern "C" moe_status moe_unpermute_combine(const void *y_perm, moe_dtype dt, in
     else if (k <= 4)
       k_combine<false, 4, NV><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
     else if (k <= 8)
-      k_combine<false, 8, NV><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
+      k_combine<false, 8, 1><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
     else
       k_combine_anyk<false><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
   }
