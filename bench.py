@@ -56,6 +56,34 @@ def gate_up_bytes(cfg, counts, gather=False):
             + (4 * M if gather else 0))
 
 
+def packed_permute_rate(layer, cfg, nbytes, reps=10):
+    """Mean duration of moe_permute with the row copy, HIP events around each
+    call on the launch stream, and its algorithmic HBM rate."""
+    import torch
+
+    from token_routing_expert_amd import moe_permute
+    x_perm = torch.empty((cfg.T * cfg.k, cfg.d), dtype=layer.x.dtype, device=layer.x.device)
+    bufs = [torch.empty_like(layer.counts), torch.empty_like(layer.offsets),
+            torch.empty_like(layer.order), torch.empty_like(layer.inv)]
+    stream = torch.cuda.current_stream()
+
+    def run():
+        moe_permute(layer.x, layer.topk_ids, cfg.E, *bufs, x_perm, layer.workspace)
+
+    for _ in range(3):
+        run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+    for i in range(reps):
+        ev[2 * i].record(stream)
+        run()
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)) / reps
+    del x_perm
+    return {"ms": round(ms, 4), "bytes": nbytes, "GBps": round(nbytes / ms / 1e6, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / PEAK_HBM, 4)}
+
+
 def load_accounting(cfg, counts, send_counts):
     """Load and padding statistics of the batch: rows per expert, the rows the
     GEMM tiles compute beyond the real ones (tile padding), and the imbalance
@@ -300,6 +328,11 @@ def main():
                                 to_host(layer.send_counts) if cfg.n_ep else None),
         "device": torch.cuda.get_device_name(0),
     }
+    if gather:
+        # The timed path never copies rows; the row-copying permute (the
+        # stable scatter into the packed buffer X[order]) is measured here
+        # on the same batch, outside the timed step, for its HBM figure.
+        result["permute_packed"] = packed_permute_rate(layer, cfg, stage_bytes(cfg)[0])
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(cfg, (x, w13, w2, logits, sh, ids_in, w_in))
