@@ -49,7 +49,7 @@ def _load():
     lib.orc_sigmoid_pinned.argtypes = [ctypes.c_float]
     lib.orc_sigmoid_pinned.restype = ctypes.c_float
     lib.orc_sigmoid_pinned_array.argtypes = [P, P, i64]
-    lib.orc_route.argtypes = [P, i32, i32, i32, i32, i32, i32, i32, P, P]
+    lib.orc_route.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, P, P]
     lib.orc_route.restype = i32
     lib.orc_send_counts.argtypes = [P, i32, i32, i32, i32, P]
     lib.orc_send_counts.restype = i32
@@ -60,6 +60,9 @@ def _load():
     lib.orc_combine.argtypes = [P, i32, i64, i32, i32, P, P, P, i32, P]
     lib.orc_alltoall_bytes.argtypes = [i64, i32, i64, i32, f64, f64, i32]
     lib.orc_alltoall_bytes.restype = f64
+    lib.orc_router_logits.argtypes = [P, i32, i64, i32, P, i32, P]
+    lib.orc_bias_update.argtypes = [P, i32, ctypes.c_float, P]
+    lib.orc_bias_update.restype = i32
     lib.orc_num_threads.restype = i32
     _lib = lib
     return lib
@@ -97,18 +100,50 @@ def sigmoid_pinned(x: np.ndarray) -> np.ndarray:
 
 
 def route(logits: np.ndarray, k: int, gating: str = "softmax", renormalize: int = 1,
-          n_groups: int = 1, topk_groups: int = 1):
-    """O1: top-k ids [T,k] int32 and gates [T,k] fp32 (oracle.c, orc_route)."""
+          n_groups: int = 1, topk_groups: int = 1, bias=None):
+    """O1: top-k ids [T,k] int32 and gates [T,k] fp32 (oracle.c, orc_route).
+
+    bias [E] fp32 (optional): selection on logits + bias, gates from the
+    unbiased logits (auxiliary-loss-free balancing)."""
     logits = _c(logits, np.float32)
     T, E = logits.shape
     ids = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float32)
     g = SOFTMAX if gating == "softmax" else SIGMOID
-    rc = _load().orc_route(_ptr(logits), T, E, k, g, int(renormalize), n_groups, topk_groups,
-                           _ptr(ids), _ptr(w))
+    b = None if bias is None else _c(bias, np.float32)
+    if b is not None and b.shape != (E,):
+        raise ValueError("bias must have one entry per expert")
+    rc = _load().orc_route(_ptr(logits), None if b is None else _ptr(b), T, E, k, g,
+                           int(renormalize), n_groups, topk_groups, _ptr(ids), _ptr(w))
     if rc != 0:
         raise ValueError("orc_route: arguments outside the contract")
     return ids, w
+
+
+def router_logits(x: np.ndarray, wg: np.ndarray) -> np.ndarray:
+    """O0: logits [T,E] fp32 = x [T,d] . wg [E,d]^T, fp64 sums (oracle.c, orc_router_logits).
+    bf16 operands are uint16 bit patterns."""
+    x = _c(x)
+    wg = _c(wg)
+    if x.dtype != wg.dtype or x.ndim != 2 or wg.ndim != 2 or x.shape[1] != wg.shape[1]:
+        raise ValueError("router_logits: x [T,d] and wg [E,d] of one dtype")
+    T, d = x.shape
+    E = wg.shape[0]
+    out = np.empty((T, E), np.float32)
+    _load().orc_router_logits(_ptr(x), _dtype_code(x), T, d, _ptr(wg), E, _ptr(out))
+    return out
+
+
+def bias_update(bias: np.ndarray, counts: np.ndarray, lr: float) -> np.ndarray:
+    """Auxiliary-loss-free bias step: returns bias + lr (avg - counts) in fp32
+    (oracle.c, orc_bias_update)."""
+    b = np.array(bias, np.float32, copy=True)
+    c = _c(counts, np.int32)
+    if b.shape != c.shape or b.ndim != 1:
+        raise ValueError("bias_update: bias and counts of shape [E]")
+    if _load().orc_bias_update(_ptr(c), c.size, float(np.float32(lr)), _ptr(b)) != 0:
+        raise ValueError("orc_bias_update: arguments outside the contract")
+    return b
 
 
 def send_counts(ids: np.ndarray, E: int, n_ep: int) -> np.ndarray:

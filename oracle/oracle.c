@@ -115,9 +115,16 @@ void orc_sigmoid_pinned_array(const float *x, float *y, int64_t n)
  *   softmax, not renorm.:  exp(l_j - m) / sum_e exp(l_e - m), m = max_e l_e
  *   sigmoid, renormalised: s(l_j) / sum_{i<k} s(l_i)
  *   sigmoid, not renorm.:  s(l_j)
+ *
+ * Auxiliary-loss-free balancing ("05 - Expert Parallelism (MoE)", section
+ * "Load balancing", family (b)): with a per-expert bias b (NULL = none) the
+ * choice is TopK(logits + bias) -- the key becomes fl32(l_e + b_e), and the
+ * group scores, being part of the choice, are taken on those keys -- while
+ * the gates above stay functions of the unbiased logits l.  Without a bias
+ * the key is l_e and nothing changes.
  * Returns 0, or -1 on arguments outside the contract.
  * ---------------------------------------------------------------------- */
-int orc_route(const float *logits, int T, int E, int k, int gating, int renorm,
+int orc_route(const float *logits, const float *bias, int T, int E, int k, int gating, int renorm,
               int n_groups, int topk_groups, int32_t *ids, float *w)
 {
     if (T < 0 || E < 1 || k < 1 || k > E || k > 64 || n_groups < 1 || E % n_groups != 0 ||
@@ -137,7 +144,7 @@ int orc_route(const float *logits, int T, int E, int k, int gating, int renorm,
         for (int t = 0; t < T; ++t) {
             const float *l = logits + (int64_t)t * E;
             for (int e = 0; e < E; ++e) {
-                key[e] = l[e] + 0.0f;          /* -0 + +0 = +0 */
+                key[e] = (bias ? l[e] + bias[e] : l[e]) + 0.0f;   /* -0 + +0 = +0 */
                 allowed[e] = 1;
                 taken[e] = 0;
             }
@@ -172,16 +179,16 @@ int orc_route(const float *logits, int T, int E, int k, int gating, int renorm,
             double v[64], sum = 0.0;     /* k <= 64 is checked above */
             if (gating == ORC_SOFTMAX) {
                 if (renorm) {
-                    double l0 = (double)key[id[0]];
-                    for (int j = 0; j < k; ++j) { v[j] = exp((double)key[id[j]] - l0); sum += v[j]; }
+                    double l0 = (double)l[id[0]];
+                    for (int j = 0; j < k; ++j) { v[j] = exp((double)l[id[j]] - l0); sum += v[j]; }
                 } else {
-                    double m = (double)key[0];
-                    for (int e = 1; e < E; ++e) if ((double)key[e] > m) m = (double)key[e];
-                    for (int e = 0; e < E; ++e) sum += exp((double)key[e] - m);
-                    for (int j = 0; j < k; ++j) v[j] = exp((double)key[id[j]] - m);
+                    double m = (double)l[0];
+                    for (int e = 1; e < E; ++e) if ((double)l[e] > m) m = (double)l[e];
+                    for (int e = 0; e < E; ++e) sum += exp((double)l[e] - m);
+                    for (int j = 0; j < k; ++j) v[j] = exp((double)l[id[j]] - m);
                 }
             } else {
-                for (int j = 0; j < k; ++j) { v[j] = 1.0 / (1.0 + exp(-(double)key[id[j]])); sum += v[j]; }
+                for (int j = 0; j < k; ++j) { v[j] = 1.0 / (1.0 + exp(-(double)l[id[j]])); sum += v[j]; }
                 if (!renorm) sum = 1.0;
             }
             for (int j = 0; j < k; ++j) wt[j] = (float)(v[j] / sum);
@@ -332,6 +339,50 @@ double orc_alltoall_bytes(int64_t T_loc, int k, int64_t d, int n_ep, double s_di
     double per = (double)T_loc * k * (double)d * (double)(n_ep - 1) / (double)n_ep;
     double b = per * s_disp + per * s_comb;
     return training ? 2.0 * b : b;
+}
+
+/* ------------------------------------------------------------------------
+ * O0  Router logits (step 1 of the forward pass: "compute the router").
+ * logits[t][e] = sum_i x[t][i] wg[e][i]: one row of wg per expert, d inputs
+ * per row (the same K-contiguous layout as the expert matrices).  The sum
+ * runs in fp64 in index order and is rounded once to fp32, the precision
+ * routing takes its decisions in.
+ * ---------------------------------------------------------------------- */
+void orc_router_logits(const void *x, int dtype, int64_t T, int d, const void *wg, int E,
+                       float *logits)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i)
+                acc += widen(x, dtype, t * d + i) * widen(wg, dtype, (int64_t)e * d + i);
+            logits[t * E + e] = (float)acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Bias update of auxiliary-loss-free balancing ("05 - Expert Parallelism
+ * (MoE)", section "Load balancing", family (b)): after a step, with load[i]
+ * the tokens expert i received, bias[i] += lr * (avg_load - load[i]), so an
+ * under-loaded expert's bias rises and an over-loaded one's falls.  In fp32,
+ * one rounding per operation: avg = fl(M) / fl(E) with M = sum of the loads,
+ * then fl(avg - fl(load[i])), times lr, added to bias[i].
+ * Returns 0, or -1 on arguments outside the contract.
+ * ---------------------------------------------------------------------- */
+int orc_bias_update(const int32_t *counts, int E, float lr, float *bias)
+{
+    if (E < 1) return -1;
+    int64_t M = 0;
+    for (int e = 0; e < E; ++e) M += counts[e];
+    const float avg = (float)M / (float)E;
+    for (int e = 0; e < E; ++e) {
+        const float dev = avg - (float)counts[e];
+        const float step = lr * dev;
+        bias[e] = bias[e] + step;
+    }
+    return 0;
 }
 
 /* Number of OpenMP threads the oracle's parallel loops use. */

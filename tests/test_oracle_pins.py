@@ -439,3 +439,114 @@ def test_sparse_layer_equals_dense_masked(gating, n_groups, topk_groups, shared)
     tok = np.array([0, 5, 15])
     yt = oracle.layer_tokens(x, ids, w, w13, w2, tok, *( (s13, s2) if shared else (None, None)))
     np.testing.assert_allclose(yt, dense[tok], rtol=1e-11, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# RM, "Load balancing — the hard part": auxiliary-loss-free bias
+# --------------------------------------------------------------------------
+
+def test_bias_update_exercise():
+    g = _golden("bias_update.json")
+    counts = np.array(g["stated"]["counts"], np.int32)
+    assert counts.mean() == g["stated"]["target_avg"]
+    b = oracle.bias_update(np.zeros(4, np.float32), counts, g["derived"]["lr"])
+    assert b.tolist() == g["derived"]["bias_after"]
+    # the stated direction, for any positive rate
+    d = oracle.bias_update(np.zeros(4, np.float32), counts, 1e-3)
+    assert d[1] > 0 and d[3] > 0 and d[2] < 0 and d[0] == 0
+
+
+def test_bias_update_invariants():
+    r = np.random.default_rng(5)
+    E = 256
+    counts = r.integers(0, 600, E).astype(np.int32)
+    counts[-1] += E * 300 - counts.sum() if counts.sum() < E * 300 else 0
+    b0 = r.standard_normal(E).astype(np.float32)
+    lr = np.float32(1e-3)
+    b1 = oracle.bias_update(b0, counts, lr)
+    # each entry is fl(b0 + fl(lr * fl(avg - count))) with avg = fl(M) / fl(E)
+    avg = np.float32(np.float32(counts.sum()) / np.float32(E))
+    ref = (b0 + (lr * (avg - counts.astype(np.float32))).astype(np.float32)).astype(np.float32)
+    assert np.array_equal(b1, ref)
+    # updates follow the sign of (avg - load), zero when the load is the mean
+    step = b1.astype(np.float64) - b0
+    dev = float(avg) - counts
+    assert np.all(np.sign(step[np.abs(dev) > 1]) == np.sign(dev[np.abs(dev) > 1]))
+    # balanced loads leave the bias unchanged
+    assert np.array_equal(oracle.bias_update(b0, np.full(E, 7, np.int32), lr), b0)
+
+
+def test_route_bias_zero_is_no_bias():
+    r = np.random.default_rng(11)
+    logits = r.standard_normal((64, 32)).astype(np.float32)
+    for gating, ng, tg in (("softmax", 1, 1), ("sigmoid", 4, 2)):
+        a = oracle.route(logits, 4, gating, 1, ng, tg)
+        b = oracle.route(logits, 4, gating, 1, ng, tg, bias=np.zeros(32, np.float32))
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("gating,n_groups,topk_groups", [("softmax", 1, 1), ("sigmoid", 1, 1),
+                                                         ("sigmoid", 4, 2)])
+def test_route_bias_selects_on_biased_keys_bruteforce(gating, n_groups, topk_groups):
+    """TopK(logits + bias): brute force over all k-subsets of the allowed
+    experts; gates from the unbiased logits."""
+    r = np.random.default_rng(3)
+    T, E, k = 40, 8, 2
+    logits = r.standard_normal((T, E)).astype(np.float32)
+    bias = (r.standard_normal(E) * 0.7).astype(np.float32)
+    ids, w = oracle.route(logits, k, gating, 1, n_groups, topk_groups, bias=bias)
+    key = (logits + bias).astype(np.float32)
+    gs = E // n_groups
+    for t in range(T):
+        allowed = list(range(E))
+        if n_groups > 1:
+            aff = oracle.sigmoid_pinned(key[t])
+            score = [np.float32(sorted(aff[g * gs:(g + 1) * gs])[-1]) + np.float32(sorted(aff[g * gs:(g + 1) * gs])[-2])
+                     for g in range(n_groups)]
+            kept = sorted(range(n_groups), key=lambda g: (-score[g], g))[:topk_groups]
+            allowed = [e for e in range(E) if e // gs in kept]
+        best = max(itertools.combinations(allowed, k),
+                   key=lambda c: (sorted(key[t, list(c)])[::-1], [-e for e in sorted(c)]))
+        chosen = sorted(best, key=lambda e: (-key[t, e], e))
+        assert ids[t].tolist() == chosen
+        l = logits[t, chosen].astype(np.float64)
+        g = np.exp(l - l[0]) if gating == "softmax" else 1 / (1 + np.exp(-l))
+        np.testing.assert_allclose(w[t], g / g.sum(), rtol=2e-7)
+
+
+def test_route_bias_changes_choice_not_gates():
+    """A bias large enough to promote expert 1 over expert 0 changes the
+    choice; the gate of the chosen expert is still computed from its logit."""
+    logits = np.array([[2.0, 1.5, 1.0, 0.0]], np.float32)
+    ids0, w0 = oracle.route(logits, 2, "sigmoid", 0)
+    ids1, w1 = oracle.route(logits, 2, "sigmoid", 0, bias=np.array([0, 0, 1.5, 0], np.float32))
+    assert ids0.tolist() == [[0, 1]] and ids1.tolist() == [[2, 0]]
+    s = 1 / (1 + np.exp(-np.array([1.0, 2.0])))
+    np.testing.assert_allclose(w1[0], s.astype(np.float32), rtol=1e-7)
+
+
+# --------------------------------------------------------------------------
+# EP, step 1 of the forward pass: "compute the router"
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_router_logits_match_library_matmul(dtype):
+    r = np.random.default_rng(2)
+    x = r.standard_normal((37, 96)).astype(np.float32)
+    wg = (r.standard_normal((11, 96)) * 0.1).astype(np.float32)
+    if dtype == "bf16":
+        x, wg = inputs.f32_to_bf16_bits(x), inputs.f32_to_bf16_bits(wg)
+        xf, wf = inputs.bf16_bits_to_f32(x).reshape(37, 96), inputs.bf16_bits_to_f32(wg).reshape(11, 96)
+    else:
+        xf, wf = x, wg
+    got = oracle.router_logits(x, wg)
+    ref = (xf.astype(np.float64) @ wf.astype(np.float64).T).astype(np.float32)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=float(np.abs(ref).max()) * 2e-7)
+
+
+def test_router_logits_one_hot_closed_form():
+    """A token that is the unit vector e_i gets logits wg[:, i] exactly."""
+    r = np.random.default_rng(4)
+    wg = r.standard_normal((9, 16)).astype(np.float32)
+    x = np.eye(16, dtype=np.float32)
+    assert np.array_equal(oracle.router_logits(x, wg), wg.T.copy())
