@@ -85,6 +85,55 @@ moe_status moe_route_topk(const float *logits, int T, int E, int k, moe_gating g
                           float *topk_w, hipStream_t stream);
 
 /*
+ * moe_route_topk with auxiliary-loss-free balancing ("05 - Expert
+ * Parallelism (MoE)", section "Load balancing", family (b)): the choice is
+ * TopK(logits + bias).  Every selection -- the group scores of the group
+ * limit included -- ranks the fp32 keys fl32(logit + bias[e]) (-0 counts as
+ * +0), while the gates are the formulas of moe_route_topk evaluated on the
+ * unbiased logits of the chosen experts.
+ *
+ *   bias  [E] fp32 device array, one entry per expert.
+ * Every other argument, and every error, as in moe_route_topk; a null bias
+ * is INVALID_ARG (for T > 0).  A zero bias gives moe_route_topk's results bit
+ * for bit.
+ */
+moe_status moe_route_topk_biased(const float *logits, const float *bias, int T, int E, int k,
+                                 moe_gating gating, int renormalize, int n_groups,
+                                 int topk_groups, int32_t *topk_ids, float *topk_w,
+                                 hipStream_t stream);
+
+/*
+ * Router product (step 1 of the forward pass computes the router before the
+ * top-k choice): logits[t][e] = sum_i x[t][i] w_router[e][i], accumulated in
+ * fp32 (MFMA), written in fp32.
+ *
+ *   x         [T, d] token rows, dtype dt.
+ *   w_router  [E, d] one row of d inputs per expert (K-contiguous, like the
+ *             expert matrices), dtype dt.
+ *   logits    [T, E] fp32 out.
+ * Errors: INVALID_ARG for null pointers, T < 0, d < 1, E < 1, misaligned x or
+ * w_router; UNSUPPORTED for d elem not a multiple of 128 bytes, or x or
+ * w_router of 64 GiB or more.
+ */
+moe_status moe_router_logits(const void *x, moe_dtype dt, int T, int d, const void *w_router,
+                             int E, float *logits, hipStream_t stream);
+
+/*
+ * Bias update of auxiliary-loss-free balancing ("05 - Expert Parallelism
+ * (MoE)", section "Load balancing", family (b)): after a step,
+ *     bias[e] += lr * (avg - counts[e]),   avg = fl(M) / fl(E),
+ * M the sum of the counts (moe_permute's per-expert histogram), one fp32
+ * rounding per operation, so an under-loaded expert's bias rises and an
+ * over-loaded one's falls.
+ *
+ *   counts  [E] int32 device array; bias [E] fp32 device array, updated in
+ *   place.  lr is a host value.
+ * Errors: INVALID_ARG for null pointers or E < 1; UNSUPPORTED for E > 1024.
+ */
+moe_status moe_router_bias_update(const int32_t *counts, int E, float lr, float *bias,
+                                  hipStream_t stream);
+
+/*
  * The pinned fp32 sigmoid applied elementwise: y[i] = s(x[i]), n elements.
  * s(x) = 1/(1+t) for x >= 0 and t/(1+t) otherwise, t = exp(-|x|), where exp
  * is Cody & Waite reduction (ln2 split into a 12-significant-bit head and a

@@ -141,6 +141,26 @@ def test_permute_index_only_validation(lib):
     assert f(NULL, 1, 8, 16, a, 2, 4, a, a, a, a, a, a, ws, NULL) == INVALID   # x_perm without x
 
 
+def test_router_validation(lib):
+    a = ctypes.c_void_p(16)
+    f = lib.moe_router_logits
+    #       x  dt T  d    w  E  logits stream
+    assert f(a, 1, 4, 96, a, 8, a, NULL) == UNSUPPORTED      # 192-byte rows
+    assert f(a, 1, 4, 128, a, 0, a, NULL) == INVALID         # E < 1
+    assert f(a, 1, 4, 128, NULL, 8, a, NULL) == INVALID      # null weights
+    assert f(a, 1, 4, 128, ctypes.c_void_p(24), 8, a, NULL) == INVALID   # misaligned
+    assert f(NULL, 1, 0, 128, NULL, 8, NULL, NULL) == 0      # T = 0: no-op
+    g = lib.moe_router_bias_update
+    assert g(a, 0, ctypes.c_float(1.0), a, NULL) == INVALID
+    assert g(a, 2000, ctypes.c_float(1.0), a, NULL) == UNSUPPORTED
+    assert g(NULL, 4, ctypes.c_float(1.0), a, NULL) == INVALID
+    h = lib.moe_route_topk_biased
+    #       logits bias T  E  k  gating renorm ng tg ids w  stream
+    assert h(a, NULL, 4, 8, 2, 0, 1, 1, 1, a, a, NULL) == INVALID   # null bias
+    assert h(a, a, 4, 8, 9, 0, 1, 1, 1, a, a, NULL) == INVALID      # k > E
+    assert h(NULL, NULL, 0, 8, 2, 0, 1, 1, 1, NULL, NULL, NULL) == 0
+
+
 def test_combine_validation(lib):
     f = lib.moe_unpermute_combine
     a = ctypes.c_void_p(16)

@@ -105,6 +105,139 @@ def test_route_topk(lib, case):
     np.testing.assert_allclose(host(w), w_ref, rtol=1e-5, atol=1e-7)
 
 
+@pytest.mark.parametrize("case", [c for c in ROUTE_CASES if c[0] <= 2000])
+def test_route_topk_biased(lib, case):
+    """Selection on logits + bias (bit-exact ids), gates from the logits."""
+    T, E, k, gating, renorm, ng, tg, integer = case
+    r = np.random.default_rng(T * 37 + E + k)
+    if integer:
+        logits = r.integers(-2, 3, size=(T, E)).astype(np.float32)
+        bias = r.integers(-1, 2, size=E).astype(np.float32) * 0.5   # ties stay ties
+    else:
+        logits = r.standard_normal((T, E), dtype=np.float32)
+        bias = (r.standard_normal(E) * 0.3).astype(np.float32)
+    ids_ref, w_ref = oracle.route(logits, k, gating, renorm, ng, tg, bias=bias)
+    ids, w = lib.moe_route_topk(dev(logits), k, gating, renorm, ng, tg, bias=dev(bias))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ids), ids_ref)
+    np.testing.assert_allclose(host(w), w_ref, rtol=1e-5, atol=1e-7)
+
+
+def test_route_topk_zero_bias_is_unbiased(lib):
+    r = np.random.default_rng(8)
+    logits = dev(r.standard_normal((1000, 256), dtype=np.float32))
+    a = lib.moe_route_topk(logits, 8, "sigmoid", 1, 8, 4)
+    b = lib.moe_route_topk(logits, 8, "sigmoid", 1, 8, 4, bias=torch.zeros(256, device="cuda"))
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert np.array_equal(host(x).view(np.uint32), host(y).view(np.uint32))
+
+
+ROUTER_CASES = [
+    # dtype, T, d, E
+    ("f32", 300, 256, 8),
+    ("bf16", 1000, 7168, 256),
+    ("bf16", 65, 128, 70),
+    ("f32", 129, 512, 130),
+    ("bf16", 4096, 4096, 8),
+    ("bf16", 1, 64, 1),
+]
+
+
+@pytest.mark.parametrize("case", ROUTER_CASES)
+def test_router_logits(lib, case):
+    """fp32-accumulated router product against the oracle's fp64 sums: per
+    row max |gpu - oracle| <= 1e-4 max |oracle row|."""
+    dt, T, d, E = case
+    r = np.random.default_rng(T + d + E)
+    x = r.standard_normal((T, d), dtype=np.float32)
+    wg = (r.standard_normal((E, d)) * (1.0 / np.sqrt(d))).astype(np.float32)
+    if dt == "bf16":
+        x, wg = inputs.f32_to_bf16_bits(x), inputs.f32_to_bf16_bits(wg)
+    ref = oracle.router_logits(x, wg).astype(np.float64)
+    got = host(lib.moe_router_logits(dev(x), dev(wg)))
+    torch.cuda.synchronize()
+    rows_close(got, ref, 1e-4)
+
+
+def test_router_logits_errors(lib):
+    x = torch.zeros((4, 96), dtype=torch.bfloat16, device="cuda")      # 192-byte rows
+    with pytest.raises(lib.MoeError):
+        lib.moe_router_logits(x, torch.zeros((8, 96), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(lib.MoeError):
+        lib.moe_router_logits(torch.zeros((4, 128), dtype=torch.bfloat16, device="cuda"),
+                              torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda"))
+    out = lib.moe_router_logits(torch.zeros((0, 128), dtype=torch.float32, device="cuda"),
+                                torch.zeros((8, 128), dtype=torch.float32, device="cuda"))
+    assert tuple(out.shape) == (0, 8)
+
+
+def _safe_tokens(logits, bias, k, n_groups, topk_groups, margin):
+    """Tokens whose choice is decided by more than `margin` (in key units) at
+    both the group and the expert cut, so any logits within margin / 4 of
+    these give the same chosen set."""
+    key = (logits + bias).astype(np.float32)
+    T, E = key.shape
+    safe = np.ones(T, bool)
+    allowed = np.ones((T, E), bool)
+    if n_groups > 1:
+        gs = E // n_groups
+        aff = oracle.sigmoid_pinned(key).reshape(T, n_groups, gs)
+        top2 = np.sort(aff, axis=2)[:, :, -2:].sum(axis=2)
+        srt = np.sort(top2, axis=1)[:, ::-1]
+        safe &= (srt[:, topk_groups - 1] - srt[:, topk_groups]) > margin
+        kept = top2 >= srt[:, topk_groups - 1:topk_groups]
+        allowed = np.repeat(kept, gs, axis=1)
+    kk = np.where(allowed, key, -np.inf)
+    srt = np.sort(kk, axis=1)[:, ::-1]
+    safe &= (srt[:, k - 1] - srt[:, k]) > margin
+    return safe
+
+
+@pytest.mark.parametrize("dt,gating,ng,tg", [("bf16", "sigmoid", 8, 4), ("f32", "softmax", 1, 1)])
+def test_router_chain_matches_oracle(lib, dt, gating, ng, tg):
+    """Router product then biased route on the GPU against the same chain in
+    the oracle: logits to the router's tolerance; chosen expert sets equal on
+    every token whose choice is decided by more than the logits' error."""
+    T, d, E, k = 2048, 1024, 256, 8
+    r = np.random.default_rng(21)
+    x = r.standard_normal((T, d), dtype=np.float32)
+    wg = (r.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)
+    bias = (r.standard_normal(E) * 0.1).astype(np.float32)
+    if dt == "bf16":
+        x, wg = inputs.f32_to_bf16_bits(x), inputs.f32_to_bf16_bits(wg)
+    lg_ref = oracle.router_logits(x, wg)
+    ids_ref, w_ref = oracle.route(lg_ref, k, gating, 1, ng, tg, bias=bias)
+    lg = lib.moe_router_logits(dev(x), dev(wg))
+    ids, w = lib.moe_route_topk(lg, k, gating, 1, ng, tg, bias=dev(bias))
+    torch.cuda.synchronize()
+    lg_h = host(lg)
+    rows_close(lg_h, lg_ref.astype(np.float64), 1e-4)
+    err = float(np.abs(lg_h.astype(np.float64) - lg_ref).max())
+    safe = _safe_tokens(lg_ref, bias, k, ng, tg, 4 * err + 1e-6)
+    assert safe.mean() > 0.9, safe.mean()
+    got = np.sort(host(ids)[safe], axis=1)
+    assert np.array_equal(got, np.sort(ids_ref[safe], axis=1))
+    np.testing.assert_allclose(np.sort(host(w)[safe], axis=1), np.sort(w_ref[safe], axis=1),
+                               rtol=1e-4, atol=1e-6)
+
+
+@pytest.mark.parametrize("E,lr", [(4, 0.25), (256, 1e-3), (1024, 3e-2), (1, 1.0)])
+def test_router_bias_update(lib, E, lr):
+    """Bit-exact against the oracle; the page's exercise for E = 4."""
+    r = np.random.default_rng(E)
+    counts = (np.array([100, 50, 200, 50], np.int32) if E == 4
+              else r.integers(0, 5000, E).astype(np.int32))
+    bias = (np.zeros(E) if E == 4 else r.standard_normal(E)).astype(np.float32)
+    ref = oracle.bias_update(bias, counts, lr)
+    b = dev(bias)
+    lib.moe_router_bias_update(dev(counts), b, lr)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(b).view(np.uint32), ref.view(np.uint32))
+    if E == 4:
+        assert host(b).tolist() == [0.0, 12.5, -25.0, 12.5]
+
+
 def test_route_empty_and_errors(lib):
     logits = torch.zeros((0, 8), dtype=torch.float32, device="cuda")
     ids, w = lib.moe_route_topk(logits, 2)

@@ -19,7 +19,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 
 # Every symbol include/moe355.h declares.
-EXPORTS = ("moe_status_string", "moe_route_topk", "moe_sigmoid_pinned", "moe_send_counts",
+EXPORTS = ("moe_status_string", "moe_route_topk", "moe_route_topk_biased", "moe_router_logits",
+           "moe_router_bias_update", "moe_sigmoid_pinned", "moe_send_counts",
            "moe_permute_workspace_bytes", "moe_permute", "moe_grouped_swiglu",
            "moe_grouped_gate_up", "moe_grouped_gate_up_gather", "moe_grouped_down",
            "moe_unpermute_combine")
@@ -44,6 +45,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_route_topk.argtypes = [P, i32, i32, i32, i32, i32, i32, i32, P, P, P]
+    lib.moe_route_topk_biased.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, P, P, P]
+    lib.moe_router_logits.argtypes = [P, i32, i32, i32, P, i32, P, P]
+    lib.moe_router_bias_update.argtypes = [P, i32, ctypes.c_float, P, P]
     lib.moe_sigmoid_pinned.argtypes = [P, P, i64, P]
     lib.moe_send_counts.argtypes = [P, i32, i32, i32, i32, P, P]
     lib.moe_permute_workspace_bytes.argtypes = [i32, i32, i32]
@@ -54,7 +58,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_grouped_gate_up_gather.argtypes = [P, i32, i32, i32, i32, i32, P, P, i32, P, P, P]
     lib.moe_grouped_down.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P]
     lib.moe_unpermute_combine.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P]
-    for name in ("moe_route_topk", "moe_sigmoid_pinned", "moe_send_counts", "moe_permute",
+    for name in ("moe_route_topk", "moe_route_topk_biased", "moe_router_logits",
+                 "moe_router_bias_update", "moe_sigmoid_pinned", "moe_send_counts", "moe_permute",
                  "moe_grouped_swiglu", "moe_grouped_gate_up", "moe_grouped_gate_up_gather",
                  "moe_grouped_down", "moe_unpermute_combine"):
         getattr(lib, name).restype = i32
@@ -114,8 +119,11 @@ def moe_sigmoid_pinned(x, y=None, stream=None):
 
 
 def moe_route_topk(logits, k, gating="softmax", renormalize=True, n_groups=1, topk_groups=1,
-                   topk_ids=None, topk_w=None, stream=None):
-    """Top-k ids [T,k] int32 and gates [T,k] fp32 from fp32 logits [T,E]."""
+                   topk_ids=None, topk_w=None, stream=None, bias=None):
+    """Top-k ids [T,k] int32 and gates [T,k] fp32 from fp32 logits [T,E].
+
+    bias [E] fp32 (optional) selects through moe_route_topk_biased: the
+    choice on logits + bias, the gates on the logits."""
     torch = _torch()
     _dev(logits, "logits", (torch.float32,))
     T, E = logits.shape
@@ -126,10 +134,49 @@ def moe_route_topk(logits, k, gating="softmax", renormalize=True, n_groups=1, to
     _dev(topk_ids, "topk_ids", (torch.int32,))
     _dev(topk_w, "topk_w", (torch.float32,))
     g = MOE_SOFTMAX if gating == "softmax" else MOE_SIGMOID if gating == "sigmoid" else -1
-    _check(load_library().moe_route_topk(_ptr(logits), T, E, k, g, int(bool(renormalize)),
-                                         n_groups, topk_groups, _ptr(topk_ids), _ptr(topk_w),
-                                         _stream(stream)), "moe_route_topk")
+    lib = load_library()
+    if bias is None:
+        _check(lib.moe_route_topk(_ptr(logits), T, E, k, g, int(bool(renormalize)), n_groups,
+                                  topk_groups, _ptr(topk_ids), _ptr(topk_w), _stream(stream)),
+               "moe_route_topk")
+    else:
+        _dev(bias, "bias", (torch.float32,))
+        if bias.numel() != E:
+            raise MoeError("moe_route_topk_biased: bias must have one entry per expert")
+        _check(lib.moe_route_topk_biased(_ptr(logits), _ptr(bias), T, E, k, g,
+                                         int(bool(renormalize)), n_groups, topk_groups,
+                                         _ptr(topk_ids), _ptr(topk_w), _stream(stream)),
+               "moe_route_topk_biased")
     return topk_ids, topk_w
+
+
+def moe_router_logits(x, w_router, logits=None, stream=None):
+    """logits [T,E] fp32 = x [T,d] . w_router [E,d]^T (fp32 accumulation)."""
+    torch = _torch()
+    _dev(x, "x", _act_dtypes())
+    _dev(w_router, "w_router", (x.dtype,))
+    T, d = x.shape
+    E, d2 = w_router.shape
+    if d2 != d:
+        raise MoeError("moe_router_logits: w_router must be [E, d]")
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if logits is None else logits
+    _dev(logits, "logits", (torch.float32,))
+    _check(load_library().moe_router_logits(_ptr(x), _dtype_code(x), T, d, _ptr(w_router), E,
+                                            _ptr(logits), _stream(stream)), "moe_router_logits")
+    return logits
+
+
+def moe_router_bias_update(counts, bias, lr, stream=None):
+    """bias [E] += lr (mean(counts) - counts), in place (fp32, one rounding per operation)."""
+    torch = _torch()
+    _dev(counts, "counts", (torch.int32,))
+    _dev(bias, "bias", (torch.float32,))
+    if counts.numel() != bias.numel():
+        raise MoeError("moe_router_bias_update: counts and bias must have E entries each")
+    _check(load_library().moe_router_bias_update(_ptr(counts), counts.numel(), float(lr),
+                                                 _ptr(bias), _stream(stream)),
+           "moe_router_bias_update")
+    return bias
 
 
 def moe_send_counts(topk_ids, E, n_ep, send_counts=None, stream=None):

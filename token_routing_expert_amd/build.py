@@ -1,8 +1,8 @@
 """Build libmoe355.so in-tree with hipcc for gfx950.
 
-Each .hip file compiles to its own object (the router keeps -ffp-contract=off
-so its pinned sigmoid is exactly the written operation sequence), then one
-shared library is linked.  Run as ``python -m token_routing_expert_amd.build``.
+Each .hip file compiles to its own object (route and router keep
+-ffp-contract=off so the pinned sigmoid and the bias update are exactly the
+written operation sequences), then one shared library is linked.  Run as ``python -m token_routing_expert_amd.build``.
 """
 from __future__ import annotations
 
@@ -19,14 +19,14 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe355.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip"]
+SOURCES = ["route.hip", "router.hip", "permute.hip", "grouped_gemm.hip", "combine.hip"]
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
     # Packed fp32 VALU forms stay off; the compiler emits scalar fp32 instead.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-Wall", "-Wno-unused-function",
 ]
-PER_FILE = {"route.hip": ["-ffp-contract=off"]}
+PER_FILE = {"route.hip": ["-ffp-contract=off"], "router.hip": ["-ffp-contract=off"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

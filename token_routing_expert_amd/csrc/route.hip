@@ -75,9 +75,13 @@ __device__ __forceinline__ void wave_argmax(float &k, int &i) {
 }
 
 // One wave per token.  Lane l holds experts l, l + 64, ... (NPER of them), so
-// each pass over the logits row is one coalesced 256-byte load.
+// each pass over the logits row is one coalesced 256-byte load.  With a bias
+// (auxiliary-loss-free balancing, "05 - Expert Parallelism (MoE)", section
+// "Load balancing"), the choice -- group scores included -- is taken on the
+// keys fl32(logit + bias) and the gates on the unbiased logits.
 template <int NPER>
-__global__ __launch_bounds__(256) void k_route_topk(const float *__restrict__ logits, int T, int E,
+__global__ __launch_bounds__(256) void k_route_topk(const float *__restrict__ logits,
+                                                    const float *__restrict__ bias, int T, int E,
                                                     int k, int gating, int renorm, int n_groups,
                                                     int topk_groups, int32_t *__restrict__ ids,
                                                     float *__restrict__ w) {
@@ -86,14 +90,16 @@ __global__ __launch_bounds__(256) void k_route_topk(const float *__restrict__ lo
   if (t >= T) return;
   const float *row = logits + (size_t)t * E;
 
-  float key[NPER];
+  float key[NPER], lg[NPER];
   uint32_t cand = 0;  // bit i: slot i holds a selectable expert
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = i * kWave + lane;
     key[i] = -INFINITY;
+    lg[i] = -INFINITY;
     if (e < E) {
-      key[i] = row[e] + 0.0f;  // -0 becomes +0
+      lg[i] = row[e] + 0.0f;  // -0 becomes +0
+      key[i] = bias ? (row[e] + bias[e]) + 0.0f : lg[i];
       cand |= 1u << i;
     }
   }
@@ -145,7 +151,8 @@ __global__ __launch_bounds__(256) void k_route_topk(const float *__restrict__ lo
       if (grp[i] >= 0 && !((kept >> grp[i]) & 1ull)) cand &= ~(1u << i);
   }
 
-  // k rounds of a wave-wide argmax; lane j keeps the j-th pick.
+  // k rounds of a wave-wide argmax; lane j keeps the j-th pick and its
+  // unbiased logit (fetched from the lane that holds the winner).
   int my_id = kNone;
   float my_key = -INFINITY, first_key = -INFINITY;
   for (int j = 0; j < k; ++j) {
@@ -157,9 +164,17 @@ __global__ __launch_bounds__(256) void k_route_topk(const float *__restrict__ lo
       if ((cand >> i & 1u) && (bi == kNone || key[i] > bk)) { bk = key[i]; bi = e; }
     }
     wave_argmax(bk, bi);
+    float bl = bk;
+    if (bias) {
+      float mine = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        if (i == (bi >> 6)) mine = lg[i];
+      bl = __shfl(mine, bi & (kWave - 1));
+    }
     if (lane == (bi & (kWave - 1))) cand &= ~(1u << (bi >> 6));
-    if (lane == j) { my_id = bi; my_key = bk; }
-    if (j == 0) first_key = bk;
+    if (lane == j) { my_id = bi; my_key = bl; }
+    if (j == 0) first_key = bl;
   }
 
   float v = 0.0f, denom = 1.0f;
@@ -171,12 +186,12 @@ __global__ __launch_bounds__(256) void k_route_topk(const float *__restrict__ lo
       float m = -INFINITY;
 #pragma unroll
       for (int i = 0; i < NPER; ++i)
-        if (i * kWave + lane < E) m = fmaxf(m, key[i]);
+        if (i * kWave + lane < E) m = fmaxf(m, lg[i]);
       m = wave_max(m);
       float s = 0.0f;
 #pragma unroll
       for (int i = 0; i < NPER; ++i)
-        if (i * kWave + lane < E) s += expf(key[i] - m);
+        if (i * kWave + lane < E) s += expf(lg[i] - m);
       denom = wave_sum(s);
       v = lane < k ? expf(my_key - m) : 0.0f;
     }
@@ -219,9 +234,9 @@ __global__ __launch_bounds__(256) void k_send_counts(const int32_t *__restrict__
 
 using namespace moe;
 
-extern "C" moe_status moe_route_topk(const float *logits, int T, int E, int k, moe_gating gating,
-                                     int renormalize, int n_groups, int topk_groups,
-                                     int32_t *topk_ids, float *topk_w, hipStream_t stream) {
+static moe_status route_topk(const float *logits, const float *bias, int T, int E, int k,
+                             moe_gating gating, int renormalize, int n_groups, int topk_groups,
+                             int32_t *topk_ids, float *topk_w, hipStream_t stream) {
   if (T < 0 || E < 1 || k < 1 || k > E || n_groups < 1 || topk_groups < 1 ||
       topk_groups > n_groups || E % n_groups != 0)
     return MOE_ERR_INVALID_ARG;
@@ -234,16 +249,32 @@ extern "C" moe_status moe_route_topk(const float *logits, int T, int E, int k, m
   const dim3 grid((T + 3) / 4), block(256);
   const int rn = renormalize ? 1 : 0;
   if (E <= 64)
-    k_route_topk<1><<<grid, block, 0, stream>>>(logits, T, E, k, gating, rn, n_groups, topk_groups, topk_ids, topk_w);
+    k_route_topk<1><<<grid, block, 0, stream>>>(logits, bias, T, E, k, gating, rn, n_groups, topk_groups, topk_ids, topk_w);
   else if (E <= 128)
-    k_route_topk<2><<<grid, block, 0, stream>>>(logits, T, E, k, gating, rn, n_groups, topk_groups, topk_ids, topk_w);
+    k_route_topk<2><<<grid, block, 0, stream>>>(logits, bias, T, E, k, gating, rn, n_groups, topk_groups, topk_ids, topk_w);
   else if (E <= 256)
-    k_route_topk<4><<<grid, block, 0, stream>>>(logits, T, E, k, gating, rn, n_groups, topk_groups, topk_ids, topk_w);
+    k_route_topk<4><<<grid, block, 0, stream>>>(logits, bias, T, E, k, gating, rn, n_groups, topk_groups, topk_ids, topk_w);
   else if (E <= 512)
-    k_route_topk<8><<<grid, block, 0, stream>>>(logits, T, E, k, gating, rn, n_groups, topk_groups, topk_ids, topk_w);
+    k_route_topk<8><<<grid, block, 0, stream>>>(logits, bias, T, E, k, gating, rn, n_groups, topk_groups, topk_ids, topk_w);
   else
-    k_route_topk<16><<<grid, block, 0, stream>>>(logits, T, E, k, gating, rn, n_groups, topk_groups, topk_ids, topk_w);
+    k_route_topk<16><<<grid, block, 0, stream>>>(logits, bias, T, E, k, gating, rn, n_groups, topk_groups, topk_ids, topk_w);
   return launch_status();
+}
+
+extern "C" moe_status moe_route_topk(const float *logits, int T, int E, int k, moe_gating gating,
+                                     int renormalize, int n_groups, int topk_groups,
+                                     int32_t *topk_ids, float *topk_w, hipStream_t stream) {
+  return route_topk(logits, nullptr, T, E, k, gating, renormalize, n_groups, topk_groups, topk_ids,
+                    topk_w, stream);
+}
+
+extern "C" moe_status moe_route_topk_biased(const float *logits, const float *bias, int T, int E,
+                                            int k, moe_gating gating, int renormalize,
+                                            int n_groups, int topk_groups, int32_t *topk_ids,
+                                            float *topk_w, hipStream_t stream) {
+  if (T > 0 && !bias) return MOE_ERR_INVALID_ARG;
+  return route_topk(logits, bias, T, E, k, gating, renormalize, n_groups, topk_groups, topk_ids,
+                    topk_w, stream);
 }
 
 extern "C" moe_status moe_sigmoid_pinned(const float *x, float *y, int64_t n, hipStream_t stream) {

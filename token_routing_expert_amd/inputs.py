@@ -10,7 +10,7 @@ Every tensor comes from its own numpy ``Generator(PCG64(SeedSequence(
 
   stream 1 logits, 2 x, 3 w13 (index = expert), 4 w2 (index = expert),
   5 shared w13, 6 shared w2, 7 cold-expert split of the EP share,
-  8 gates of the EP share, 9 parity sample.
+  8 gates of the EP share, 9 parity sample, 10 router matrix.
 
 Normal draws are fp32 ``standard_normal`` times the stated std; bf16
 tensors are those fp32 draws rounded to nearest-even and kept as uint16 bit
@@ -32,7 +32,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-S_LOGITS, S_X, S_W13, S_W2, S_SH_W13, S_SH_W2, S_COLD, S_GATES, S_SAMPLE = range(1, 10)
+S_LOGITS, S_X, S_W13, S_W2, S_SH_W13, S_SH_W2, S_COLD, S_GATES, S_SAMPLE, S_ROUTER = range(1, 11)
 
 
 @dataclass(frozen=True)
@@ -149,6 +149,12 @@ def _normal_into(out: np.ndarray, g: np.random.Generator, std: float) -> None:
 def gen_logits(cfg: MoeConfig) -> np.ndarray:
     """Router logits [T, E], fp32 N(0,1)."""
     return rng(cfg, S_LOGITS).standard_normal((cfg.T, cfg.E), dtype=np.float32)
+
+
+def gen_router_weights(cfg: MoeConfig) -> np.ndarray:
+    """Router matrix [E, d], N(0, 1/d) in the layer dtype, so that with x ~ N(0,1)
+    the router's logits are ~N(0,1) like gen_logits'."""
+    return _normal(rng(cfg, S_ROUTER), cfg.E * cfg.d, 1.0 / np.sqrt(cfg.d), cfg.dtype).reshape(cfg.E, cfg.d)
 
 
 def gen_x(cfg: MoeConfig) -> np.ndarray:

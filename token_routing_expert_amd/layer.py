@@ -12,7 +12,7 @@ import numpy as np
 
 from . import (moe_grouped_down, moe_grouped_gate_up, moe_grouped_gate_up_gather,
                moe_grouped_swiglu, moe_permute, moe_permute_workspace_bytes, moe_route_topk,
-               moe_send_counts, moe_unpermute_combine)
+               moe_router_bias_update, moe_router_logits, moe_send_counts, moe_unpermute_combine)
 from .inputs import MoeConfig
 
 
@@ -40,10 +40,17 @@ class MoeLayer:
     fused_gather=True skips the packed copy X[order]: the permute computes
     indices only and the first expert product reads the token rows through
     order itself (moe_grouped_gate_up_gather).  Both paths give the same bits.
+
+    w_router [E, d] (optional) puts the router product in front of the route:
+    each forward computes the logits from x.  bias [E] fp32 (optional)
+    selects on logits + bias (auxiliary-loss-free balancing); with
+    bias_lr != 0 every forward ends with the bias update from that batch's
+    per-expert counts, so the next forward routes with the new bias.
     """
 
     def __init__(self, cfg: MoeConfig, x, w13, w2, logits=None, sh_w13=None, sh_w2=None,
-                 topk_ids=None, topk_w=None, device="cuda", fused_gather=False):
+                 topk_ids=None, topk_w=None, device="cuda", fused_gather=False, w_router=None,
+                 bias=None, bias_lr=0.0):
         import torch
         self.cfg = cfg
         self.fused_gather = fused_gather
@@ -61,9 +68,17 @@ class MoeLayer:
             self.topk_ids = topk_ids if isinstance(topk_ids, torch.Tensor) else to_device(topk_ids, dev)
             self.topk_w = topk_w if isinstance(topk_w, torch.Tensor) else to_device(topk_w, dev)
         else:
-            self.logits = logits if isinstance(logits, torch.Tensor) else to_device(logits, dev)
+            if w_router is not None:
+                self.logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+            else:
+                self.logits = logits if isinstance(logits, torch.Tensor) else to_device(logits, dev)
             self.topk_ids = torch.empty((T, k), dtype=i32, device=dev)
             self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.w_router = None if w_router is None else (
+            w_router if isinstance(w_router, torch.Tensor) else to_device(w_router, dev))
+        self.bias = None if bias is None else (
+            bias if isinstance(bias, torch.Tensor) else to_device(bias, dev))
+        self.bias_lr = float(bias_lr)
         self.send_counts = torch.empty((cfg.n_ep, cfg.n_ep), dtype=i32, device=dev) if cfg.n_ep else None
         self.counts = torch.empty(E, dtype=i32, device=dev)
         self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
@@ -84,11 +99,16 @@ class MoeLayer:
         else:
             self.y_sh = None
 
+    def router(self, stream=None):
+        """The router product logits = x w_router^T (a no-op without w_router)."""
+        if self.w_router is not None:
+            moe_router_logits(self.x, self.w_router, self.logits, stream=stream)
+
     def route(self, stream=None):
         c = self.cfg
         if c.gating != "given":
             moe_route_topk(self.logits, c.k, c.gating, c.renormalize, c.n_groups, c.topk_groups,
-                           self.topk_ids, self.topk_w, stream=stream)
+                           self.topk_ids, self.topk_w, stream=stream, bias=self.bias)
         if c.n_ep:
             moe_send_counts(self.topk_ids, c.E, c.n_ep, self.send_counts, stream=stream)
 
@@ -129,9 +149,17 @@ class MoeLayer:
     def combine(self, stream=None):
         moe_unpermute_combine(self.y_perm, self.inv, self.topk_w, self.y_sh, self.y, stream=stream)
 
+    def bias_update(self, stream=None):
+        """bias += bias_lr (mean load - load) from this batch's counts (a no-op
+        without a bias or with bias_lr = 0)."""
+        if self.bias is not None and self.bias_lr != 0.0:
+            moe_router_bias_update(self.counts, self.bias, self.bias_lr, stream=stream)
+
     def forward(self, stream=None):
+        self.router(stream)
         self.route(stream)
         self.permute(stream)
         self.experts(stream)
         self.combine(stream)
+        self.bias_update(stream)
         return self.y
