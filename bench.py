@@ -176,6 +176,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--router", action="store_true",
+                    help="put the router product (x . w_router^T) and the auxiliary-loss-free "
+                         "bias (selection on logits + bias, bias update after each step, rate "
+                         "--bias-lr) in the step; the default step takes the logits as input")
+    ap.add_argument("--bias-lr", type=float, default=1e-3)
     ap.add_argument("--path", choices=("gather", "packed"), default="gather",
                     help="gather: the first expert product reads token rows through the "
                          "permutation; packed: the permute writes the packed copy X[order]")
@@ -188,6 +193,7 @@ def main():
               "this build has no cross-GPU exchange. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     from token_routing_expert_amd import inputs, load_library
@@ -207,12 +213,19 @@ def main():
         logits = inputs.gen_logits(cfg)
         ids_in = w_in = None
     log(f"generated in {time.perf_counter() - t0:.1f} s; uploading")
-    layer = MoeLayer(cfg, x, w13, w2, logits=logits, sh_w13=sh[0], sh_w2=sh[1],
+    router = args.router and cfg.gating != "given"
+    wr_kw = {}
+    if router:
+        wr_kw = dict(w_router=inputs.gen_router_weights(cfg),
+                     bias=np.zeros(cfg.E, np.float32), bias_lr=args.bias_lr)
+    layer = MoeLayer(cfg, x, w13, w2, logits=logits, sh_w13=sh[0], sh_w2=sh[1], **wr_kw,
                      topk_ids=ids_in, topk_w=w_in, fused_gather=args.path == "gather")
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     stages = ["route", "permute", "gate_up", "down", "experts_shared", "combine"]
+    if router:
+        stages = ["router"] + stages + ["bias_update"]
 
     def step(evs=None):
         if evs is not None:
@@ -308,6 +321,7 @@ def main():
             "workload": cfg.name, "T": cfg.T, "E": cfg.E, "k": cfg.k, "d": cfg.d, "ffn": cfg.ffn,
             "gating": cfg.gating, "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups,
             "shared_experts": int(cfg.shared), "n_ep_simulated": cfg.n_ep, "path": args.path,
+            "router": bool(router), "bias_lr": args.bias_lr if router else None,
         },
         "roofline": {
             "kernel": ("moe_grouped_gate_up_gather" if gather else "moe_grouped_gate_up")
