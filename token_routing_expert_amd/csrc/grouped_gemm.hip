@@ -634,26 +634,22 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
-        // Memory phase.  First let the previous compute phase's MFMAs drain
-        // (they may still read the fragment registers the loads below
-        // overwrite): a use of every accumulator makes the compiler wait for
-        // the MFMA results.
-#pragma unroll
-        for (int i = 0; i < NL; ++i)
-#pragma unroll
-          for (int j = 0; j < NB; ++j) asm volatile("" ::"v"(acc[i][j][0]));
+        // Memory phase.  The weight fragments are read first: the compute
+        // phase's first MFMAs need them and one row fragment.  (The compiler
+        // orders these loads after the previous phase's MFMAs that read the
+        // same registers.)
         const u32x4 *As = a_ring + (kt % SA) * ASTAGE;
         const u32x4 *Bs = b_ring + (kt % SB) * BSTAGE;
         u32x4 fa[2][NLM], fb[2][NB];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int cc = 2 * (2 * h + q) + (lane >> 5);
+          fb[q][0] = Bs[swz_c<CPR>(brow0 + (lane & 31), cc)];
+          fb[q][1] = Bs[swz_c<CPR>(brow1 + (lane & 31), cc)];
 #pragma unroll
           for (int i = 0; i < NL; ++i)
             if (!DYN || i < live)
               fa[q][i] = As[swz_c<CPR>((GRP + 2 * (wm + WMG * i)) * 32 + (lane & 31), cc)];
-          fb[q][0] = Bs[swz_c<CPR>(brow0 + (lane & 31), cc)];
-          fb[q][1] = Bs[swz_c<CPR>(brow1 + (lane & 31), cc)];
         }
         if (h == 0) {
           if constexpr (GRP == 0) {
