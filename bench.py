@@ -275,6 +275,13 @@ def main():
     gather = args.path == "gather"
     b_perm, b_comb = stage_bytes(cfg, gather)
     b_gate_up = gate_up_bytes(cfg, counts, gather)
+    if layer.merge_shared:
+        # The shared expert runs as one more group of the routed launches.
+        f_gate_up += 2 * f_shared // 3
+        f_down += f_shared // 3
+        f_shared = 0
+        s_el = cfg.elem_bytes
+        b_gate_up += 2 * cfg.ffn * cfg.d * s_el + cfg.T * (cfg.d + cfg.ffn) * s_el + 4 * cfg.T
     stage_info = {}
     for name in stages:
         ms = stage_ms[name]
@@ -321,6 +328,7 @@ def main():
             "workload": cfg.name, "T": cfg.T, "E": cfg.E, "k": cfg.k, "d": cfg.d, "ffn": cfg.ffn,
             "gating": cfg.gating, "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups,
             "shared_experts": int(cfg.shared), "n_ep_simulated": cfg.n_ep, "path": args.path,
+            "shared_in_routed_launches": bool(layer.merge_shared),
             "router": bool(router), "bias_lr": args.bias_lr if router else None,
         },
         "roofline": {

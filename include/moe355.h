@@ -250,21 +250,23 @@ moe_status moe_grouped_down(const void *h, moe_dtype dt, int M, int ffn, int d,
  * moe_grouped_gate_up with the permute's row copy folded into the product's
  * loads ("Token permutation and grouped GEMMs": X[order] is only ever read by
  * the first expert product, so the rows can be gathered where they are
- * consumed).  Packed row p is token order[p] / k of x; the result is
- * bit-identical to moe_permute's x_perm followed by moe_grouped_gate_up.
+ * consumed).  Packed row p (p < M) is token order[p] / k of x; with M = T k
+ * and moe_permute's order the result is bit-identical to moe_permute's x_perm
+ * followed by moe_grouped_gate_up.  M may exceed T k: entries order[p] = t k
+ * past T k add token t again, e.g. as the rows of an always-active shared
+ * expert placed as one more group after the routed ones.
  *
  *   x        [T, d] activations in token order, dtype dt.
- *   k        assignments per token (M = T k packed rows).
- *   order    [M] int32 from moe_permute (its index-only mode suffices); every
- *            entry must lie in [0, M).
+ *   k        assignments per token (the divisor applied to order).
+ *   M        packed rows of the product; offsets[G] = M.
+ *   order    [M] int32, every entry in [0, T k).
  *   offsets, w13, h, G, d, ffn as in moe_grouped_gate_up.
- * Errors: those of moe_grouped_gate_up with M = T k, and INVALID_ARG for
- * k < 1 or a null order; UNSUPPORTED also for x of 4 GiB or more
- * (T d elem >= 2^32) or T k >= 2^31.  An order entry outside [0, M) is outside
- * the contract: the read it steers is bounded by x's extent, the row it
- * produces is undefined.
+ * Errors: those of moe_grouped_gate_up, and INVALID_ARG for k < 1 or a null
+ * order; UNSUPPORTED also for x of 4 GiB or more (T d elem >= 2^32).  An
+ * order entry outside [0, T k) is outside the contract: the read it steers is
+ * bounded by x's extent, the row it produces is undefined.
  */
-moe_status moe_grouped_gate_up_gather(const void *x, moe_dtype dt, int T, int k, int d,
+moe_status moe_grouped_gate_up_gather(const void *x, moe_dtype dt, int T, int k, int M, int d,
                                       int ffn, const int32_t *order, const int32_t *offsets,
                                       int G, const void *w13, void *h, hipStream_t stream);
 

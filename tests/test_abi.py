@@ -122,14 +122,14 @@ def test_grouped_halves_validation(lib):
 def test_gate_up_gather_validation(lib):
     f = lib.moe_grouped_gate_up_gather
     a = ctypes.c_void_p(16)
-    #       x  dt T  k  d    ffn  order off G  w13 h  stream
-    assert f(a, 1, 8, 0, 128, 256, a, a, 4, a, a, NULL) == INVALID          # k < 1
-    assert f(a, 1, 8, 2, 96, 256, a, a, 4, a, a, NULL) == UNSUPPORTED       # d % 128
-    assert f(a, 1, 8, 2, 128, 256, NULL, a, 4, a, a, NULL) == INVALID       # null order
-    assert f(a, 1, 8, 2, 128, 256, a, a, 4, a, ctypes.c_void_p(24), NULL) == INVALID
-    assert f(a, 1, 1 << 20, 2, 4096, 256, a, a, 4, a, a, NULL) == UNSUPPORTED  # x >= 4 GiB
-    assert f(a, 1, 1 << 30, 2, 128, 256, a, a, 4, a, a, NULL) == UNSUPPORTED   # T k >= 2^31
-    assert f(NULL, 1, 0, 2, 128, 256, NULL, NULL, 4, NULL, NULL, NULL) == 0  # T = 0: no-op
+    #       x  dt T  k  M   d    ffn  order off G  w13 h  stream
+    assert f(a, 1, 8, 0, 16, 128, 256, a, a, 4, a, a, NULL) == INVALID          # k < 1
+    assert f(a, 1, 8, 2, -1, 128, 256, a, a, 4, a, a, NULL) == INVALID          # M < 0
+    assert f(a, 1, 8, 2, 16, 96, 256, a, a, 4, a, a, NULL) == UNSUPPORTED       # d % 128
+    assert f(a, 1, 8, 2, 16, 128, 256, NULL, a, 4, a, a, NULL) == INVALID       # null order
+    assert f(a, 1, 8, 2, 16, 128, 256, a, a, 4, a, ctypes.c_void_p(24), NULL) == INVALID
+    assert f(a, 1, 1 << 20, 2, 16, 4096, 256, a, a, 4, a, a, NULL) == UNSUPPORTED  # x >= 4 GiB
+    assert f(NULL, 1, 8, 2, 0, 128, 256, NULL, NULL, 4, NULL, NULL, NULL) == 0    # M = 0: no-op
 
 
 def test_permute_index_only_validation(lib):

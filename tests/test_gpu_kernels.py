@@ -457,13 +457,47 @@ def test_gate_up_gather_matches_the_packed_rows(lib, case):
     rows_close(as_f64(host(h)[p]), h_or, 1e-4 if dt == "f32" else 2e-2)
 
 
+@pytest.mark.parametrize("T,k,E,d,ffn", [(100, 8, 32, 256, 256), (700, 2, 4, 256, 384)])
+def test_shared_expert_as_extra_group(lib, T, k, E, d, ffn):
+    """A shared expert appended as group E (order entries t k after the T k
+    routed rows) gives, row for row, the bits of the separate calls."""
+    cfg = inputs.MoeConfig("t", 7, T=T, E=E, k=k, d=d, ffn=ffn, dtype="bf16", gating="softmax",
+                           w_std=0.05)
+    r = np.random.default_rng(T + E)
+    ids = _ids("random", T, k, E, r)
+    x = dev(inputs.gen_x(cfg))
+    w13, w2 = (dev(w) for w in inputs.gen_expert_weights(cfg))
+    sh13, sh2 = (dev(w) for w in inputs.gen_expert_weights(cfg, shared=True))
+    _, offsets, order, _, _ = lib.moe_permute(x, dev(ids), E, rows=False)
+    M = T * k
+    order_all = torch.cat([order, torch.arange(T, dtype=torch.int32, device="cuda") * k])
+    offsets_all = torch.cat([offsets, torch.tensor([M + T], dtype=torch.int32, device="cuda")])
+    w13_all, w2_all = torch.cat([w13, sh13]), torch.cat([w2, sh2])
+    h_all = lib.moe_grouped_gate_up_gather(x, order_all, k, offsets_all, w13_all)
+    y_all = lib.moe_grouped_down(h_all, offsets_all, w2_all)
+    h_r = lib.moe_grouped_gate_up_gather(x, order, k, offsets, w13)
+    y_r = lib.moe_grouped_down(h_r, offsets, w2)
+    sh_off = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    y_s = lib.moe_grouped_swiglu(x, sh_off, sh13, sh2)
+    torch.cuda.synchronize()
+    got, ref_r, ref_s = host(y_all).view(np.uint16), host(y_r).view(np.uint16), host(y_s).view(np.uint16)
+    # routed rows: same family either way at these sizes -> same bits
+    assert np.array_equal(got[:M], ref_r)
+    # shared rows against the oracle (the separate call may use another tile family)
+    sh_ref = oracle.expert_swiglu_rows(inputs.gen_x(cfg), np.zeros(T, np.int32),
+                                       *inputs.gen_expert_weights(cfg, shared=True))
+    rows_close(as_f64(got[M:]), sh_ref, 2e-2)
+    rows_close(as_f64(ref_s), sh_ref, 2e-2)
+
+
 def test_gate_up_gather_errors(lib):
     x = torch.zeros((4, 128), dtype=torch.bfloat16, device="cuda")
     w13 = torch.zeros((1, 2, 128, 128), dtype=torch.bfloat16, device="cuda")
     off = torch.tensor([0, 8], dtype=torch.int32, device="cuda")
     order = torch.zeros(8, dtype=torch.int32, device="cuda")
-    with pytest.raises(lib.MoeError):
-        lib.moe_grouped_gate_up_gather(x, order[:7], 2, off, w13)   # order of the wrong size
+    with pytest.raises(lib.MoeError):   # weights of another d
+        lib.moe_grouped_gate_up_gather(x, order, 2, off,
+                                       torch.zeros((1, 2, 128, 256), dtype=torch.bfloat16, device="cuda"))
     h = lib.moe_grouped_gate_up_gather(x[:0], order[:0], 2, torch.zeros(2, dtype=torch.int32,
                                                                          device="cuda"), w13)
     torch.cuda.synchronize()

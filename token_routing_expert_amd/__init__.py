@@ -55,7 +55,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_permute.argtypes = [P, i32, i32, i32, P, i32, i32, P, P, P, P, P, P, sz, P]
     lib.moe_grouped_swiglu.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P, P, P]
     lib.moe_grouped_gate_up.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P]
-    lib.moe_grouped_gate_up_gather.argtypes = [P, i32, i32, i32, i32, i32, P, P, i32, P, P, P]
+    lib.moe_grouped_gate_up_gather.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, i32, P, P, P]
     lib.moe_grouped_down.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P]
     lib.moe_unpermute_combine.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P]
     for name in ("moe_route_topk", "moe_route_topk_biased", "moe_router_logits",
@@ -287,21 +287,22 @@ def moe_grouped_gate_up(a, offsets, w13, h=None, stream=None):
 def moe_grouped_gate_up_gather(x, order, k, offsets, w13, h=None, stream=None):
     """moe_grouped_gate_up on the rows x[order // k] without materialising them.
 
-    x [T, d] in token order, order [T k] from moe_permute; returns h [T k, ffn].
+    x [T, d] in token order, order [M] (moe_permute's order, M = T k, possibly
+    followed by entries t k that repeat token t); returns h [M, ffn].
     """
     torch = _torch()
     G = _expert_shapes("moe_grouped_gate_up_gather", x, offsets, w13=w13)
     _dev(order, "order", (torch.int32,))
     T, d = x.shape
-    M = T * k
+    M = order.numel()
     ffn = w13.shape[2]
-    if w13.shape[3] != d or order.numel() != M:
+    if w13.shape[3] != d:
         raise MoeError("moe_grouped_gate_up_gather: inconsistent shapes")
     h = torch.empty((M, ffn), dtype=x.dtype, device=x.device) if h is None else h
     _dev(h, "h", (x.dtype,))
     _check(load_library().moe_grouped_gate_up_gather(
-        _ptr(x), _dtype_code(x), T, k, d, ffn, _ptr(order), _ptr(offsets), G, _ptr(w13), _ptr(h),
-        _stream(stream)), "moe_grouped_gate_up_gather")
+        _ptr(x), _dtype_code(x), T, k, M, d, ffn, _ptr(order), _ptr(offsets), G, _ptr(w13),
+        _ptr(h), _stream(stream)), "moe_grouped_gate_up_gather")
     return h
 
 

@@ -941,13 +941,11 @@ extern "C" moe_status moe_grouped_gate_up(const void *a, moe_dtype dt, int M, in
   return launch_status();
 }
 
-extern "C" moe_status moe_grouped_gate_up_gather(const void *x, moe_dtype dt, int T, int k, int d,
-                                                 int ffn, const int32_t *order,
+extern "C" moe_status moe_grouped_gate_up_gather(const void *x, moe_dtype dt, int T, int k, int M,
+                                                 int d, int ffn, const int32_t *order,
                                                  const int32_t *offsets, int G, const void *w13,
                                                  void *h, hipStream_t stream) {
-  if (T < 0 || k < 1) return MOE_ERR_INVALID_ARG;
-  if ((int64_t)T * k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
-  const int M = T * k;
+  if (T < 0 || k < 1 || M < 0) return MOE_ERR_INVALID_ARG;
   const moe_status st = check_shape(dt, M, d, ffn, G);
   if (st != MOE_OK || M == 0) return st;
   // Byte offsets inside x are 32-bit in the kernels.

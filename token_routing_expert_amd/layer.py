@@ -25,6 +25,18 @@ def to_device(a: np.ndarray, device="cuda"):
     return torch.from_numpy(a).to(device)
 
 
+def _upload_into(dst, a):
+    """Copy a host array (or device tensor) into the device tensor dst."""
+    import torch
+    if isinstance(a, torch.Tensor):
+        dst.copy_(a)
+        return
+    a = np.ascontiguousarray(a)
+    src = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 \
+        else torch.from_numpy(a)
+    dst.copy_(src)
+
+
 def to_host(t) -> np.ndarray:
     """Device tensor to a host array; bf16 comes back as uint16 bit patterns."""
     import torch
@@ -41,6 +53,14 @@ class MoeLayer:
     indices only and the first expert product reads the token rows through
     order itself (moe_grouped_gate_up_gather).  Both paths give the same bits.
 
+    merge_shared puts the always-active shared expert into the routed launches
+    as group E (fused-gather path only): its T rows follow the T k packed rows,
+    gathered through order entries t k, and its matrices sit after the routed
+    experts' in one weight tensor each.  The outputs are the same bits either
+    way; at DeepSeek-V3 decode shape the step time is too (the shared expert's
+    88 MB stream costs the same inside the routed launches as in its own), so
+    the default is off.
+
     w_router [E, d] (optional) puts the router product in front of the route:
     each forward computes the logits from x.  bias [E] fp32 (optional)
     selects on logits + bias (auxiliary-loss-free balancing); with
@@ -50,19 +70,32 @@ class MoeLayer:
 
     def __init__(self, cfg: MoeConfig, x, w13, w2, logits=None, sh_w13=None, sh_w2=None,
                  topk_ids=None, topk_w=None, device="cuda", fused_gather=False, w_router=None,
-                 bias=None, bias_lr=0.0):
+                 bias=None, bias_lr=0.0, merge_shared=False):
         import torch
         self.cfg = cfg
         self.fused_gather = fused_gather
+        if merge_shared and not (fused_gather and cfg.shared):
+            raise ValueError("merge_shared needs the fused-gather path and a shared expert")
+        self.merge_shared = bool(merge_shared)
         dev = torch.device(device)
         self.device = dev
         self.x = x if isinstance(x, torch.Tensor) else to_device(x, dev)
-        self.w13 = w13 if isinstance(w13, torch.Tensor) else to_device(w13, dev)
-        self.w2 = w2 if isinstance(w2, torch.Tensor) else to_device(w2, dev)
         act = self.x.dtype
         T, k, E, d, ffn = cfg.T, cfg.k, cfg.E, cfg.d, cfg.ffn
         M = T * k
         i32 = torch.int32
+        if self.merge_shared:
+            # Routed experts 0 .. E-1, then the shared expert as group E.
+            self.w13_all = torch.empty((E + 1, 2, ffn, d), dtype=act, device=dev)
+            self.w2_all = torch.empty((E + 1, d, ffn), dtype=act, device=dev)
+            _upload_into(self.w13_all[:E], w13)
+            _upload_into(self.w2_all[:E], w2)
+            _upload_into(self.w13_all[E:], sh_w13)
+            _upload_into(self.w2_all[E:], sh_w2)
+            self.w13, self.w2 = self.w13_all[:E], self.w2_all[:E]
+        else:
+            self.w13 = w13 if isinstance(w13, torch.Tensor) else to_device(w13, dev)
+            self.w2 = w2 if isinstance(w2, torch.Tensor) else to_device(w2, dev)
         if cfg.gating == "given":
             self.logits = None
             self.topk_ids = topk_ids if isinstance(topk_ids, torch.Tensor) else to_device(topk_ids, dev)
@@ -81,16 +114,31 @@ class MoeLayer:
         self.bias_lr = float(bias_lr)
         self.send_counts = torch.empty((cfg.n_ep, cfg.n_ep), dtype=i32, device=dev) if cfg.n_ep else None
         self.counts = torch.empty(E, dtype=i32, device=dev)
-        self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
-        self.order = torch.empty(M, dtype=i32, device=dev)
         self.inv = torch.empty(M, dtype=i32, device=dev)
         self.x_perm = None if fused_gather else torch.empty((M, d), dtype=act, device=dev)
         self.workspace = torch.empty(max(16, moe_permute_workspace_bytes(T, k, E)), dtype=torch.uint8,
                                      device=dev)
-        self.h = torch.empty((M, ffn), dtype=act, device=dev)
-        self.y_perm = torch.empty((M, d), dtype=act, device=dev)
         self.y = torch.empty((T, d), dtype=act, device=dev)
-        if cfg.shared:
+        if self.merge_shared:
+            # The permute writes the first M (E + 1) entries; the shared group's
+            # entries are fixed: order[M + t] = t k, offsets[E + 1] = M + T.
+            R = M + T
+            self.order_all = torch.empty(R, dtype=i32, device=dev)
+            self.order_all[M:] = torch.arange(T, dtype=i32, device=dev) * k
+            self.offsets_all = torch.empty(E + 2, dtype=i32, device=dev)
+            self.offsets_all[E + 1] = R
+            self.order, self.offsets = self.order_all[:M], self.offsets_all[:E + 1]
+            self.h = torch.empty((R, ffn), dtype=act, device=dev)
+            self.y_perm_all = torch.empty((R, d), dtype=act, device=dev)
+            self.y_perm, self.y_sh = self.y_perm_all[:M], self.y_perm_all[M:]
+        else:
+            self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
+            self.order = torch.empty(M, dtype=i32, device=dev)
+            self.h = torch.empty((M, ffn), dtype=act, device=dev)
+            self.y_perm = torch.empty((M, d), dtype=act, device=dev)
+        if self.merge_shared:
+            self.sh_w13, self.sh_w2 = self.w13_all[E:], self.w2_all[E:]
+        elif cfg.shared:
             self.sh_w13 = sh_w13 if isinstance(sh_w13, torch.Tensor) else to_device(sh_w13, dev)
             self.sh_w2 = sh_w2 if isinstance(sh_w2, torch.Tensor) else to_device(sh_w2, dev)
             self.sh_offsets = torch.tensor([0, T], dtype=i32, device=dev)
@@ -127,7 +175,10 @@ class MoeLayer:
 
     def gate_up(self, stream=None):
         """The routed experts' first product alone (the same launch experts_routed makes)."""
-        if self.fused_gather:
+        if self.merge_shared:
+            moe_grouped_gate_up_gather(self.x, self.order_all, self.cfg.k, self.offsets_all,
+                                       self.w13_all, self.h, stream=stream)
+        elif self.fused_gather:
             moe_grouped_gate_up_gather(self.x, self.order, self.cfg.k, self.offsets, self.w13,
                                        self.h, stream=stream)
         else:
@@ -135,10 +186,15 @@ class MoeLayer:
 
     def down(self, stream=None):
         """The routed experts' second product alone."""
-        moe_grouped_down(self.h, self.offsets, self.w2, self.y_perm, stream=stream)
+        if self.merge_shared:
+            moe_grouped_down(self.h, self.offsets_all, self.w2_all, self.y_perm_all, stream=stream)
+        else:
+            moe_grouped_down(self.h, self.offsets, self.w2, self.y_perm, stream=stream)
 
     def experts_shared(self, stream=None):
-        if self.cfg.shared:
+        """The shared expert's own launches (with merge_shared its rows are
+        part of the routed launches and this does nothing)."""
+        if self.cfg.shared and not self.merge_shared:
             moe_grouped_swiglu(self.x, self.sh_offsets, self.sh_w13, self.sh_w2, self.sh_h,
                                self.y_sh, stream=stream)
 
