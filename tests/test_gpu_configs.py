@@ -154,6 +154,23 @@ def test_row_copy_path_is_bit_identical(case):
     assert np.array_equal(y.view(np.uint8), case.g["y"].view(np.uint8))
 
 
+def test_shared_in_routed_launches_is_bit_identical(case):
+    """With the shared expert as group E of the routed launches the layer
+    output keeps its bits."""
+    from token_routing_expert_amd.layer import MoeLayer, to_host
+    cfg, lay = case.cfg, case.layer
+    if not cfg.shared:
+        pytest.skip("no shared expert")
+    other = MoeLayer(cfg, lay.x, lay.w13, lay.w2, logits=lay.logits, sh_w13=lay.sh_w13,
+                     sh_w2=lay.sh_w2, fused_gather=True, merge_shared=True)
+    other.forward()
+    torch.cuda.synchronize()
+    y = to_host(other.y)
+    del other
+    torch.cuda.empty_cache()
+    assert np.array_equal(y.view(np.uint8), case.g["y"].view(np.uint8))
+
+
 def _host_rows(t, idx):
     from token_routing_expert_amd.layer import to_host
     return to_host(t[torch.as_tensor(idx, device=t.device)])
