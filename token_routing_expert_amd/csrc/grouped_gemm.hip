@@ -843,8 +843,10 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
 //          an expert's rows, each weight byte is read once and the
 //          workgroups of an XCD share the expert's rows through L2.  The
 //          wide weight tile halves how often the rows are re-read; 64-byte K
-//          slices let LDS hold 6 weight stages, 5 slices ahead.
-//   Large  (many rows per expert): ping-pong tiles of 256 rows.
+//          slices let LDS hold 4 row stages (2 slices ahead, so no memory
+//          phase has to drain its LDS reads) and 5 weight stages (4 ahead).
+//   Large  (many rows per expert): ping-pong tiles of 256 rows, 128-byte
+//          slices, 2 row stages (1 ahead) and 3 weight stages (2 ahead).
 #ifndef MOE_G1_SMALL
 #define MOE_G1_SMALL 32, 128, 1, 4, 2, 4
 #endif
