@@ -378,6 +378,9 @@ GEMM_CASES = [
     ("bf16", 512, 512, [250, 0, 321, 97, 640, 1]),
     ("bf16", 768, 640, [300, 40, 513]),
     ("bf16", 512, 1024, [1000]),
+    # many rows per expert and a long down reduction (ffn >= 8192): the down
+    # product switches to the medium tiles
+    ("bf16", 256, 8192, [600, 0, 345]),
 ]
 
 

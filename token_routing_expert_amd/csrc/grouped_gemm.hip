@@ -876,6 +876,7 @@ using G2Large = PpCfg<MOE_PP2_LARGE>;
 // of an expert MLP use the same family.  The ping-pong tiles are up to 128
 // columns of h and 256 columns of y wide.
 enum class Family { Small, Medium, Large };
+constexpr int kLongK = 8192;   // reduction length from which the down product uses medium tiles
 inline Family family_of(int M, int G, int d) {
   const int64_t per_expert = ((int64_t)M + G - 1) / G;
   if (per_expert < 96 || d % 256 != 0) return Family::Small;
@@ -901,7 +902,9 @@ void launch_down(Family f, const void *h, int M, int ffn, int d, const int32_t *
                  const void *w2, void *y, hipStream_t stream) {
   if (f == Family::Small)
     launch_one<BF16, false, G2Small>(h, M, ffn, d, offsets, G, w2, y, stream);
-  else if (f == Family::Medium)
+  else if (f == Family::Medium || ffn >= kLongK)
+    // A long K (wide experts) is better served by the medium tiles' deeper
+    // rings of 64-byte slices, also when there are many rows per expert.
     launch_one<BF16, false, G2Medium>(h, M, ffn, d, offsets, G, w2, y, stream);
   else
     launch_one<BF16, false, G2Large>(h, M, ffn, d, offsets, G, w2, y, stream);
