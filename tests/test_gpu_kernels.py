@@ -381,6 +381,11 @@ GEMM_CASES = [
     # many rows per expert and a long down reduction (ffn >= 8192): the down
     # product switches to the medium tiles
     ("bf16", 256, 8192, [600, 0, 345]),
+    # the family boundaries: 95 | 96 and 288 | 289 rows per expert on average
+    ("bf16", 256, 256, [95]),
+    ("bf16", 256, 256, [96]),
+    ("bf16", 256, 256, [288, 288]),
+    ("bf16", 256, 256, [289, 289]),
 ]
 
 
@@ -540,6 +545,8 @@ COMBINE_CASES = [
     (500, 1, 4, 128, "bf16", False),
     (77, 3, 5, 40, "f32", True),
     (64, 20, 30, 16, "bf16", False),
+    (300, 6, 16, 256, "f32", True),     # k below the kernel's slot count (8)
+    (50, 64, 64, 8, "bf16", True),      # the largest k
 ]
 
 
