@@ -577,3 +577,36 @@ def test_unpermute_of_permute_is_identity(lib):
     y = lib.moe_unpermute_combine(xp, inv, torch.ones((T, 1), dtype=torch.float32, device="cuda"))
     torch.cuda.synchronize()
     assert np.array_equal(host(y), x)
+
+
+# --------------------------------------------------------------------------
+# Graph capture: the library allocates nothing and sets no memory with
+# memset, so a whole layer forward can be captured and replayed.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fused_gather", [True, False])
+def test_layer_forward_graph_replays_bitwise(lib, fused_gather):
+    from token_routing_expert_amd.layer import MoeLayer
+    cfg = inputs.CONFIGS["small_fp32"]
+    w13, w2 = inputs.gen_expert_weights(cfg)
+    L = MoeLayer(cfg, inputs.gen_x(cfg), w13, w2, logits=inputs.gen_logits(cfg),
+                 fused_gather=fused_gather)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        L.forward()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = L.y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.forward()
+    for i in range(3):
+        L.y.zero_()                  # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(L.y, ref), i
+    L.forward()                      # and eager use after them
+    torch.cuda.synchronize()
+    assert torch.equal(L.y, ref)
