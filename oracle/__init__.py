@@ -1,4 +1,4 @@
-"""CPU oracle for the MoE forward path -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the MoE layer (forward and backward) -- TEST INFRASTRUCTURE ONLY.
 
 The product (the HIP library and its Python binding) never imports this
 package.  Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline
@@ -63,6 +63,11 @@ def _load():
     lib.orc_router_logits.argtypes = [P, i32, i64, i32, P, i32, P]
     lib.orc_bias_update.argtypes = [P, i32, ctypes.c_float, P]
     lib.orc_bias_update.restype = i32
+    lib.orc_combine_backward.argtypes = [P, i32, i64, i32, i32, P, P, P, i32, P, P]
+    lib.orc_expert_swiglu_backward_rows.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, P, P, P, P]
+    lib.orc_gate_backward.argtypes = [P, i32, i32, i32, P, i32, i32, P, P]
+    lib.orc_gate_backward.restype = i32
+    lib.orc_router_backward.argtypes = [P, i32, i64, i32, P, i32, P, P, P]
     lib.orc_num_threads.restype = i32
     _lib = lib
     return lib
@@ -242,3 +247,129 @@ def layer_tokens(x, ids, w, w13, w2, tokens, sh_w13=None, sh_w2=None):
         y_sh = expert_swiglu_rows(xs, np.zeros(len(tokens), np.int32), sh_w13, sh_w2)
     inv = np.arange(len(tokens) * k, dtype=np.int32)
     return combine(y_rows, inv, w[tokens], y_sh)
+
+
+# --------------------------------------------------------------------------
+# Backward pass (oracle.c, functions B0..B5): the chain rule applied to the
+# forward definition; "Expert parallelism", section "How many bytes move",
+# gives its shape (the combine's gradient is dispatched, the dispatch's
+# gradient combined).
+# --------------------------------------------------------------------------
+
+def combine_backward(dy: np.ndarray, inv: np.ndarray, w: np.ndarray, y_perm: np.ndarray):
+    """B5: dy_perm [T k, d] (row inv[t k + j] = w[t,j] dy[t]) and dw [T,k]
+    (dw[t,j] = dy[t] . y_perm[inv[t k + j]]), fp64 (oracle.c)."""
+    dy = _c(dy)
+    y_perm = _c(y_perm)
+    w = _c(w, np.float32)
+    T, k = w.shape
+    d = dy.shape[1]
+    inv = _c(inv, np.int32).reshape(-1)
+    assert inv.size == T * k and dy.shape == (T, d) and y_perm.shape[1] == d
+    dy_perm = np.empty((T * k, d), np.float64)
+    dw = np.empty((T, k), np.float64)
+    _load().orc_combine_backward(_ptr(dy), _dtype_code(dy), T, k, d, _ptr(inv), _ptr(w),
+                                 _ptr(y_perm), _dtype_code(y_perm), _ptr(dy_perm), _ptr(dw))
+    return dy_perm, dw
+
+
+def expert_swiglu_backward_rows(xrows: np.ndarray, expert_of_row: np.ndarray, w13: np.ndarray,
+                                w2: np.ndarray, dyrows: np.ndarray, want_dx: bool = True,
+                                want_dw: bool = True):
+    """B4: (dx [R,d], dw13 [G,2,ffn,d], dw2 [G,d,ffn]) in fp64 for rows x_r of
+    experts expert_of_row[r] with output gradients dyrows (oracle.c).  An
+    output not asked for is None."""
+    xrows = _c(xrows)
+    w13 = _c(w13)
+    w2 = _c(w2)
+    dt = _dtype_code(xrows)
+    if _dtype_code(w13) != dt or _dtype_code(w2) != dt:
+        raise TypeError("rows and weights must share a dtype")
+    R, d = xrows.shape
+    G, two, ffn, d2 = w13.shape
+    assert two == 2 and d2 == d and w2.shape == (G, d, ffn)
+    e = _c(expert_of_row, np.int32).reshape(-1)
+    assert e.size == R and (R == 0 or (e.min() >= 0 and e.max() < G))
+    dyrows = _c(dyrows, np.float64)
+    assert dyrows.shape == (R, d)
+    dx = np.empty((R, d), np.float64) if want_dx else None
+    dw13 = np.empty((G, 2, ffn, d), np.float64) if want_dw else None
+    dw2 = np.empty((G, d, ffn), np.float64) if want_dw else None
+    _load().orc_expert_swiglu_backward_rows(
+        _ptr(xrows), dt, R, d, ffn, _ptr(e), G, _ptr(w13), _ptr(w2), _ptr(dyrows),
+        None if dx is None else _ptr(dx), None if dw13 is None else _ptr(dw13),
+        None if dw2 is None else _ptr(dw2))
+    return dx, dw13, dw2
+
+
+def gate_backward(logits: np.ndarray, ids: np.ndarray, dw: np.ndarray, gating: str = "softmax",
+                  renormalize: int = 1) -> np.ndarray:
+    """B1: dlogits [T,E] fp64 from the gate gradients dw [T,k] (oracle.c)."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    ids = _c(ids, np.int32)
+    k = ids.shape[1]
+    dw = _c(dw, np.float64)
+    assert ids.shape == (T, k) and dw.shape == (T, k)
+    out = np.empty((T, E), np.float64)
+    g = SOFTMAX if gating == "softmax" else SIGMOID
+    if _load().orc_gate_backward(_ptr(logits), T, E, k, _ptr(ids), g, int(renormalize), _ptr(dw),
+                                 _ptr(out)) != 0:
+        raise ValueError("orc_gate_backward: arguments outside the contract")
+    return out
+
+
+def router_backward(x: np.ndarray, wg: np.ndarray, dlogits: np.ndarray, want_dx: bool = True,
+                    want_dwg: bool = True):
+    """B0: dx = dlogits wg [T,d] and dwg = dlogits^T x [E,d], fp64 (oracle.c)."""
+    x = _c(x)
+    wg = _c(wg)
+    if x.dtype != wg.dtype:
+        raise TypeError("x and wg must share a dtype")
+    T, d = x.shape
+    E = wg.shape[0]
+    dl = _c(dlogits, np.float64)
+    assert dl.shape == (T, E) and wg.shape == (E, d)
+    dx = np.empty((T, d), np.float64) if want_dx else None
+    dwg = np.empty((E, d), np.float64) if want_dwg else None
+    _load().orc_router_backward(_ptr(x), _dtype_code(x), T, d, _ptr(wg), E, _ptr(dl),
+                                None if dx is None else _ptr(dx), None if dwg is None else _ptr(dwg))
+    return dx, dwg
+
+
+def layer_backward(x, logits, ids, w, w13, w2, dy, gating="softmax", renormalize=1,
+                   sh_w13=None, sh_w2=None, wg=None):
+    """The whole layer's backward for all T tokens, composed from B0..B5 in
+    the reverse order of the forward steps.  ids, w are the forward's route
+    (logits may be None when the gates were given).  Returns a dict of fp64
+    gradients: dx [T,d], dw13, dw2, dgate [T,k], and when present dlogits
+    [T,E], dsh_w13, dsh_w2, dwg [E,d]."""
+    T, k = ids.shape
+    d = x.shape[1]
+    xs = _c(x)
+    rows = np.repeat(xs, k, axis=0)                        # row a = t k + j holds x[t]
+    expert = _c(ids, np.int32).reshape(-1)
+    y_rows = expert_swiglu_rows(rows, expert, w13, w2)    # the forward's y_perm, token-major
+    ident = np.arange(T * k, dtype=np.int32)
+    dy_rows, dgate = combine_backward(dy, ident, w, y_rows)
+    dx_rows, dw13, dw2 = expert_swiglu_backward_rows(rows, expert, w13, w2, dy_rows)
+    dx = dx_rows.reshape(T, k, d).sum(axis=1)              # the permute's gradient: a token's rows summed
+    out = {"dw13": dw13, "dw2": dw2, "dgate": dgate}
+    if sh_w13 is not None:
+        dx_sh, out["dsh_w13"], out["dsh_w2"] = expert_swiglu_backward_rows(
+            xs, np.zeros(T, np.int32), sh_w13, sh_w2, _c(dy).astype(np.float64)
+            if _dtype_code(_c(dy)) != BF16 else bf16_bits_to_f64(dy))
+        dx = dx + dx_sh
+    if logits is not None:
+        out["dlogits"] = gate_backward(logits, ids, dgate, gating, renormalize)
+        if wg is not None:
+            dxr, out["dwg"] = router_backward(xs, wg, out["dlogits"])
+            dx = dx + dxr
+    out["dx"] = dx
+    return out
+
+
+def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) widened exactly to fp64."""
+    a = np.ascontiguousarray(a, np.uint16)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

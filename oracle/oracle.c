@@ -1,5 +1,6 @@
 /*
- * CPU oracle for one GPU's share of an expert-parallel MoE forward pass.
+ * CPU oracle for one GPU's share of an expert-parallel MoE layer: forward
+ * pass and its backward.
  *
  * TEST INFRASTRUCTURE ONLY.  This file is what the HIP path is checked
  * against; it is never part of the product.  Only the tests, the smoke
@@ -383,6 +384,217 @@ int orc_bias_update(const int32_t *counts, int E, float lr, float *bias)
         bias[e] = bias[e] + step;
     }
     return 0;
+}
+
+/* ========================================================================
+ * Backward pass.
+ *
+ * The pages give the backward's shape, not its formulas: it runs the
+ * forward's steps in reverse, the gradient of the combine going out the way
+ * the dispatch did and the gradient of the dispatch coming back the way the
+ * combine did ("Expert parallelism", section "How many bytes move"), and it
+ * costs twice the forward's products, 12 d d_e per assignment (section "A
+ * worked example at DeepSeek-V3's shape").  What it computes is fixed by the
+ * forward definition and the chain rule; each function below is that
+ * derivative written out, in fp64.  dy is the gradient of the loss at the
+ * layer output y.
+ * ====================================================================== */
+
+/* ------------------------------------------------------------------------
+ * B5  Backward of O5 (unpermute and weight).  From
+ *   y[t] = sum_j w[t,j] y_perm[inv[t k + j]]  (+ y_sh[t]):
+ *   dy_perm[inv[t k + j]] = w[t,j] dy[t]          (the combine's gradient,
+ *                                                   dispatched to the rows)
+ *   dw[t,j]               = sum_m dy[t,m] y_perm[inv[t k + j], m]
+ *   (dy_sh[t] = dy[t], not written here.)
+ * dy_perm is [T k, d] indexed by packed position; dw is [T, k].
+ * ---------------------------------------------------------------------- */
+void orc_combine_backward(const void *dy, int dy_dt, int64_t T, int k, int d, const int32_t *inv,
+                          const float *w, const void *y_perm, int yp_dt, double *dy_perm,
+                          double *dw)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            const int64_t p = inv[t * k + j];
+            const double g = (double)w[t * k + j];
+            double acc = 0.0;
+            for (int m = 0; m < d; ++m) {
+                const double v = widen(dy, dy_dt, t * d + m);
+                dy_perm[p * d + m] = g * v;
+                acc += v * widen(y_perm, yp_dt, p * d + m);
+            }
+            dw[t * k + j] = acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * B4  Backward of O4 (one expert's SwiGLU MLP) for a set of rows.  Forward,
+ * per row x of expert e:  g = W_gate x,  u = W_up x,  h = SiLU(g) u,
+ * y = W_down h.  With dy the gradient at y:
+ *   dh      = W_down^T dy
+ *   dg      = dh u SiLU'(g),   SiLU'(z) = s(z) (1 + z (1 - s(z))),  s = 1/(1+e^-z)
+ *   du      = dh SiLU(g)
+ *   dx      = W_gate^T dg + W_up^T du
+ *   dW_down += dy h^T,   dW_gate += dg x^T,   dW_up += du x^T
+ * The forward is recomputed from x in fp64.  Weight gradients are summed
+ * over each expert's rows in increasing row order; dx, dw13 and dw2 may each
+ * be NULL.  dw13 is [G, 2, ffn, d] and dw2 [G, d, ffn], both overwritten.
+ * ---------------------------------------------------------------------- */
+void orc_expert_swiglu_backward_rows(const void *xrows, int dtype, int64_t R, int d, int ffn,
+                                     const int32_t *expert_of_row, int G, const void *w13,
+                                     const void *w2, const double *dyrows, double *dx,
+                                     double *dw13, double *dw2)
+{
+    if (dw13) memset(dw13, 0, sizeof(double) * (size_t)G * 2 * ffn * d);
+    if (dw2) memset(dw2, 0, sizeof(double) * (size_t)G * d * ffn);
+#pragma omp parallel
+    {
+        double *xv = malloc(sizeof(double) * (size_t)d);
+        double *g = malloc(sizeof(double) * (size_t)ffn);
+        double *u = malloc(sizeof(double) * (size_t)ffn);
+        double *dg = malloc(sizeof(double) * (size_t)ffn);
+        double *du = malloc(sizeof(double) * (size_t)ffn);
+        double *h = malloc(sizeof(double) * (size_t)ffn);
+#pragma omp for schedule(dynamic, 1)
+        for (int e = 0; e < G; ++e) {
+            const int64_t gate0 = (int64_t)e * 2 * ffn * d, up0 = gate0 + (int64_t)ffn * d;
+            const int64_t down0 = (int64_t)e * d * ffn;
+            for (int64_t r = 0; r < R; ++r) {
+                if (expert_of_row[r] != e) continue;
+                const double *dyv = dyrows + r * d;
+                for (int i = 0; i < d; ++i) xv[i] = widen(xrows, dtype, r * d + i);
+                for (int n = 0; n < ffn; ++n) {
+                    double a = 0.0, b = 0.0;
+                    for (int i = 0; i < d; ++i) {
+                        a += widen(w13, dtype, gate0 + (int64_t)n * d + i) * xv[i];
+                        b += widen(w13, dtype, up0 + (int64_t)n * d + i) * xv[i];
+                    }
+                    g[n] = a;
+                    u[n] = b;
+                }
+                for (int n = 0; n < ffn; ++n) {
+                    double dh = 0.0;
+                    for (int m = 0; m < d; ++m)
+                        dh += widen(w2, dtype, down0 + (int64_t)m * ffn + n) * dyv[m];
+                    const double s = 1.0 / (1.0 + exp(-g[n]));
+                    const double silu = g[n] * s;
+                    const double dsilu = s * (1.0 + g[n] * (1.0 - s));
+                    h[n] = silu * u[n];
+                    dg[n] = dh * u[n] * dsilu;
+                    du[n] = dh * silu;
+                }
+                if (dx) {
+                    for (int i = 0; i < d; ++i) {
+                        double acc = 0.0;
+                        for (int n = 0; n < ffn; ++n)
+                            acc += widen(w13, dtype, gate0 + (int64_t)n * d + i) * dg[n] +
+                                   widen(w13, dtype, up0 + (int64_t)n * d + i) * du[n];
+                        dx[r * d + i] = acc;
+                    }
+                }
+                if (dw2)
+                    for (int m = 0; m < d; ++m)
+                        for (int n = 0; n < ffn; ++n) dw2[down0 + (int64_t)m * ffn + n] += dyv[m] * h[n];
+                if (dw13)
+                    for (int n = 0; n < ffn; ++n)
+                        for (int i = 0; i < d; ++i) {
+                            dw13[gate0 + (int64_t)n * d + i] += dg[n] * xv[i];
+                            dw13[up0 + (int64_t)n * d + i] += du[n] * xv[i];
+                        }
+            }
+        }
+        free(xv); free(g); free(u); free(dg); free(du); free(h);
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * B1  Backward of the gates (O1, the gate formulas).  The choice of experts
+ * is piecewise constant in the logits and the bias of auxiliary-loss-free
+ * balancing is outside the gradient ("05 - Expert Parallelism (MoE)",
+ * section "Load balancing", family (b)), so the gradient reaches the logits
+ * through the gate formulas only.  With c_j the chosen experts and dw the
+ * gradient at the gates:
+ *   softmax, renormalised:  p_j = w_j;  dl[c_j] = p_j (dw_j - sum_i p_i dw_i)
+ *   softmax, not renorm.:   P = softmax over all E;
+ *                           dl[e] = P_e ([e = c_j] dw_j - sum_i P_{c_i} dw_i)
+ *   sigmoid, renormalised:  s_j = s(l_{c_j}), S = sum s_j, w_j = s_j / S;
+ *                           dl[c_j] = s_j (1 - s_j) (dw_j - sum_i w_i dw_i) / S
+ *   sigmoid, not renorm.:   dl[c_j] = s_j (1 - s_j) dw_j
+ * All other entries are 0.  dlogits is [T, E], overwritten.
+ * Returns 0, or -1 on arguments outside the contract.
+ * ---------------------------------------------------------------------- */
+int orc_gate_backward(const float *logits, int T, int E, int k, const int32_t *ids, int gating,
+                      int renorm, const double *dw, double *dlogits)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E || k > 64) return -1;
+#pragma omp parallel
+    {
+        double *P = malloc(sizeof(double) * (size_t)E);
+#pragma omp for schedule(static)
+        for (int t = 0; t < T; ++t) {
+            const float *l = logits + (int64_t)t * E;
+            const int32_t *c = ids + (int64_t)t * k;
+            const double *g = dw + (int64_t)t * k;
+            double *out = dlogits + (int64_t)t * E;
+            for (int e = 0; e < E; ++e) out[e] = 0.0;
+            double v[64], sum = 0.0, dot = 0.0;
+            if (gating == ORC_SOFTMAX && renorm) {
+                const double l0 = (double)l[c[0]];
+                for (int j = 0; j < k; ++j) { v[j] = exp((double)l[c[j]] - l0); sum += v[j]; }
+                for (int j = 0; j < k; ++j) { v[j] /= sum; dot += v[j] * g[j]; }
+                for (int j = 0; j < k; ++j) out[c[j]] = v[j] * (g[j] - dot);
+            } else if (gating == ORC_SOFTMAX) {
+                double m = (double)l[0];
+                for (int e = 1; e < E; ++e) if ((double)l[e] > m) m = (double)l[e];
+                for (int e = 0; e < E; ++e) { P[e] = exp((double)l[e] - m); sum += P[e]; }
+                for (int e = 0; e < E; ++e) P[e] /= sum;
+                for (int j = 0; j < k; ++j) dot += P[c[j]] * g[j];
+                for (int e = 0; e < E; ++e) out[e] = -P[e] * dot;
+                for (int j = 0; j < k; ++j) out[c[j]] += P[c[j]] * g[j];
+            } else {
+                for (int j = 0; j < k; ++j) { v[j] = 1.0 / (1.0 + exp(-(double)l[c[j]])); sum += v[j]; }
+                if (renorm) {
+                    for (int j = 0; j < k; ++j) dot += v[j] / sum * g[j];
+                    for (int j = 0; j < k; ++j) out[c[j]] = v[j] * (1.0 - v[j]) * (g[j] - dot) / sum;
+                } else {
+                    for (int j = 0; j < k; ++j) out[c[j]] = v[j] * (1.0 - v[j]) * g[j];
+                }
+            }
+        }
+        free(P);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * B0  Backward of the router product O0, logits = x wg^T:
+ *   dx[t][i]  = sum_e dlogits[t][e] wg[e][i]
+ *   dwg[e][i] = sum_t dlogits[t][e] x[t][i]
+ * Either output may be NULL.
+ * ---------------------------------------------------------------------- */
+void orc_router_backward(const void *x, int dtype, int64_t T, int d, const void *wg, int E,
+                         const double *dlogits, double *dx, double *dwg)
+{
+    if (dx) {
+#pragma omp parallel for schedule(static)
+        for (int64_t t = 0; t < T; ++t)
+            for (int i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int e = 0; e < E; ++e) acc += dlogits[t * E + e] * widen(wg, dtype, (int64_t)e * d + i);
+                dx[t * d + i] = acc;
+            }
+    }
+    if (dwg) {
+#pragma omp parallel for schedule(static)
+        for (int e = 0; e < E; ++e)
+            for (int i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int64_t t = 0; t < T; ++t) acc += dlogits[t * E + e] * widen(x, dtype, t * d + i);
+                dwg[(int64_t)e * d + i] = acc;
+            }
+    }
 }
 
 /* Number of OpenMP threads the oracle's parallel loops use. */
