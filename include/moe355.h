@@ -279,7 +279,8 @@ moe_status moe_grouped_gate_up_gather(const void *x, moe_dtype dt, int T, int k,
  *   y_perm    [T k, d] expert outputs in packed (expert) order, dtype dt.
  *   inv       [T k] int32 from moe_permute.  Entries outside [0, T k) are
  *             skipped (contribute nothing).
- *   topk_w    [T, k] fp32 gates.
+ *   topk_w    [T, k] fp32 gates, or NULL: every gate 1 (the sum of a
+ *             token's k rows, which is the permute's backward).
  *   y_shared  [T, d] dtype dt, or NULL for none.
  *   y         [T, d] out, dtype dt.
  * Errors: INVALID_ARG for null required pointers, T < 0, k < 1, misalignment;
@@ -288,6 +289,104 @@ moe_status moe_grouped_gate_up_gather(const void *x, moe_dtype dt, int T, int k,
 moe_status moe_unpermute_combine(const void *y_perm, moe_dtype dt, int T, int k, int d,
                                  const int32_t *inv, const float *topk_w, const void *y_shared,
                                  void *y, hipStream_t stream);
+
+/* ========================================================================
+ * Training: the forward product that keeps what the backward needs, and the
+ * backward pass.  The backward runs the forward's steps in reverse: the
+ * combine's gradient goes out to the expert rows as the dispatch did, and
+ * the dispatch's gradient is combined back into the tokens ("Expert
+ * parallelism", section "How many bytes move"); its products cost twice the
+ * forward's, 12 d ffn FLOPs per assignment (section "A worked example at
+ * DeepSeek-V3's shape").  All values are the chain rule applied to the
+ * forward's definitions.
+ * ====================================================================== */
+
+/*
+ * moe_grouped_gate_up / moe_grouped_gate_up_gather that also stores the
+ * pre-activations: gu [M, 2 ffn] row p = (W_gate,e x_p, W_up,e x_p) in the
+ * dtype of x (gate columns 0 .. ffn-1, then up columns), besides h.
+ * order == NULL: x is the packed rows [M, d] (T and k unused); otherwise row
+ * p is x[order[p] / k] as in moe_grouped_gate_up_gather.  Errors as the
+ * calls it extends, plus a NULL or misaligned gu.
+ */
+moe_status moe_grouped_gate_up_save(const void *x, moe_dtype dt, int T, int k, int M, int d,
+                                    int ffn, const int32_t *order, const int32_t *offsets, int G,
+                                    const void *w13, void *h, void *gu, hipStream_t stream);
+
+/*
+ * Backward of moe_unpermute_combine: for each token t and slot j, with
+ * p = inv[t k + j],
+ *     dy_perm[p]  = topk_w[t,j] dy[t]                (dtype of dy, [T k, d])
+ *     dgate[t,j]  = sum_m dy[t,m] y_perm[p,m]         (fp32, [T, k])
+ *     dy_shared[t] = dy[t]                            (optional copy, [T, d])
+ * dgate and y_perm are both given or both NULL (no gate gradient).  The dot
+ * products sum in a fixed order, so results are deterministic.  Errors:
+ * INVALID_ARG for a NULL dy / inv / topk_w / dy_perm, one of dgate and
+ * y_perm without the other, misaligned rows, T < 0, k < 1, d < 1;
+ * UNSUPPORTED for d not a multiple of 8, k > 64 or T k >= 2^31.
+ */
+moe_status moe_combine_backward(const void *dy, moe_dtype dt, int T, int k, int d,
+                                const int32_t *inv, const float *topk_w, const void *y_perm,
+                                void *dy_perm, float *dgate, void *dy_shared, hipStream_t stream);
+
+/*
+ * Backward of the gates of moe_route_topk (the gate formulas of O1; the
+ * choice is piecewise constant and a balancing bias is outside the
+ * gradient, "05 - Expert Parallelism (MoE)", section "Load balancing"):
+ * dlogits [T, E] fp32 from dgate [T, k], the route's topk_ids and topk_w and
+ * the logits.  With dot = sum_j w_j dgate_j:
+ *   softmax, renormalised:  dl[c_j] = w_j (dgate_j - dot)
+ *   softmax, not renorm.:   dl[e] = P_e ([e = c_j] dgate_j - dot), P = softmax(l)
+ *   sigmoid, renormalised:  dl[c_j] = s_j (1 - s_j) (dgate_j - dot) / sum_i s_i
+ *   sigmoid, not renorm.:   dl[c_j] = s_j (1 - s_j) dgate_j,  s_j = 1/(1+e^-l_j)
+ * every other entry 0.  Errors: INVALID_ARG for NULL pointers, T < 0,
+ * k < 1, k > E, an unknown gating; UNSUPPORTED for k > 64 or E > 4096.
+ */
+moe_status moe_gate_backward(const float *logits, const int32_t *topk_ids, const float *topk_w,
+                             const float *dgate, int T, int E, int k, moe_gating gating,
+                             int renormalize, float *dlogits, hipStream_t stream);
+
+/*
+ * Backward of the second expert product and of SwiGLU, per expert segment
+ * (offsets as in moe_grouped_swiglu): dh = dy_perm W_down,e ([M, d] x
+ * [d, ffn], W_down,e = w2[e] row-major), then with (g, u) = gu[p] the
+ * forward's pre-activations (moe_grouped_gate_up_save),
+ *     dgu[p] = (dh u SiLU'(g), dh SiLU(g)),   SiLU'(g) = s (1 + g (1 - s)),
+ * s = 1/(1+e^-g); dgu [M, 2 ffn], gate columns then up columns.
+ * bf16 only (fp32 accumulation, RNE output).  Errors: INVALID_ARG for NULL
+ * or misaligned pointers, M < 0, G < 1; UNSUPPORTED for fp32, d or ffn not
+ * a multiple of 128, G > 4096, or operands of 4 GiB or more.
+ */
+moe_status moe_grouped_down_backward(const void *dy_perm, moe_dtype dt, int M, int d, int ffn,
+                                     const int32_t *offsets, int G, const void *w2,
+                                     const void *gu, void *dgu, hipStream_t stream);
+
+/*
+ * Backward of the first expert product to its rows: dx_perm [M, d] =
+ * dgu [M, 2 ffn] W13,e per segment, with W13,e = w13[e] read as [2 ffn, d]
+ * (gate rows then up rows).  The token gradient is then
+ * moe_unpermute_combine(dx_perm, inv, NULL gates) (+ the shared expert's).
+ * bf16 only; errors as moe_grouped_down_backward.
+ */
+moe_status moe_grouped_gate_up_backward(const void *dgu, moe_dtype dt, int M, int d, int ffn,
+                                        const int32_t *offsets, int G, const void *w13,
+                                        void *dx_perm, hipStream_t stream);
+
+/*
+ * Weight gradients: for each expert segment e = [offsets[e], offsets[e+1]),
+ *     c[e] = a[seg]^T b[rows of seg]        c [G, m_dim, n_dim], a [M, m_dim]
+ * where row p of b is b[b_order[p] / b_k] (b has b_rows rows), or b[p] when
+ * b_order is NULL (then b has M rows).  An empty segment gives zeros.  Uses:
+ * dW_down = weight_grad(dy_perm, h), dW13 = weight_grad(dgu, x, order, k)
+ * (the second is [G, 2 ffn, d] = w13's layout).  bf16 only.  Errors:
+ * INVALID_ARG for NULL or misaligned pointers, M < 0, G < 1, b_k < 1;
+ * UNSUPPORTED for fp32, m_dim or n_dim not a multiple of 128, G > 4096, or
+ * operands of 4 GiB or more.
+ */
+moe_status moe_grouped_weight_grad(const void *a, const void *b, moe_dtype dt, int M, int m_dim,
+                                   int n_dim, const int32_t *offsets, int G,
+                                   const int32_t *b_order, int b_k, int b_rows, void *c,
+                                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -64,7 +64,11 @@ def _load():
     lib.orc_bias_update.argtypes = [P, i32, ctypes.c_float, P]
     lib.orc_bias_update.restype = i32
     lib.orc_combine_backward.argtypes = [P, i32, i64, i32, i32, P, P, P, i32, P, P]
-    lib.orc_expert_swiglu_backward_rows.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, P, P, P, P]
+    lib.orc_expert_swiglu_backward_rows.argtypes = [P, i32, i64, i32, i32, P, i32, P, P, P, P, P,
+                                                    P, P, P]
+    lib.orc_down_backward_rows.argtypes = [P, i64, i32, i32, P, P, i32, P, P]
+    lib.orc_gate_up_backward_rows.argtypes = [P, i64, i32, i32, P, P, i32, P]
+    lib.orc_weight_grad.argtypes = [P, i64, i32, P, i32, P, i32, P, i32, P]
     lib.orc_gate_backward.argtypes = [P, i32, i32, i32, P, i32, i32, P, P]
     lib.orc_gate_backward.restype = i32
     lib.orc_router_backward.argtypes = [P, i32, i64, i32, P, i32, P, P, P]
@@ -275,10 +279,11 @@ def combine_backward(dy: np.ndarray, inv: np.ndarray, w: np.ndarray, y_perm: np.
 
 def expert_swiglu_backward_rows(xrows: np.ndarray, expert_of_row: np.ndarray, w13: np.ndarray,
                                 w2: np.ndarray, dyrows: np.ndarray, want_dx: bool = True,
-                                want_dw: bool = True):
+                                want_dw: bool = True, want_act: bool = False):
     """B4: (dx [R,d], dw13 [G,2,ffn,d], dw2 [G,d,ffn]) in fp64 for rows x_r of
-    experts expert_of_row[r] with output gradients dyrows (oracle.c).  An
-    output not asked for is None."""
+    experts expert_of_row[r] with output gradients dyrows (oracle.c).  With
+    want_act also (gu, dgu), each [R, 2 ffn]: the pre-activations (g, u) and
+    their gradients (dg, du).  An output not asked for is None."""
     xrows = _c(xrows)
     w13 = _c(w13)
     w2 = _c(w2)
@@ -295,11 +300,65 @@ def expert_swiglu_backward_rows(xrows: np.ndarray, expert_of_row: np.ndarray, w1
     dx = np.empty((R, d), np.float64) if want_dx else None
     dw13 = np.empty((G, 2, ffn, d), np.float64) if want_dw else None
     dw2 = np.empty((G, d, ffn), np.float64) if want_dw else None
+    gu = np.empty((R, 2 * ffn), np.float64) if want_act else None
+    dgu = np.empty((R, 2 * ffn), np.float64) if want_act else None
+    opt = lambda a: None if a is None else _ptr(a)
     _load().orc_expert_swiglu_backward_rows(
-        _ptr(xrows), dt, R, d, ffn, _ptr(e), G, _ptr(w13), _ptr(w2), _ptr(dyrows),
-        None if dx is None else _ptr(dx), None if dw13 is None else _ptr(dw13),
-        None if dw2 is None else _ptr(dw2))
+        _ptr(xrows), dt, R, d, ffn, _ptr(e), G, _ptr(w13), _ptr(w2), _ptr(dyrows), opt(dx), opt(gu),
+        opt(dgu), opt(dw13), opt(dw2))
+    if want_act:
+        return dx, dw13, dw2, gu, dgu
     return dx, dw13, dw2
+
+
+def _f64(a):
+    a = np.asarray(a)
+    return _c(bf16_bits_to_f64(a) if a.dtype == np.uint16 else a, np.float64)
+
+
+def down_backward_rows(dyrows, expert_of_row, w2, gu):
+    """B4a: dgu [R, 2 ffn] from dy rows, w2 [G, d, ffn] and given
+    pre-activations gu [R, 2 ffn] (bf16 bit patterns are widened exactly)."""
+    dy = _f64(dyrows)
+    gu = _f64(gu)
+    w2 = _c(w2)
+    R, d = dy.shape
+    ffn = w2.shape[2]
+    e = _c(expert_of_row, np.int32).reshape(-1)
+    assert gu.shape == (R, 2 * ffn) and e.size == R
+    out = np.empty((R, 2 * ffn), np.float64)
+    _load().orc_down_backward_rows(_ptr(dy), R, d, ffn, _ptr(e), _ptr(w2), _dtype_code(w2),
+                                   _ptr(gu), _ptr(out))
+    return out
+
+
+def gate_up_backward_rows(dgu, expert_of_row, w13):
+    """B4b: dx [R, d] from given dgu [R, 2 ffn] and w13 [G, 2, ffn, d]."""
+    dgu = _f64(dgu)
+    w13 = _c(w13)
+    R = dgu.shape[0]
+    ffn, d = w13.shape[2], w13.shape[3]
+    e = _c(expert_of_row, np.int32).reshape(-1)
+    assert dgu.shape == (R, 2 * ffn) and e.size == R
+    out = np.empty((R, d), np.float64)
+    _load().orc_gate_up_backward_rows(_ptr(dgu), R, d, ffn, _ptr(e), _ptr(w13), _dtype_code(w13),
+                                      _ptr(out))
+    return out
+
+
+def weight_grad(a, b, offsets, b_order=None, b_k=1):
+    """B4c: c [G, m, n], c[e] = sum over segment e's rows of a[r]^T b[src(r)]."""
+    a = _f64(a)
+    b = _f64(b)
+    offsets = _c(offsets, np.int32)
+    G = offsets.size - 1
+    R, m = a.shape
+    n = b.shape[1]
+    order = None if b_order is None else _c(b_order, np.int32)
+    out = np.empty((G, m, n), np.float64)
+    _load().orc_weight_grad(_ptr(a), R, m, _ptr(b), n, _ptr(offsets), G,
+                            None if order is None else _ptr(order), int(b_k), _ptr(out))
+    return out
 
 
 def gate_backward(logits: np.ndarray, ids: np.ndarray, dw: np.ndarray, gating: str = "softmax",

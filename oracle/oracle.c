@@ -438,74 +438,170 @@ void orc_combine_backward(const void *dy, int dy_dt, int64_t T, int k, int d, co
  *   du      = dh SiLU(g)
  *   dx      = W_gate^T dg + W_up^T du
  *   dW_down += dy h^T,   dW_gate += dg x^T,   dW_up += du x^T
- * The forward is recomputed from x in fp64.  Weight gradients are summed
- * over each expert's rows in increasing row order; dx, dw13 and dw2 may each
- * be NULL.  dw13 is [G, 2, ffn, d] and dw2 [G, d, ffn], both overwritten.
+ * The forward is recomputed from x in fp64.  First pass, row by row: g, u,
+ * h, dh, dg, du and dx.  Second pass, one weight-gradient row at a time:
+ * the sums over each expert's rows, in increasing row order.  Outputs, each
+ * may be NULL: dx [R, d]; gu [R, 2 ffn] = (g, u) and dgu [R, 2 ffn] =
+ * (dg, du) per row; dw13 [G, 2, ffn, d] and dw2 [G, d, ffn], overwritten.
  * ---------------------------------------------------------------------- */
 void orc_expert_swiglu_backward_rows(const void *xrows, int dtype, int64_t R, int d, int ffn,
                                      const int32_t *expert_of_row, int G, const void *w13,
                                      const void *w2, const double *dyrows, double *dx,
-                                     double *dw13, double *dw2)
+                                     double *gu, double *dgu, double *dw13, double *dw2)
 {
-    if (dw13) memset(dw13, 0, sizeof(double) * (size_t)G * 2 * ffn * d);
-    if (dw2) memset(dw2, 0, sizeof(double) * (size_t)G * d * ffn);
+    double *h = malloc(sizeof(double) * (size_t)(R > 0 ? R : 1) * ffn);
+    double *dg = malloc(sizeof(double) * (size_t)(R > 0 ? R : 1) * ffn);
+    double *du = malloc(sizeof(double) * (size_t)(R > 0 ? R : 1) * ffn);
 #pragma omp parallel
     {
         double *xv = malloc(sizeof(double) * (size_t)d);
         double *g = malloc(sizeof(double) * (size_t)ffn);
         double *u = malloc(sizeof(double) * (size_t)ffn);
-        double *dg = malloc(sizeof(double) * (size_t)ffn);
-        double *du = malloc(sizeof(double) * (size_t)ffn);
-        double *h = malloc(sizeof(double) * (size_t)ffn);
 #pragma omp for schedule(dynamic, 1)
-        for (int e = 0; e < G; ++e) {
-            const int64_t gate0 = (int64_t)e * 2 * ffn * d, up0 = gate0 + (int64_t)ffn * d;
-            const int64_t down0 = (int64_t)e * d * ffn;
-            for (int64_t r = 0; r < R; ++r) {
-                if (expert_of_row[r] != e) continue;
-                const double *dyv = dyrows + r * d;
-                for (int i = 0; i < d; ++i) xv[i] = widen(xrows, dtype, r * d + i);
+        for (int64_t r = 0; r < R; ++r) {
+            const int64_t e = expert_of_row[r];
+            const int64_t gate0 = e * 2 * ffn * d, up0 = gate0 + (int64_t)ffn * d;
+            const int64_t down0 = e * d * ffn;
+            const double *dyv = dyrows + r * d;
+            for (int i = 0; i < d; ++i) xv[i] = widen(xrows, dtype, r * d + i);
+            for (int n = 0; n < ffn; ++n) {
+                double a = 0.0, b = 0.0;
+                for (int i = 0; i < d; ++i) {
+                    a += widen(w13, dtype, gate0 + (int64_t)n * d + i) * xv[i];
+                    b += widen(w13, dtype, up0 + (int64_t)n * d + i) * xv[i];
+                }
+                g[n] = a;
+                u[n] = b;
+            }
+            for (int n = 0; n < ffn; ++n) {
+                double dh = 0.0;
+                for (int m = 0; m < d; ++m)
+                    dh += widen(w2, dtype, down0 + (int64_t)m * ffn + n) * dyv[m];
+                const double s = 1.0 / (1.0 + exp(-g[n]));
+                const double silu = g[n] * s;
+                const double dsilu = s * (1.0 + g[n] * (1.0 - s));
+                h[r * ffn + n] = silu * u[n];
+                dg[r * ffn + n] = dh * u[n] * dsilu;
+                du[r * ffn + n] = dh * silu;
+            }
+            if (gu)
                 for (int n = 0; n < ffn; ++n) {
-                    double a = 0.0, b = 0.0;
-                    for (int i = 0; i < d; ++i) {
-                        a += widen(w13, dtype, gate0 + (int64_t)n * d + i) * xv[i];
-                        b += widen(w13, dtype, up0 + (int64_t)n * d + i) * xv[i];
-                    }
-                    g[n] = a;
-                    u[n] = b;
+                    gu[r * 2 * ffn + n] = g[n];
+                    gu[r * 2 * ffn + ffn + n] = u[n];
                 }
+            if (dgu)
                 for (int n = 0; n < ffn; ++n) {
-                    double dh = 0.0;
-                    for (int m = 0; m < d; ++m)
-                        dh += widen(w2, dtype, down0 + (int64_t)m * ffn + n) * dyv[m];
-                    const double s = 1.0 / (1.0 + exp(-g[n]));
-                    const double silu = g[n] * s;
-                    const double dsilu = s * (1.0 + g[n] * (1.0 - s));
-                    h[n] = silu * u[n];
-                    dg[n] = dh * u[n] * dsilu;
-                    du[n] = dh * silu;
+                    dgu[r * 2 * ffn + n] = dg[r * ffn + n];
+                    dgu[r * 2 * ffn + ffn + n] = du[r * ffn + n];
                 }
-                if (dx) {
-                    for (int i = 0; i < d; ++i) {
-                        double acc = 0.0;
-                        for (int n = 0; n < ffn; ++n)
-                            acc += widen(w13, dtype, gate0 + (int64_t)n * d + i) * dg[n] +
-                                   widen(w13, dtype, up0 + (int64_t)n * d + i) * du[n];
-                        dx[r * d + i] = acc;
-                    }
-                }
-                if (dw2)
-                    for (int m = 0; m < d; ++m)
-                        for (int n = 0; n < ffn; ++n) dw2[down0 + (int64_t)m * ffn + n] += dyv[m] * h[n];
-                if (dw13)
+            if (dx) {
+                for (int i = 0; i < d; ++i) {
+                    double acc = 0.0;
                     for (int n = 0; n < ffn; ++n)
-                        for (int i = 0; i < d; ++i) {
-                            dw13[gate0 + (int64_t)n * d + i] += dg[n] * xv[i];
-                            dw13[up0 + (int64_t)n * d + i] += du[n] * xv[i];
-                        }
+                        acc += widen(w13, dtype, gate0 + (int64_t)n * d + i) * dg[r * ffn + n] +
+                               widen(w13, dtype, up0 + (int64_t)n * d + i) * du[r * ffn + n];
+                    dx[r * d + i] = acc;
+                }
             }
         }
-        free(xv); free(g); free(u); free(dg); free(du); free(h);
+        free(xv); free(g); free(u);
+    }
+    if (dw2) {
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t em = 0; em < (int64_t)G * d; ++em) {      /* row m of dW_down,e */
+            const int64_t e = em / d, m = em % d;
+            double *row = dw2 + em * ffn;
+            for (int n = 0; n < ffn; ++n) row[n] = 0.0;
+            for (int64_t r = 0; r < R; ++r) {
+                if (expert_of_row[r] != e) continue;
+                const double a = dyrows[r * d + m];
+                for (int n = 0; n < ffn; ++n) row[n] += a * h[r * ffn + n];
+            }
+        }
+    }
+    if (dw13) {
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t en = 0; en < (int64_t)G * 2 * ffn; ++en) { /* row n of dW_gate,e / dW_up,e */
+            const int64_t e = en / (2 * ffn), n = en % (2 * ffn);
+            const double *src = n < ffn ? dg : du;
+            const int64_t nn = n < ffn ? n : n - ffn;
+            double *row = dw13 + en * d;
+            for (int i = 0; i < d; ++i) row[i] = 0.0;
+            for (int64_t r = 0; r < R; ++r) {
+                if (expert_of_row[r] != e) continue;
+                const double a = src[r * ffn + nn];
+                for (int i = 0; i < d; ++i) row[i] += a * widen(xrows, dtype, r * d + i);
+            }
+        }
+    }
+    free(h); free(dg); free(du);
+}
+
+/* ------------------------------------------------------------------------
+ * B4's steps one at a time, each taking the previous step's result as an
+ * input (so a stage of an implementation can be fed the same values):
+ *
+ * B4a  dgu from the output gradient and given pre-activations:
+ *        dh = W_down^T dy;  dg = dh u SiLU'(g);  du = dh SiLU(g)
+ *      with (g, u) = gu[r] ([R, 2 ffn], gate then up); dgu [R, 2 ffn].
+ * B4b  dx = W_gate^T dg + W_up^T du from given (dg, du) = dgu[r]; dx [R, d].
+ * B4c  the weight-gradient sum over each expert's rows,
+ *        c[e] = sum_{r in e, increasing} a[r]^T b[src(r)]   ([G, m, n]),
+ *      src(r) = b_order[r] / b_k, or r when b_order is NULL: dW_down =
+ *      B4c(dy, h), dW13 = B4c(dgu, x rows).
+ * ---------------------------------------------------------------------- */
+void orc_down_backward_rows(const double *dyrows, int64_t R, int d, int ffn,
+                            const int32_t *expert_of_row, const void *w2, int dtype,
+                            const double *gu, double *dgu)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < R; ++r) {
+        const int64_t down0 = (int64_t)expert_of_row[r] * d * ffn;
+        for (int n = 0; n < ffn; ++n) {
+            double dh = 0.0;
+            for (int m = 0; m < d; ++m)
+                dh += widen(w2, dtype, down0 + (int64_t)m * ffn + n) * dyrows[r * d + m];
+            const double g = gu[r * 2 * ffn + n], u = gu[r * 2 * ffn + ffn + n];
+            const double s = 1.0 / (1.0 + exp(-g));
+            dgu[r * 2 * ffn + n] = dh * u * (s * (1.0 + g * (1.0 - s)));
+            dgu[r * 2 * ffn + ffn + n] = dh * (g * s);
+        }
+    }
+}
+
+void orc_gate_up_backward_rows(const double *dgu, int64_t R, int d, int ffn,
+                               const int32_t *expert_of_row, const void *w13, int dtype,
+                               double *dx)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < R; ++r) {
+        const int64_t gate0 = (int64_t)expert_of_row[r] * 2 * ffn * d, up0 = gate0 + (int64_t)ffn * d;
+        for (int i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int n = 0; n < ffn; ++n)
+                acc += widen(w13, dtype, gate0 + (int64_t)n * d + i) * dgu[r * 2 * ffn + n] +
+                       widen(w13, dtype, up0 + (int64_t)n * d + i) * dgu[r * 2 * ffn + ffn + n];
+            dx[r * d + i] = acc;
+        }
+    }
+}
+
+void orc_weight_grad(const double *a, int64_t R, int m, const double *b, int n,
+                     const int32_t *offsets, int G, const int32_t *b_order, int b_k, double *c)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t ei = 0; ei < (int64_t)G * m; ++ei) {
+        const int64_t e = ei / m, i = ei % m;
+        double *row = c + ei * n;
+        for (int j = 0; j < n; ++j) row[j] = 0.0;
+        int64_t lo = offsets[e], hi = offsets[e + 1];
+        if (lo < 0) lo = 0;
+        if (hi > R) hi = R;
+        for (int64_t r = lo; r < hi; ++r) {
+            const int64_t src = b_order ? b_order[r] / b_k : r;
+            const double ar = a[r * m + i];
+            for (int j = 0; j < n; ++j) row[j] += ar * b[src * n + j];
+        }
     }
 }
 

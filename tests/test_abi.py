@@ -172,6 +172,51 @@ def test_combine_validation(lib):
     assert f(a, 1, 0, 2, 16, NULL, NULL, NULL, NULL, NULL) == 0
 
 
+def test_backward_validation(lib):
+    a = ctypes.c_void_p(16)
+    mis = ctypes.c_void_p(24)
+    f = lib.moe_grouped_gate_up_save
+    #       x  dt T  k  M   d    ffn  order off G  w13 h  gu    stream
+    assert f(a, 1, 8, 2, 16, 128, 256, a, a, 4, a, a, NULL, NULL) == INVALID      # null gu
+    assert f(a, 1, 8, 2, 16, 128, 256, a, a, 4, a, a, mis, NULL) == INVALID       # misaligned gu
+    assert f(a, 1, 8, 2, 16, 96, 256, a, a, 4, a, a, a, NULL) == UNSUPPORTED      # d % 128
+    assert f(NULL, 1, 8, 2, 0, 128, 256, NULL, NULL, 4, NULL, NULL, NULL, NULL) == 0
+    f = lib.moe_combine_backward
+    #       dy dt T  k  d   inv w  y_perm dy_perm dgate dy_sh stream
+    assert f(a, 1, 4, 2, 16, a, a, a, a, NULL, NULL, NULL) == INVALID       # y_perm without dgate
+    assert f(a, 1, 4, 2, 16, a, a, NULL, a, a, NULL, NULL) == INVALID       # dgate without y_perm
+    assert f(a, 1, 4, 2, 12, a, a, a, a, a, NULL, NULL) == UNSUPPORTED      # d % 8
+    assert f(a, 1, 4, 65, 16, a, a, a, a, a, NULL, NULL) == UNSUPPORTED     # k > 64
+    assert f(a, 1, 4, 2, 16, a, NULL, a, a, a, NULL, NULL) == INVALID       # null gates
+    assert f(a, 1, 4, 2, 16, a, a, a, mis, a, NULL, NULL) == INVALID        # misaligned dy_perm
+    assert f(NULL, 1, 0, 2, 16, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == 0
+    f = lib.moe_gate_backward
+    #       logits ids w  dgate T  E  k  gating renorm dl stream
+    assert f(a, a, a, a, 4, 8, 9, 0, 1, a, NULL) == INVALID                 # k > E
+    assert f(a, a, a, a, 4, 8, 2, 7, 1, a, NULL) == INVALID                 # gating
+    assert f(a, a, a, NULL, 4, 8, 2, 0, 1, a, NULL) == INVALID              # null dgate
+    assert f(a, a, a, a, 4, 5000, 2, 0, 1, a, NULL) == UNSUPPORTED          # E > 4096
+    assert f(NULL, NULL, NULL, NULL, 0, 8, 2, 0, 1, NULL, NULL) == 0
+    for g in (lib.moe_grouped_down_backward, lib.moe_grouped_gate_up_backward):
+        extra = (a,) if g is lib.moe_grouped_down_backward else ()
+        #          a  dt M   d    ffn  off G  w  [gu] out stream
+        assert g(a, 0, 64, 128, 256, a, 4, a, *extra, a, NULL) == UNSUPPORTED   # fp32
+        assert g(a, 1, 64, 96, 256, a, 4, a, *extra, a, NULL) == UNSUPPORTED    # d % 128
+        assert g(a, 1, 64, 128, 200, a, 4, a, *extra, a, NULL) == UNSUPPORTED   # ffn % 128
+        assert g(a, 1, 64, 128, 256, a, 0, a, *extra, a, NULL) == INVALID       # G < 1
+        assert g(a, 1, 64, 128, 256, NULL, 4, a, *extra, a, NULL) == INVALID    # null offsets
+        assert g(a, 1, 64, 128, 256, a, 4, a, *extra, mis, NULL) == INVALID     # misaligned out
+        assert g(a, 1, 0, 128, 256, NULL, 4, NULL, *((NULL,) if extra else ()), NULL, NULL) == 0
+    g = lib.moe_grouped_weight_grad
+    #       a  b  dt M   m    n    off G  order bk brows c  stream
+    assert g(a, a, 0, 64, 128, 256, a, 4, NULL, 1, 0, a, NULL) == UNSUPPORTED   # fp32
+    assert g(a, a, 1, 64, 96, 256, a, 4, NULL, 1, 0, a, NULL) == UNSUPPORTED    # m % 128
+    assert g(a, a, 1, 64, 128, 256, a, 4, NULL, 0, 0, a, NULL) == INVALID       # b_k < 1
+    assert g(a, a, 1, 64, 128, 256, a, 4, a, 2, 0, a, NULL) == INVALID          # b_rows < 1
+    assert g(a, a, 1, 64, 128, 256, NULL, 4, NULL, 1, 0, a, NULL) == INVALID    # null offsets
+    assert g(a, mis, 1, 64, 128, 256, a, 4, NULL, 1, 0, a, NULL) == INVALID     # misaligned b
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(moe.MoeError):
         moe.load_library(str(tmp_path / "missing.so"))

@@ -1,0 +1,162 @@
+"""GPU parity of the backward pass at the full-size bf16 workloads, through
+MoeLayer(train=True) on the fused-gather path.
+
+Sampled, because the oracle's fp64 backward of a whole DeepSeek-V3-shaped
+batch is hours of CPU work:
+  * the token gradient dx and the gate gradients on 64 seeded tokens,
+    against the oracle's backward computed from x alone (dx per row within
+    2e-2 of the row's largest magnitude; dgate within 2e-2 of sum |dy y|;
+    dlogits on the GPU's dgate within 1e-4 of the operand scale);
+  * each backward product on sampled rows or output rows, against the
+    oracle's step fed the very values the GPU step read (dgu, dx_perm per
+    packed row; weight-gradient output rows of two experts), within 2e-2 of
+    the row's largest magnitude.
+The shared expert's weight gradients sum over every token and are checked at
+the small sizes of test_gpu_backward.py only.
+"""
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+from token_routing_expert_amd import inputs
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(1500)]
+
+torch = pytest.importorskip("torch")
+
+TRAIN_CONFIGS = [n for n in inputs.CONFIG_ORDER if inputs.CONFIGS[n].dtype == "bf16"]
+
+
+def log(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+def f64(a):
+    a = np.asarray(a)
+    return oracle.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def rows_close(gpu, ref, rel, what):
+    gpu = f64(gpu).reshape(ref.shape[0], -1)
+    err = np.abs(gpu - ref).max(axis=1)
+    scale = np.abs(ref).max(axis=1)
+    worst = float(np.max(err / np.maximum(scale, 1e-300))) if len(ref) else 0.0
+    assert (err <= rel * scale).all(), f"{what}: {int((err > rel * scale).sum())} rows off, worst {worst:.3g}"
+    return worst
+
+
+class Case:
+    pass
+
+
+@pytest.fixture(scope="module", params=TRAIN_CONFIGS)
+def case(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from token_routing_expert_amd.layer import MoeLayer, to_device, to_host
+    cfg = inputs.CONFIGS[request.param]
+    c = Case()
+    c.cfg = cfg
+    log(f"{cfg.name}: generating inputs")
+    c.x = inputs.gen_x(cfg)
+    c.w13, c.w2 = inputs.gen_expert_weights(cfg, verbose=True)
+    c.sh = inputs.gen_expert_weights(cfg, shared=True) if cfg.shared else (None, None)
+    if cfg.gating == "given":
+        c.logits = None
+        c.ids, c.w = inputs.gen_ep_share_routing(cfg)
+    else:
+        c.logits = inputs.gen_logits(cfg)
+        c.ids, c.w = oracle.route(c.logits, cfg.k, cfg.gating, cfg.renormalize, cfg.n_groups,
+                                  cfg.topk_groups)
+    c.dy = inputs.f32_to_bf16_bits(
+        np.random.default_rng(1000 + cfg.index).standard_normal((cfg.T, cfg.d)).astype(np.float32))
+    log(f"{cfg.name}: forward + backward")
+    layer = MoeLayer(cfg, c.x, c.w13, c.w2, logits=c.logits, sh_w13=c.sh[0], sh_w2=c.sh[1],
+                     topk_ids=c.ids if c.logits is None else None,
+                     topk_w=c.w if c.logits is None else None, fused_gather=True, train=True)
+    layer.forward()
+    g = layer.backward(to_device(c.dy))
+    torch.cuda.synchronize()
+    c.g = {k: to_host(v) for k, v in g.items()}
+    b = layer._grads
+    c.g.update(dy_perm=to_host(b["dy_perm"]), dgu=to_host(b["dgu"]), dx_perm=to_host(b["dx_perm"]),
+               gu=to_host(layer.gu), h=to_host(layer.h), offsets=to_host(layer.offsets),
+               order=to_host(layer.order), topk_ids=to_host(layer.topk_ids))
+    del layer
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(77)
+    c.tokens = np.sort(rng.choice(cfg.T, size=min(64, cfg.T), replace=False))
+    M = cfg.T * cfg.k
+    c.rows = np.sort(rng.choice(M, size=min(64, M), replace=False))
+    counts = np.diff(c.g["offsets"])
+    nonempty = np.flatnonzero(counts)
+    c.experts = np.sort(rng.choice(nonempty, size=min(2, nonempty.size), replace=False))
+    log(f"{cfg.name}: ready")
+    yield c
+
+
+def test_token_gradients(case):
+    cfg, c = case.cfg, case
+    k, t = cfg.k, c.tokens
+    assert np.array_equal(c.g["topk_ids"], c.ids)
+    xs = np.ascontiguousarray(c.x[t])
+    rows = np.repeat(xs, k, axis=0)
+    ids = c.ids[t].reshape(-1)
+    log(f"{cfg.name}: oracle backward on {len(t)} tokens")
+    y_rows = oracle.expert_swiglu_rows(rows, ids, c.w13, c.w2)
+    ident = np.arange(len(t) * k, dtype=np.int32)
+    dy_rows, dgate = oracle.combine_backward(c.dy[t], ident, c.w[t], y_rows)
+    dx_rows, _, _ = oracle.expert_swiglu_backward_rows(rows, ids, c.w13, c.w2, dy_rows, want_dw=False)
+    dx = dx_rows.reshape(len(t), k, cfg.d).sum(axis=1)
+    if cfg.shared:
+        dx_sh, _, _ = oracle.expert_swiglu_backward_rows(xs, np.zeros(len(t), np.int32), *c.sh,
+                                                         f64(c.dy[t]), want_dw=False)
+        dx = dx + dx_sh
+    worst = {"dx": rows_close(c.g["dx"][t], dx, 2e-2, "dx")}
+    if cfg.gating != "given":
+        got = c.g["dgate"][t].astype(np.float64)
+        absdot = (np.abs(f64(c.dy[t]))[:, None, :] * np.abs(y_rows.reshape(len(t), k, -1))).sum(axis=2)
+        assert np.all(np.abs(got - dgate) <= 2e-2 * absdot), "dgate"
+        worst["dgate"] = float(np.max(np.abs(got - dgate) / absdot))
+        ref = oracle.gate_backward(c.logits[t], c.ids[t], got, cfg.gating, cfg.renormalize)
+        scale = np.abs(c.w[t]).max(axis=1) * np.abs(got).sum(axis=1)
+        err = np.abs(c.g["dlogits"][t] - ref).max(axis=1)
+        assert np.all(err <= 1e-4 * scale), "dlogits"
+        worst["dlogits"] = float(np.max(err / scale))
+    log(f"{cfg.name}: {worst}")
+
+
+def test_backward_products_on_sampled_rows(case):
+    cfg, c = case.cfg, case
+    p = c.rows
+    expert = (np.searchsorted(c.g["offsets"], p, side="right") - 1).astype(np.int32)
+    dgu = oracle.down_backward_rows(c.g["dy_perm"][p], expert, c.w2, c.g["gu"][p])
+    w1 = rows_close(c.g["dgu"][p], dgu, 2e-2, "dgu")
+    dx = oracle.gate_up_backward_rows(c.g["dgu"][p], expert, c.w13)
+    w2_ = rows_close(c.g["dx_perm"][p], dx, 2e-2, "dx_perm")
+    log(f"{cfg.name}: dgu {w1:.2e} dx_perm {w2_:.2e}")
+
+
+def test_weight_gradients_of_sampled_experts(case):
+    cfg, c = case.cfg, case
+    rng = np.random.default_rng(5)
+    d, ffn, k = cfg.d, cfg.ffn, cfg.k
+    off = c.g["offsets"]
+    worst = []
+    for e in c.experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        seg = np.array([0, hi - lo], np.int32)
+        m_sub = np.sort(rng.choice(d, 8, replace=False))
+        n_sub = np.sort(rng.choice(2 * ffn, 8, replace=False))
+        # dW_down,e rows m_sub: sum over the segment of dy_perm[r, m] h[r, :]
+        ref2 = oracle.weight_grad(c.g["dy_perm"][lo:hi][:, m_sub], c.g["h"][lo:hi], seg)[0]
+        got2 = c.g["dw2"][e][m_sub]
+        worst.append(rows_close(got2, ref2, 2e-2, f"dw2[{e}]"))
+        # dW13,e rows n_sub: sum over the segment of dgu[r, n] x[order[r] / k, :]
+        ref13 = oracle.weight_grad(c.g["dgu"][lo:hi][:, n_sub], c.x, seg,
+                                   c.g["order"][lo:hi], k)[0]
+        got13 = c.g["dw13"][e].reshape(2 * ffn, d)[n_sub]
+        worst.append(rows_close(got13, ref13, 2e-2, f"dw13[{e}]"))
+    log(f"{cfg.name}: experts {list(c.experts)} worst {max(worst):.2e}")

@@ -201,3 +201,54 @@ def test_combine_backward_packed_positions():
         t, j = divmod(int(order[p]), k)
         np.testing.assert_array_equal(dy_perm[p], np.float64(w[t, j]) * dy[t])
         assert abs(dw[t, j] - float(np.dot(dy[t], y_perm[p]))) < 1e-12
+
+
+def test_preactivations_and_their_gradients_match_autodiff():
+    """B4's optional outputs: the pre-activations (g, u) of each row and their
+    gradients (dg, du), against torch's evaluation and reverse-mode autodiff
+    of one SwiGLU MLP per expert."""
+    rng = np.random.default_rng(12)
+    R, G, d, ffn = 9, 3, 16, 8
+    x = rng.standard_normal((R, d))
+    e = rng.integers(0, G, R).astype(np.int32)
+    w13 = 0.3 * rng.standard_normal((G, 2, ffn, d))
+    w2 = 0.3 * rng.standard_normal((G, d, ffn))
+    dy = rng.standard_normal((R, d))
+    _, _, _, gu, dgu = oracle.expert_swiglu_backward_rows(x, e, w13, w2, dy, want_act=True)
+    for r in range(R):
+        X = torch.tensor(x[r])
+        g = (torch.tensor(w13[e[r], 0]) @ X).requires_grad_(True)
+        u = (torch.tensor(w13[e[r], 1]) @ X).requires_grad_(True)
+        y = torch.tensor(w2[e[r]]) @ (torch.nn.functional.silu(g) * u)
+        (y * torch.tensor(dy[r])).sum().backward()
+        np.testing.assert_allclose(gu[r], np.concatenate([g.detach().numpy(), u.detach().numpy()]),
+                                   rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dgu[r], np.concatenate([g.grad.numpy(), u.grad.numpy()]),
+                                   rtol=1e-10, atol=1e-12)
+
+
+def test_backward_stages_compose_to_the_whole():
+    """B4a, B4b and B4c fed B4's own intermediates reproduce B4's outputs, so
+    they carry B4's autodiff pin; B4c with an order reads the gathered rows."""
+    rng = np.random.default_rng(13)
+    R, G, d, ffn, k = 11, 3, 16, 8, 2
+    x = rng.standard_normal((R, d))
+    e = np.sort(rng.integers(0, G, R)).astype(np.int32)
+    offsets = np.searchsorted(e, np.arange(G + 1)).astype(np.int32)
+    w13 = 0.3 * rng.standard_normal((G, 2, ffn, d))
+    w2 = 0.3 * rng.standard_normal((G, d, ffn))
+    dy = rng.standard_normal((R, d))
+    dx, dw13, dw2, gu, dgu = oracle.expert_swiglu_backward_rows(x, e, w13, w2, dy, want_act=True)
+    np.testing.assert_allclose(oracle.down_backward_rows(dy, e, w2, gu), dgu, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(oracle.gate_up_backward_rows(dgu, e, w13), dx, rtol=1e-13, atol=1e-13)
+    g, u = gu[:, :ffn], gu[:, ffn:]
+    h = g / (1 + np.exp(-g)) * u
+    np.testing.assert_allclose(oracle.weight_grad(dy, h, offsets), dw2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.weight_grad(dgu, x, offsets).reshape(G, 2, ffn, d), dw13,
+                               rtol=1e-12, atol=1e-12)
+    # The gathered form: row r of b is xt[order[r] // k].
+    T = 7
+    xt = rng.standard_normal((T, d))
+    order = rng.integers(0, T * k, R).astype(np.int32)
+    np.testing.assert_array_equal(oracle.weight_grad(dgu, xt, offsets, order, k),
+                                  oracle.weight_grad(dgu, xt[order // k], offsets))

@@ -23,7 +23,9 @@ EXPORTS = ("moe_status_string", "moe_route_topk", "moe_route_topk_biased", "moe_
            "moe_router_bias_update", "moe_sigmoid_pinned", "moe_send_counts",
            "moe_permute_workspace_bytes", "moe_permute", "moe_grouped_swiglu",
            "moe_grouped_gate_up", "moe_grouped_gate_up_gather", "moe_grouped_down",
-           "moe_unpermute_combine")
+           "moe_unpermute_combine", "moe_grouped_gate_up_save", "moe_combine_backward",
+           "moe_gate_backward", "moe_grouped_down_backward", "moe_grouped_gate_up_backward",
+           "moe_grouped_weight_grad")
 
 
 class MoeError(RuntimeError):
@@ -58,10 +60,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_grouped_gate_up_gather.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, i32, P, P, P]
     lib.moe_grouped_down.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P]
     lib.moe_unpermute_combine.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P]
+    lib.moe_grouped_gate_up_save.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, i32, P, P, P, P]
+    lib.moe_combine_backward.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, P]
+    lib.moe_gate_backward.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, P, P]
+    lib.moe_grouped_down_backward.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P, P]
+    lib.moe_grouped_gate_up_backward.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P]
+    lib.moe_grouped_weight_grad.argtypes = [P, P, i32, i32, i32, i32, P, i32, P, i32, i32, P, P]
     for name in ("moe_route_topk", "moe_route_topk_biased", "moe_router_logits",
                  "moe_router_bias_update", "moe_sigmoid_pinned", "moe_send_counts", "moe_permute",
                  "moe_grouped_swiglu", "moe_grouped_gate_up", "moe_grouped_gate_up_gather",
-                 "moe_grouped_down", "moe_unpermute_combine"):
+                 "moe_grouped_down", "moe_unpermute_combine", "moe_grouped_gate_up_save",
+                 "moe_combine_backward", "moe_gate_backward", "moe_grouped_down_backward",
+                 "moe_grouped_gate_up_backward", "moe_grouped_weight_grad"):
         getattr(lib, name).restype = i32
     if path == LIB_PATH:
         _lib = lib
@@ -320,13 +330,21 @@ def moe_grouped_down(h, offsets, w2, y=None, stream=None):
     return y
 
 
-def moe_unpermute_combine(y_perm, inv, topk_w, y_shared=None, y=None, stream=None):
-    """y [T, d] = sum_j topk_w[t,j] y_perm[inv[t k + j]] (+ y_shared[t])."""
+def moe_unpermute_combine(y_perm, inv, topk_w, y_shared=None, y=None, stream=None, k=None):
+    """y [T, d] = sum_j topk_w[t,j] y_perm[inv[t k + j]] (+ y_shared[t]).
+
+    topk_w None (then k is required): every gate is 1, the sum of a token's
+    k rows -- the permute's backward."""
     torch = _torch()
     _dev(y_perm, "y_perm", _act_dtypes())
     _dev(inv, "inv", (torch.int32,))
-    _dev(topk_w, "topk_w", (torch.float32,))
-    T, k = topk_w.shape
+    if topk_w is None:
+        if not k or inv.numel() % k:
+            raise MoeError("moe_unpermute_combine: k must divide inv's length when topk_w is None")
+        T = inv.numel() // k
+    else:
+        _dev(topk_w, "topk_w", (torch.float32,))
+        T, k = topk_w.shape
     d = y_perm.shape[1]
     if y_shared is not None:
         _dev(y_shared, "y_shared", (y_perm.dtype,))
@@ -336,3 +354,142 @@ def moe_unpermute_combine(y_perm, inv, topk_w, y_shared=None, y=None, stream=Non
                                                 _ptr(inv), _ptr(topk_w), _ptr(y_shared), _ptr(y),
                                                 _stream(stream)), "moe_unpermute_combine")
     return y
+
+
+# --------------------------------------------------------------------------
+# Training: the forward product that keeps the pre-activations, and the
+# backward pass.
+# --------------------------------------------------------------------------
+
+def moe_grouped_gate_up_save(x, offsets, w13, h=None, gu=None, order=None, k=1, stream=None):
+    """h [M, ffn] as moe_grouped_gate_up(_gather), plus the pre-activations
+    gu [M, 2 ffn] (gate columns, then up columns) for the backward.  With
+    order, row p is x[order[p] // k] (M = order.numel()); else x is [M, d]."""
+    torch = _torch()
+    G = _expert_shapes("moe_grouped_gate_up_save", x, offsets, w13=w13)
+    T, d = x.shape
+    if order is not None:
+        _dev(order, "order", (torch.int32,))
+        M = order.numel()
+    else:
+        M = T
+    ffn = w13.shape[2]
+    if w13.shape[3] != d:
+        raise MoeError("moe_grouped_gate_up_save: inconsistent shapes")
+    h = torch.empty((M, ffn), dtype=x.dtype, device=x.device) if h is None else h
+    gu = torch.empty((M, 2 * ffn), dtype=x.dtype, device=x.device) if gu is None else gu
+    _dev(h, "h", (x.dtype,))
+    _dev(gu, "gu", (x.dtype,))
+    _check(load_library().moe_grouped_gate_up_save(
+        _ptr(x), _dtype_code(x), T, k, M, d, ffn, _ptr(order), _ptr(offsets), G, _ptr(w13),
+        _ptr(h), _ptr(gu), _stream(stream)), "moe_grouped_gate_up_save")
+    return h, gu
+
+
+def moe_combine_backward(dy, inv, topk_w, y_perm=None, dy_perm=None, dgate=None, dy_shared=None,
+                         stream=None, want_dgate=True):
+    """The combine's backward: dy_perm [M, d] (row inv[t k + j] = w[t,j] dy[t])
+    and, with y_perm, dgate [T, k] (dgate[t,j] = dy[t] . y_perm[inv[t k + j]]).
+    dy_shared [T, d] (optional) receives a copy of dy (the shared expert's
+    gradient rows).  Returns (dy_perm, dgate or None)."""
+    torch = _torch()
+    _dev(dy, "dy", _act_dtypes())
+    _dev(inv, "inv", (torch.int32,))
+    _dev(topk_w, "topk_w", (torch.float32,))
+    T, k = topk_w.shape
+    d = dy.shape[1]
+    dev = dy.device
+    dy_perm = torch.empty((T * k, d), dtype=dy.dtype, device=dev) if dy_perm is None else dy_perm
+    _dev(dy_perm, "dy_perm", (dy.dtype,))
+    if want_dgate and y_perm is not None:
+        _dev(y_perm, "y_perm", (dy.dtype,))
+        dgate = torch.empty((T, k), dtype=torch.float32, device=dev) if dgate is None else dgate
+        _dev(dgate, "dgate", (torch.float32,))
+    else:
+        y_perm, dgate = None, None
+    if dy_shared is not None:
+        _dev(dy_shared, "dy_shared", (dy.dtype,))
+    _check(load_library().moe_combine_backward(
+        _ptr(dy), _dtype_code(dy), T, k, d, _ptr(inv), _ptr(topk_w), _ptr(y_perm), _ptr(dy_perm),
+        _ptr(dgate), _ptr(dy_shared), _stream(stream)), "moe_combine_backward")
+    return dy_perm, dgate
+
+
+def moe_gate_backward(logits, topk_ids, topk_w, dgate, gating="softmax", renormalize=True,
+                      dlogits=None, stream=None):
+    """dlogits [T, E] fp32 from the gate gradients dgate [T, k]."""
+    torch = _torch()
+    _dev(logits, "logits", (torch.float32,))
+    _dev(topk_ids, "topk_ids", (torch.int32,))
+    _dev(topk_w, "topk_w", (torch.float32,))
+    _dev(dgate, "dgate", (torch.float32,))
+    T, E = logits.shape
+    k = topk_ids.shape[1]
+    dlogits = torch.empty((T, E), dtype=torch.float32, device=logits.device) if dlogits is None \
+        else dlogits
+    _dev(dlogits, "dlogits", (torch.float32,))
+    g = MOE_SOFTMAX if gating == "softmax" else MOE_SIGMOID if gating == "sigmoid" else -1
+    _check(load_library().moe_gate_backward(_ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+                                            _ptr(dgate), T, E, k, g, int(bool(renormalize)),
+                                            _ptr(dlogits), _stream(stream)), "moe_gate_backward")
+    return dlogits
+
+
+def moe_grouped_down_backward(dy_perm, offsets, w2, gu, dgu=None, stream=None):
+    """dgu [M, 2 ffn]: dh = dy_perm W_down,e per segment, then the SwiGLU
+    backward at the saved pre-activations gu (gate columns, then up)."""
+    G = _expert_shapes("moe_grouped_down_backward", dy_perm, offsets, w2=w2)
+    M, d = dy_perm.shape
+    ffn = w2.shape[2]
+    if w2.shape[1] != d or tuple(gu.shape) != (M, 2 * ffn):
+        raise MoeError("moe_grouped_down_backward: inconsistent shapes")
+    _dev(gu, "gu", (dy_perm.dtype,))
+    dgu = _torch().empty((M, 2 * ffn), dtype=dy_perm.dtype, device=dy_perm.device) if dgu is None \
+        else dgu
+    _dev(dgu, "dgu", (dy_perm.dtype,))
+    _check(load_library().moe_grouped_down_backward(
+        _ptr(dy_perm), _dtype_code(dy_perm), M, d, ffn, _ptr(offsets), G, _ptr(w2), _ptr(gu),
+        _ptr(dgu), _stream(stream)), "moe_grouped_down_backward")
+    return dgu
+
+
+def moe_grouped_gate_up_backward(dgu, offsets, w13, dx_perm=None, stream=None):
+    """dx_perm [M, d] = dgu [M, 2 ffn] W13,e per segment (W13,e as [2 ffn, d])."""
+    G = _expert_shapes("moe_grouped_gate_up_backward", dgu, offsets, w13=w13)
+    M = dgu.shape[0]
+    ffn, d = w13.shape[2], w13.shape[3]
+    if dgu.shape[1] != 2 * ffn:
+        raise MoeError("moe_grouped_gate_up_backward: inconsistent shapes")
+    dx_perm = _torch().empty((M, d), dtype=dgu.dtype, device=dgu.device) if dx_perm is None \
+        else dx_perm
+    _dev(dx_perm, "dx_perm", (dgu.dtype,))
+    _check(load_library().moe_grouped_gate_up_backward(
+        _ptr(dgu), _dtype_code(dgu), M, d, ffn, _ptr(offsets), G, _ptr(w13), _ptr(dx_perm),
+        _stream(stream)), "moe_grouped_gate_up_backward")
+    return dx_perm
+
+
+def moe_grouped_weight_grad(a, b, offsets, out=None, b_order=None, b_k=1, stream=None):
+    """out [G, m, n]: out[e] = a[seg e]^T b[rows of seg e] for a [M, m] and
+    b [*, n]; with b_order, row p of b is b[b_order[p] // b_k]."""
+    torch = _torch()
+    _dev(a, "a", _act_dtypes())
+    _dev(b, "b", (a.dtype,))
+    _dev(offsets, "offsets", (torch.int32,))
+    G = offsets.numel() - 1
+    M, m = a.shape
+    b_rows, n = b.shape
+    if b_order is not None:
+        _dev(b_order, "b_order", (torch.int32,))
+        if b_order.numel() != M:
+            raise MoeError("moe_grouped_weight_grad: b_order must have one entry per row of a")
+    elif b_rows != M:
+        raise MoeError("moe_grouped_weight_grad: a and b must have the same rows")
+    out = torch.empty((G, m, n), dtype=a.dtype, device=a.device) if out is None else out
+    _dev(out, "out", (a.dtype,))
+    if out.numel() != G * m * n:
+        raise MoeError("moe_grouped_weight_grad: out must hold [G, m, n]")
+    _check(load_library().moe_grouped_weight_grad(
+        _ptr(a), _ptr(b), _dtype_code(a), M, m, n, _ptr(offsets), G, _ptr(b_order), b_k, b_rows,
+        _ptr(out), _stream(stream)), "moe_grouped_weight_grad")
+    return out

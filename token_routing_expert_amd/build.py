@@ -19,7 +19,8 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe355.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["route.hip", "router.hip", "permute.hip", "grouped_gemm.hip", "combine.hip"]
+SOURCES = ["route.hip", "router.hip", "permute.hip", "grouped_gemm.hip", "grouped_gemm_bwd.hip",
+           "combine.hip", "backward.hip"]
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
     # Packed fp32 VALU forms stay off; the compiler emits scalar fp32 instead.

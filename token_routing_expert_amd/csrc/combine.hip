@@ -1,4 +1,7 @@
 // Unpermute and weight: y[t] = sum_j w[t,j] y_perm[inv[t k + j]] (+ y_shared[t]).
+// With no gates (w = NULL) every gate is 1: the sum of a token's k rows,
+// which is also the backward of the permute (the dispatch's gradient is
+// combined back into the token).
 //
 // Step 7 of the forward pass in "Expert parallelism" (zerotofrontier.app):
 // undo the sort and scatter-add each row into its token with its gate.  Here
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint4 *__restrict__ 
     if (j < k) {
       const int q = uniform(inv[(int64_t)t * k + j]);
       p[j] = q >= 0 && q < M ? q : -1;
-      g[j] = __uint_as_float(uniform(__float_as_uint(w[(int64_t)t * k + j])));
+      g[j] = w ? __uint_as_float(uniform(__float_as_uint(w[(int64_t)t * k + j]))) : 1.0f;
     }
   }
   for (int v0 = lane; v0 < nvec; v0 += NV * kWave) {
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_anyk(const uint4 *__restri
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int p = uniform(inv[(int64_t)t * k + j + u]);
-        g[u] = w[(int64_t)t * k + j + u];
+        g[u] = w ? w[(int64_t)t * k + j + u] : 1.0f;
         ok[u] = p >= 0 && p < M;
         if (ok[u]) r[u] = y_perm[(int64_t)p * nvec + v];
       }
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_anyk(const uint4 *__restri
     }
     for (; j < k; ++j) {
       const int p = uniform(inv[(int64_t)t * k + j]);
-      if (p >= 0 && p < M) V::add(acc, w[(int64_t)t * k + j], y_perm[(int64_t)p * nvec + v]);
+      if (p >= 0 && p < M) V::add(acc, w ? w[(int64_t)t * k + j] : 1.0f, y_perm[(int64_t)p * nvec + v]);
     }
     if (y_sh) V::add(acc, 1.0f, y_sh[(int64_t)t * nvec + v]);
     y[(int64_t)t * nvec + v] = V::pack(acc);
@@ -176,7 +179,7 @@ extern "C" moe_status moe_unpermute_combine(const void *y_perm, moe_dtype dt, in
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (d % 8 != 0 || k > 64 || (int64_t)T * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  if (!y_perm || !inv || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!y_perm || !inv || !y) return MOE_ERR_INVALID_ARG;   // topk_w NULL: every gate is 1
   if (!aligned16(y_perm) || !aligned16(y) || (y_shared && !aligned16(y_shared)))
     return MOE_ERR_INVALID_ARG;
   const int elem = dt == MOE_F32 ? 4 : 2;

@@ -19,15 +19,10 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "gemm_common.hpp"
 
 namespace moe {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-// 16 bytes as a native vector (HIP's uint4 struct defeats register promotion
-// of small arrays).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <bool BF16>
 struct Mma;
@@ -60,108 +55,6 @@ struct Mma<false> {
 __device__ __forceinline__ int swz_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz(int r, int cc) { return r * 8 + (cc ^ swz_key(r)); }
 
-__device__ __forceinline__ int clamp_row(int v, int M) { return v < 0 ? 0 : (v > M ? M : v); }
-
-struct Tile {
-  int expert, lo, hi, m0, n_tile;
-};
-
-// MI355X dispatches workgroup i of a launch to XCD i % 8; each XCD has its own
-// L2.  The persistent kernels below give XCD x a contiguous band of tiles so
-// the tiles that share operands run on the same L2 at the same time.
-constexpr int kXcds = 8;
-
-// Total number of (m, n) tiles over all expert segments.  Every wave
-// computes the same value.
-template <int BM>
-__device__ __forceinline__ int count_tiles(const int32_t *__restrict__ offsets, int G, int M,
-                                           int ntiles) {
-  const int lane = lane_id();
-  int sum = 0;
-  for (int eb = 0; eb < G; eb += kWave) {
-    const int e = eb + lane;
-    if (e < G) {
-      const int a = clamp_row(offsets[e], M), b = clamp_row(offsets[e + 1], M);
-      const int n = b > a ? b - a : 0;
-      sum += ((n + BM - 1) / BM) * ntiles;
-    }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-  return uniform(sum);
-}
-
-// Which expert and which (m, n) tile is tile number L.  Tiles are numbered
-// expert by expert; inside an expert n-tile major and m-tile minor, so the
-// m-tiles that share one weight tile are adjacent and the n-tiles that share
-// the expert's rows follow each other.  Every wave computes the same answer.
-// A workgroup asks for increasing L, so the search resumes at the expert
-// (e0) and tile number (base) of the previous answer: one 64-expert window
-// per call in the usual case instead of a scan from expert 0.
-template <int BM>
-__device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int G, int M,
-                                          int ntiles, int L, Tile &t, int &e0, int &base) {
-  const int lane = lane_id();
-  int running = base;
-  for (int eb = e0; eb < G; eb += kWave) {
-    const int e = eb + lane;
-    int a = 0, b = 0, tiles = 0;
-    if (e < G) {
-      a = clamp_row(offsets[e], M);
-      b = clamp_row(offsets[e + 1], M);
-      const int n = b > a ? b - a : 0;
-      tiles = ((n + BM - 1) / BM) * ntiles;
-    }
-    int incl = tiles;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    const int excl = running + incl - tiles;
-    const uint64_t hit = __ballot(tiles > 0 && L >= excl && L < excl + tiles);
-    if (hit) {
-      const int src = __ffsll((unsigned long long)hit) - 1;
-      t.expert = eb + src;
-      t.lo = uniform(__shfl(a, src));
-      t.hi = uniform(__shfl(b, src));
-      const int first = uniform(__shfl(excl, src));
-      const int local = L - first;
-      const int mtiles = (t.hi - t.lo + BM - 1) / BM;
-      t.m0 = t.lo + (local % mtiles) * BM;
-      t.n_tile = local / mtiles;
-      e0 = t.expert;
-      base = first;
-      return true;
-    }
-    running += __shfl(incl, kWave - 1);
-  }
-  return false;
-}
-
-// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 63] (the count is an
-// immediate, so the value selects one of 64 waits through a branch tree).
-template <int LO, int HI>
-__device__ __forceinline__ void wait_vmcnt_range(int n) {
-  if constexpr (LO == HI) {
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (LO & 15) | ((LO >> 4) << 14));
-  } else {
-    constexpr int MID = (LO + HI) / 2;
-    if (n <= MID) wait_vmcnt_range<LO, MID>(n);
-    else wait_vmcnt_range<MID + 1, HI>(n);
-  }
-}
-__device__ __forceinline__ void wait_vmcnt(int n) { wait_vmcnt_range<0, 63>(n < 63 ? n : 63); }
-
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
-
-// Source row of packed row p under a gather: token gather[p] / gk, clamped to
-// [0, a_rows) so a corrupt index can only steer a read inside A.
-__device__ __forceinline__ uint32_t gather_row(const int32_t *gather, int p, int gk, int a_rows) {
-  const uint32_t src = (uint32_t)gather[p] / (uint32_t)gk;
-  return src < (uint32_t)a_rows ? src : (uint32_t)a_rows - 1u;
-}
-
 // Block tile: up to BM rows x BN output columns (of h or y), WM x WN waves.
 // Wave (wm, wn) owns row blocks wm, wm + WM, wm + 2 WM, ... (32 rows each,
 // interleaved so a short tile still spreads over all waves) and BN / WN
@@ -188,11 +81,12 @@ __device__ __forceinline__ uint32_t gather_row(const int32_t *gather, int p, int
 // its LDS slot.  Row groups wholly past the segment end are not loaded.  Each
 // wave waits (vmcnt) only for its own loads of the slice about to be used,
 // then one barrier makes the whole slice visible.
-template <bool BF16, int BM, int BN, int WM, int WN, bool SWIGLU, int SA, int SB>
+template <bool BF16, int BM, int BN, int WM, int WN, bool SWIGLU, int SA, int SB, bool SAVE = false>
 __global__ __launch_bounds__(WM *WN * 64) void k_grouped_gemm(
     const u32x4 *__restrict__ A, int M, int kvec, const int32_t *__restrict__ offsets, int G,
     const u32x4 *__restrict__ B, int64_t b_expert_vec, int64_t b_up_vec, int ntiles, int N,
-    void *__restrict__ C, const int32_t *__restrict__ gather, int gk, int a_rows) {
+    void *__restrict__ C, const int32_t *__restrict__ gather, int gk, int a_rows,
+    void *__restrict__ GU) {
   constexpr int NW = WM * WN;
   constexpr int BR = SWIGLU ? 2 * BN : BN;      // weight rows per tile
   constexpr int NWA = NW / 2, NWB = NW - NWA;   // row-tile loaders, weight-tile loaders
@@ -388,6 +282,18 @@ __global__ __launch_bounds__(WM *WN * 64) void k_grouped_gemm(
               static_cast<uint16_t *>(C)[idx] = (uint16_t)f32_to_bf16_rne(val);
             else
               static_cast<float *>(C)[idx] = val;
+            if constexpr (SAVE && SWIGLU) {
+              // Pre-activations for the backward: gate at column col, up at
+              // N + col of a [M, 2 N] row.
+              const int64_t g = (int64_t)row * 2 * N + col;
+              if (BF16) {
+                static_cast<uint16_t *>(GU)[g] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+                static_cast<uint16_t *>(GU)[g + N] = (uint16_t)f32_to_bf16_rne(acc[i][FN + j][v]);
+              } else {
+                static_cast<float *>(GU)[g] = acc[i][j][v];
+                static_cast<float *>(GU)[g + N] = acc[i][FN + j][v];
+              }
+            }
           }
         }
       }
@@ -424,30 +330,6 @@ __global__ __launch_bounds__(WM *WN * 64) void k_grouped_gemm(
 // 1 for weight slice k + 1 at the end of its last memory phase of slice k --
 // both right before the barrier after which group 0 reads slice k + 1.  A
 // stage is refilled only after both groups' last reads of it.
-// Fourth word of a raw buffer resource on gfx9-class GPUs: 32-bit data
-// format, no swizzle, no stride; accesses at or past the byte count return 0.
-constexpr int kBufferFlags = 0x00020000;
-
-
-// One wave's 16-byte-per-lane buffer load straight into LDS: lane l's data
-// lands at lds + 16 l.  base/bytes describe the buffer; voff is the lane's
-// byte offset, soff a wave-uniform byte offset added to it.
-__device__ __forceinline__ void buffer_load_lds16(const void *base, uint32_t bytes, u32x4 *lds,
-                                                  uint32_t voff, uint32_t soff) {
-  const __amdgpu_buffer_rsrc_t res =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferFlags);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (__attribute__((address_space(3))) void *)lds, 16,
-                                           voff, soff, 0, 0);
-}
-
-// A workgroup barrier that is also a scheduling fence: without the fences the
-// compiler may move MFMAs (register-only instructions) across s_barrier, which
-// would pull one group's compute phase into the other group's window.
-__device__ __forceinline__ void phase_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 template <int CPR>
 __device__ __forceinline__ int swz_c(int r, int cc) {
@@ -457,11 +339,13 @@ __device__ __forceinline__ int swz_c(int r, int cc) {
     return r * 4 + (cc ^ ((r >> 2) & 3));   // 16 consecutive rows at one chunk: all banks once
 }
 
-template <bool BF16, int BM, int BR, int SA, int SB, int CPR, int DA, bool SWIGLU, bool SPLIT>
+template <bool BF16, int BM, int BR, int SA, int SB, int CPR, int DA, bool SWIGLU, bool SPLIT,
+          bool SAVE = false>
 __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     const u32x4 *__restrict__ A, int M, int kvec, const int32_t *__restrict__ offsets, int G,
     const u32x4 *__restrict__ B, int64_t b_expert_vec, int64_t b_up_vec, int ntiles, int N,
-    void *__restrict__ C, const int32_t *__restrict__ gather, int gk, int a_rows) {
+    void *__restrict__ C, const int32_t *__restrict__ gather, int gk, int a_rows,
+    void *__restrict__ GU) {
   constexpr int BN = SWIGLU ? BR / 2 : BR;       // output columns per tile
   constexpr int WNG = BR / 64, WMG = 4 / WNG;    // waves of a group across N and M
   constexpr int FM = (BM / 64 + WMG - 1) / WMG;  // row blocks per wave
@@ -691,6 +575,34 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     // each group of four rows, odd lanes rows t = 1, 3.
     const int col_l = lane & 31, row_l = 4 * (lane >> 5);
     const bool odd = lane & 1;
+    // Stores one 32 x 32 block (this lane's 16 values) at column col of the
+    // row-major [*, ld] output dst.
+    auto put = [&](void *dst, int64_t ld, int rblk, int col, const float(&val)[16]) {
+      if constexpr (BF16) {
+        uint32_t *out = static_cast<uint32_t *>(dst);
+        const int c0 = col & ~1;
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          // Rows t = v % 4 (even lanes keep it) and t + 1 (odd lanes).
+          const float mine = odd ? val[v + 1] : val[v];
+          const float give = odd ? val[v] : val[v + 1];
+          const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0xB1, 0xF, 0xF, false));
+          const float lo = odd ? got : mine, hi2 = odd ? mine : got;   // columns c0, c0 + 1
+          const int row = rblk + 8 * (v >> 2) + row_l + (v & 3) + (odd ? 1 : 0);
+          if (row < hi) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 pk = {(__bf16)lo, (__bf16)hi2};
+            out[((int64_t)row * ld + c0) >> 1] = __builtin_bit_cast(uint32_t, pk);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = rblk + 8 * (v >> 2) + row_l + (v & 3);
+          if (row < hi) static_cast<float *>(dst)[(int64_t)row * ld + col] = val[v];
+        }
+      }
+    };
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       if (DYN && i >= live) continue;
@@ -701,29 +613,18 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
         float val[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) val[v] = SWIGLU ? silu(acc[i][0][v]) * acc[i][1][v] : acc[i][j][v];
-        if constexpr (BF16) {
-          uint32_t *out = static_cast<uint32_t *>(C);
-          const int c0 = col & ~1;
-#pragma unroll
-          for (int v = 0; v < 16; v += 2) {
-            // Rows t = v % 4 (even lanes keep it) and t + 1 (odd lanes).
-            const float mine = odd ? val[v + 1] : val[v];
-            const float give = odd ? val[v] : val[v + 1];
-            const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0xB1, 0xF, 0xF, false));
-            const float lo = odd ? got : mine, hi2 = odd ? mine : got;   // columns c0, c0 + 1
-            const int row = rblk + 8 * (v >> 2) + row_l + (v & 3) + (odd ? 1 : 0);
-            if (row < hi) {
-              typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-              const bf16x2 pk = {(__bf16)lo, (__bf16)hi2};
-              out[((int64_t)row * N + c0) >> 1] = __builtin_bit_cast(uint32_t, pk);
-            }
-          }
-        } else {
+        put(C, N, rblk, col, val);
+        if constexpr (SAVE && SWIGLU) {
+          // Pre-activations for the backward: gate at column col, up at
+          // N + col of a [M, 2 N] row.
+          float g[16], u[16];
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int row = rblk + 8 * (v >> 2) + row_l + (v & 3);
-            if (row < hi) static_cast<float *>(C)[(int64_t)row * N + col] = val[v];
+            g[v] = acc[i][0][v];
+            u[v] = acc[i][1][v];
           }
+          put(GU, 2 * (int64_t)N, rblk, col, g);
+          put(GU, 2 * (int64_t)N, rblk, N + col, u);
         }
       }
     }
@@ -753,37 +654,6 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
   }
 }
 
-// Compute units of the current device (cached per device id).
-inline int device_cus() {
-  static int cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
-// Persistent grid: resident workgroups (CUs x blocks per CU), no more than
-// there can be tiles, rounded to a multiple of the XCD count.  per_cu caches
-// the occupancy query of one kernel instantiation.
-inline int persistent_grid(const void *kernel, int threads, int &per_cu, int64_t max_tiles) {
-  if (per_cu == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1)
-      n = 1;
-    per_cu = n;
-  }
-  int64_t g = (int64_t)device_cus() * per_cu;
-  const int64_t cap = (max_tiles + kXcds - 1) / kXcds * kXcds;
-  if (g > cap) g = cap;
-  g = g / kXcds * kXcds;
-  return (int)(g < kXcds ? kXcds : g);
-}
-
 // One launch of the grouped GEMM with tile shape Cfg.
 template <int BM_, int BN_, int WM_, int WN_, int SA_, int SB_>
 struct TileCfg {
@@ -802,10 +672,11 @@ struct PpCfg {
 
 // gather (optional): packed row p of the product is row gather[p] / gk of a,
 // which then has a_rows rows.
-template <bool BF16, bool SWIGLU, typename Cfg>
+// gu (SAVE only): also store the gate and up pre-activations, [M, 2 N].
+template <bool BF16, bool SWIGLU, typename Cfg, bool SAVE = false>
 void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int G, const void *w,
                 void *out, hipStream_t stream, const int32_t *gather = nullptr, int gk = 1,
-                int a_rows = 0) {
+                int a_rows = 0, void *gu = nullptr) {
   const int elem = BF16 ? 2 : 4;
   const int kvec = K * elem / 16;
   // w13 is [G, 2, N, K] (gate rows, then up rows); w2 is [G, N, K].
@@ -816,22 +687,22 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
     const int ntiles = N / BN;
     const int64_t mtiles_max = (M + Cfg::BM - 1) / Cfg::BM + G;
     auto kern = k_grouped_gemm_pp<BF16, Cfg::BM, Cfg::BR, Cfg::SA, Cfg::SB, Cfg::CPR, Cfg::DA, SWIGLU,
-                                  Cfg::SPLIT>;
+                                  Cfg::SPLIT, SAVE>;
     static int per_cu = 0;
     const int grid = persistent_grid((const void *)kern, 512, per_cu, mtiles_max * ntiles);
     kern<<<dim3(grid), dim3(512), 0, stream>>>(static_cast<const u32x4 *>(a), M, kvec, offsets, G,
                                               static_cast<const u32x4 *>(w), b_expert, b_up,
-                                              ntiles, N, out, gather, gk, a_rows);
+                                              ntiles, N, out, gather, gk, a_rows, gu);
   } else {
     const int ntiles = N / Cfg::BN;
     const int64_t mtiles_max = (M + Cfg::BM - 1) / Cfg::BM + G;
-    auto kern = k_grouped_gemm<BF16, Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, SWIGLU, Cfg::SA, Cfg::SB>;
+    auto kern = k_grouped_gemm<BF16, Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, SWIGLU, Cfg::SA, Cfg::SB, SAVE>;
     static int per_cu = 0;
     const int threads = Cfg::WM * Cfg::WN * 64;
     const int grid = persistent_grid((const void *)kern, threads, per_cu, mtiles_max * ntiles);
     kern<<<dim3(grid), dim3(threads), 0, stream>>>(static_cast<const u32x4 *>(a), M, kvec, offsets,
                                                   G, static_cast<const u32x4 *>(w), b_expert,
-                                                  b_up, ntiles, N, out, gather, gk, a_rows);
+                                                  b_up, ntiles, N, out, gather, gk, a_rows, gu);
   }
 }
 
@@ -883,11 +754,21 @@ inline Family family_of(int M, int G, int d) {
   return per_expert <= 288 ? Family::Medium : Family::Large;
 }
 
-// GEMM1: gate/up + SwiGLU, K = d, N = ffn.
+// GEMM1: gate/up + SwiGLU, K = d, N = ffn.  With gu, the pre-activations
+// are stored too (the forward of a training step).
 template <bool BF16>
 void launch_gate_up(Family f, const void *a, int M, int d, int ffn, const int32_t *offsets, int G,
                     const void *w13, void *h, hipStream_t stream, const int32_t *gather = nullptr,
-                    int gk = 1, int a_rows = 0) {
+                    int gk = 1, int a_rows = 0, void *gu = nullptr) {
+  if (gu) {
+    if (f == Family::Small)
+      launch_one<BF16, true, G1Small, true>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows, gu);
+    else if (f == Family::Medium)
+      launch_one<BF16, true, G1Medium, true>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows, gu);
+    else
+      launch_one<BF16, true, G1Large, true>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows, gu);
+    return;
+  }
   if (f == Family::Small)
     launch_one<BF16, true, G1Small>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows);
   else if (f == Family::Medium)
@@ -963,6 +844,25 @@ extern "C" moe_status moe_grouped_gate_up_gather(const void *x, moe_dtype dt, in
     launch_gate_up<true>(f, x, M, d, ffn, offsets, G, w13, h, stream, order, k, T);
   else
     launch_gate_up<false>(f, x, M, d, ffn, offsets, G, w13, h, stream, order, k, T);
+  return launch_status();
+}
+
+extern "C" moe_status moe_grouped_gate_up_save(const void *x, moe_dtype dt, int T, int k, int M,
+                                               int d, int ffn, const int32_t *order,
+                                               const int32_t *offsets, int G, const void *w13,
+                                               void *h, void *gu, hipStream_t stream) {
+  if (T < 0 || k < 1 || M < 0) return MOE_ERR_INVALID_ARG;
+  const moe_status st = check_shape(dt, M, d, ffn, G);
+  if (st != MOE_OK || M == 0) return st;
+  const int64_t elem = dt == MOE_F32 ? 4 : 2;
+  if (order && (int64_t)T * d * elem >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  if (!x || !offsets || !w13 || !h || !gu) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w13) || !aligned16(h) || !aligned16(gu)) return MOE_ERR_INVALID_ARG;
+  const Family f = family_of(M, G, d);
+  if (dt == MOE_BF16)
+    launch_gate_up<true>(f, x, M, d, ffn, offsets, G, w13, h, stream, order, order ? k : 1, order ? T : M, gu);
+  else
+    launch_gate_up<false>(f, x, M, d, ffn, offsets, G, w13, h, stream, order, order ? k : 1, order ? T : M, gu);
   return launch_status();
 }
 

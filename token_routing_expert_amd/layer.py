@@ -10,8 +10,10 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (moe_grouped_down, moe_grouped_gate_up, moe_grouped_gate_up_gather,
-               moe_grouped_swiglu, moe_permute, moe_permute_workspace_bytes, moe_route_topk,
+from . import (MoeError, moe_combine_backward, moe_gate_backward, moe_grouped_down,
+               moe_grouped_down_backward, moe_grouped_gate_up, moe_grouped_gate_up_backward,
+               moe_grouped_gate_up_gather, moe_grouped_gate_up_save, moe_grouped_swiglu,
+               moe_grouped_weight_grad, moe_permute, moe_permute_workspace_bytes, moe_route_topk,
                moe_router_bias_update, moe_router_logits, moe_send_counts, moe_unpermute_combine)
 from .inputs import MoeConfig
 
@@ -66,13 +68,23 @@ class MoeLayer:
     selects on logits + bias (auxiliary-loss-free balancing); with
     bias_lr != 0 every forward ends with the bias update from that batch's
     per-expert counts, so the next forward routes with the new bias.
+
+    train=True keeps what the backward needs: the first product also stores
+    the pre-activations gu, and ``backward(dy)`` then returns the gradients
+    of the layer (bf16 only).  The backward is the forward's steps in
+    reverse ("Expert parallelism", section "How many bytes move"): the
+    combine's gradient goes out to the expert rows, through the two products
+    (input and weight gradients), and back into the tokens.
     """
 
     def __init__(self, cfg: MoeConfig, x, w13, w2, logits=None, sh_w13=None, sh_w2=None,
                  topk_ids=None, topk_w=None, device="cuda", fused_gather=False, w_router=None,
-                 bias=None, bias_lr=0.0, merge_shared=False):
+                 bias=None, bias_lr=0.0, merge_shared=False, train=False):
         import torch
         self.cfg = cfg
+        self.train = bool(train)
+        if self.train and w_router is not None:
+            raise MoeError("train=True with a router product: its backward is not built")
         self.fused_gather = fused_gather
         if merge_shared and not (fused_gather and cfg.shared):
             raise ValueError("merge_shared needs the fused-gather path and a shared expert")
@@ -146,6 +158,13 @@ class MoeLayer:
             self.y_sh = torch.empty((T, d), dtype=act, device=dev)
         else:
             self.y_sh = None
+        if self.train:
+            if act != torch.bfloat16:
+                raise MoeError("train=True needs bf16 activations and weights")
+            self.gu = torch.empty((self.h.shape[0], 2 * ffn), dtype=act, device=dev)
+            if cfg.shared and not self.merge_shared:
+                self.sh_gu = torch.empty((T, 2 * ffn), dtype=act, device=dev)
+        self._grads = None
 
     def router(self, stream=None):
         """The router product logits = x w_router^T (a no-op without w_router)."""
@@ -166,7 +185,7 @@ class MoeLayer:
                     rows=not self.fused_gather)
 
     def experts_routed(self, stream=None):
-        if self.fused_gather:
+        if self.fused_gather or self.train:
             self.gate_up(stream)
             self.down(stream)
         else:
@@ -175,7 +194,17 @@ class MoeLayer:
 
     def gate_up(self, stream=None):
         """The routed experts' first product alone (the same launch experts_routed makes)."""
-        if self.merge_shared:
+        if self.train:
+            if self.merge_shared:
+                moe_grouped_gate_up_save(self.x, self.offsets_all, self.w13_all, self.h, self.gu,
+                                         order=self.order_all, k=self.cfg.k, stream=stream)
+            elif self.fused_gather:
+                moe_grouped_gate_up_save(self.x, self.offsets, self.w13, self.h, self.gu,
+                                         order=self.order, k=self.cfg.k, stream=stream)
+            else:
+                moe_grouped_gate_up_save(self.x_perm, self.offsets, self.w13, self.h, self.gu,
+                                         stream=stream)
+        elif self.merge_shared:
             moe_grouped_gate_up_gather(self.x, self.order_all, self.cfg.k, self.offsets_all,
                                        self.w13_all, self.h, stream=stream)
         elif self.fused_gather:
@@ -195,8 +224,13 @@ class MoeLayer:
         """The shared expert's own launches (with merge_shared its rows are
         part of the routed launches and this does nothing)."""
         if self.cfg.shared and not self.merge_shared:
-            moe_grouped_swiglu(self.x, self.sh_offsets, self.sh_w13, self.sh_w2, self.sh_h,
-                               self.y_sh, stream=stream)
+            if self.train:
+                moe_grouped_gate_up_save(self.x, self.sh_offsets, self.sh_w13, self.sh_h,
+                                         self.sh_gu, stream=stream)
+                moe_grouped_down(self.sh_h, self.sh_offsets, self.sh_w2, self.y_sh, stream=stream)
+            else:
+                moe_grouped_swiglu(self.x, self.sh_offsets, self.sh_w13, self.sh_w2, self.sh_h,
+                                   self.y_sh, stream=stream)
 
     def experts(self, stream=None):
         self.experts_routed(stream)
@@ -219,3 +253,97 @@ class MoeLayer:
         self.combine(stream)
         self.bias_update(stream)
         return self.y
+
+    # ------------------------------------------------------------------
+    # Backward (train=True)
+    # ------------------------------------------------------------------
+
+    def _grad_buffers(self):
+        """Every buffer of the backward, allocated on its first call."""
+        if self._grads is not None:
+            return self._grads
+        import torch
+        c, dev, act = self.cfg, self.device, self.x.dtype
+        T, k, E, d, ffn = c.T, c.k, c.E, c.d, c.ffn
+        M = T * k
+        R = self.h.shape[0]             # M, or M + T with the shared expert merged
+        G = E + 1 if self.merge_shared else E
+        b = {
+            "dy_perm": torch.empty((R, d), dtype=act, device=dev),
+            "dgu": torch.empty((R, 2 * ffn), dtype=act, device=dev),
+            "dx_perm": torch.empty((R, d), dtype=act, device=dev),
+            "dx": torch.empty((T, d), dtype=act, device=dev),
+            "dw13": torch.empty((G, 2, ffn, d), dtype=act, device=dev),
+            "dw2": torch.empty((G, d, ffn), dtype=act, device=dev),
+        }
+        if c.gating != "given":
+            b["dgate"] = torch.empty((T, k), dtype=torch.float32, device=dev)
+            b["dlogits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+        if c.shared and not self.merge_shared:
+            b["sh_dgu"] = torch.empty((T, 2 * ffn), dtype=act, device=dev)
+            b["dx_sh"] = torch.empty((T, d), dtype=act, device=dev)
+            b["dsh_w13"] = torch.empty((1, 2, ffn, d), dtype=act, device=dev)
+            b["dsh_w2"] = torch.empty((1, d, ffn), dtype=act, device=dev)
+        self._grads = b
+        return b
+
+    def backward(self, dy, stream=None):
+        """Gradients of the layer at its last forward, for the output gradient
+        dy [T, d].  Returns a dict of device tensors: dx, dw13, dw2, and when
+        present dgate and dlogits (through the gates), dsh_w13, dsh_w2 (shared
+        expert).
+        The buffers are reused by the next call."""
+        if not self.train:
+            raise MoeError("backward() needs a layer built with train=True")
+        c = self.cfg
+        b = self._grad_buffers()
+        M = c.T * c.k
+        merged = self.merge_shared
+        dy_perm = b["dy_perm"][:M] if merged else b["dy_perm"]
+        # 1. Combine's backward: the gradient goes out to the expert rows.
+        moe_combine_backward(dy, self.inv, self.topk_w, self.y_perm if "dgate" in b else None,
+                             dy_perm, b.get("dgate"), b["dy_perm"][M:] if merged else None,
+                             stream=stream, want_dgate="dgate" in b)
+        offsets = self.offsets_all if merged else self.offsets
+        w13 = self.w13_all if merged else self.w13
+        w2 = self.w2_all if merged else self.w2
+        order = self.order_all if merged else self.order
+        # 2. Second product and SwiGLU backward, 3. first product to the rows.
+        moe_grouped_down_backward(b["dy_perm"], offsets, w2, self.gu, b["dgu"], stream=stream)
+        moe_grouped_gate_up_backward(b["dgu"], offsets, w13, b["dx_perm"], stream=stream)
+        # 4. Weight gradients of both products.
+        moe_grouped_weight_grad(b["dy_perm"], self.h, offsets, b["dw2"], stream=stream)
+        if self.x_perm is not None:
+            moe_grouped_weight_grad(b["dgu"], self.x_perm, offsets, b["dw13"], stream=stream)
+        else:
+            moe_grouped_weight_grad(b["dgu"], self.x, offsets, b["dw13"], b_order=order, b_k=c.k,
+                                    stream=stream)
+        dx_sh = None
+        if c.shared and not merged:
+            moe_grouped_down_backward(dy, self.sh_offsets, self.sh_w2, self.sh_gu, b["sh_dgu"],
+                                      stream=stream)
+            dx_sh = moe_grouped_gate_up_backward(b["sh_dgu"], self.sh_offsets, self.sh_w13,
+                                                 b["dx_sh"], stream=stream)
+            moe_grouped_weight_grad(dy, self.sh_h, self.sh_offsets, b["dsh_w2"], stream=stream)
+            moe_grouped_weight_grad(b["sh_dgu"], self.x, self.sh_offsets, b["dsh_w13"],
+                                    stream=stream)
+        elif merged:
+            dx_sh = b["dx_perm"][M:]
+        # 5. The dispatch's gradient combined back into the tokens.
+        moe_unpermute_combine(b["dx_perm"][:M] if merged else b["dx_perm"], self.inv, None,
+                              dx_sh, b["dx"], stream=stream, k=c.k)
+        out = {"dx": b["dx"]}
+        if merged:
+            out.update(dw13=b["dw13"][:c.E], dw2=b["dw2"][:c.E], dsh_w13=b["dw13"][c.E:],
+                       dsh_w2=b["dw2"][c.E:])
+        else:
+            out.update(dw13=b["dw13"], dw2=b["dw2"])
+            if c.shared:
+                out.update(dsh_w13=b["dsh_w13"], dsh_w2=b["dsh_w2"])
+        # 6. The gates' backward to the logits.
+        if "dgate" in b:
+            moe_gate_backward(self.logits, self.topk_ids, self.topk_w, b["dgate"], c.gating,
+                              c.renormalize, b["dlogits"], stream=stream)
+            out["dlogits"] = b["dlogits"]
+            out["dgate"] = b["dgate"]
+        return out
