@@ -169,6 +169,166 @@ def cpu_baseline(cfg, data, budget_s=15.0, max_tokens=2048):
     }
 
 
+TRAIN_METRIC = ("MoE-layer fwd+bwd tokens/s at DSV3 shape, 1 GPU (training step: forward keeping "
+                "pre-activations, backward to dx, dW and dlogits)")
+
+
+def cpu_baseline_train(cfg, data, dy, budget_s=20.0):
+    """The oracle's forward and backward, untuned, on the host cores: the
+    per-token part (expert outputs, the combine's and the experts' input
+    gradients, the gate gradients) on seeded tokens, and the weight gradients
+    on rows of one expert; per-token costs extrapolated to the full batch."""
+    import numpy as np
+
+    import oracle
+    from token_routing_expert_amd import inputs
+
+    x, w13, w2, logits, sh, ids_in, w_in = data
+    t0 = time.perf_counter()
+    if cfg.gating == "given":
+        ids, w = ids_in, w_in
+    else:
+        ids, w = oracle.route(logits, cfg.k, cfg.gating, cfg.renormalize, cfg.n_groups,
+                              cfg.topk_groups)
+    _, offsets, order, _ = oracle.permute_index(ids, cfg.E)
+    t_index = time.perf_counter() - t0
+    k, d = cfg.k, cfg.d
+    sample = inputs.sample_tokens(cfg, 256)
+    done, t_tok = 0, 0.0
+    while done < len(sample) and t_tok < budget_s / 2:
+        t = sample[done:done + 4]
+        t1 = time.perf_counter()
+        rows = np.repeat(np.ascontiguousarray(x[t]), k, axis=0)
+        e = ids[t].reshape(-1)
+        y_rows = oracle.expert_swiglu_rows(rows, e, w13, w2)
+        ident = np.arange(len(t) * k, dtype=np.int32)
+        dy_rows, dgate = oracle.combine_backward(dy[t], ident, w[t], y_rows)
+        oracle.expert_swiglu_backward_rows(rows, e, w13, w2, dy_rows, want_dw=False)
+        if logits is not None:
+            oracle.gate_backward(logits[t], ids[t], dgate, cfg.gating, cfg.renormalize)
+        t_tok += time.perf_counter() - t1
+        done += len(t)
+    # Weight gradients: rows of the first non-empty expert, that expert alone.
+    e0 = int(np.flatnonzero(np.diff(offsets))[0])
+    seg = order[offsets[e0]:offsets[e0 + 1]][:64]
+    rows = np.ascontiguousarray(x[seg // k])
+    dy_rows = oracle.bf16_bits_to_f64(dy[seg // k]) if dy.dtype == np.uint16 else dy[seg // k]
+    t1 = time.perf_counter()
+    oracle.expert_swiglu_backward_rows(rows, np.zeros(len(seg), np.int32), w13[e0:e0 + 1],
+                                       w2[e0:e0 + 1], dy_rows, want_dx=False)
+    t_w = time.perf_counter() - t1
+    per_token = t_index / cfg.T + t_tok / done + k * t_w / len(seg)
+    return {
+        "value": 1.0 / per_token,
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"route and permute on all {cfg.T} tokens ({t_index:.2f} s); forward, combine, "
+                   f"input and gate gradients on {done} seeded tokens ({t_tok:.2f} s); weight "
+                   f"gradients of expert {e0} over {len(seg)} of its rows ({t_w:.2f} s); per-token "
+                   f"costs extrapolated to {cfg.T} tokens (shared expert not included)"),
+    }
+
+
+def run_train(args, cfg, layer, data, stream):
+    """--train: time forward + backward steps; one JSON line."""
+    import numpy as np
+    import torch
+
+    from token_routing_expert_amd import inputs
+    from token_routing_expert_amd.layer import to_device, to_host
+
+    dy_host = inputs.f32_to_bf16_bits(
+        np.random.default_rng(2000 + cfg.index).standard_normal((cfg.T, cfg.d)).astype(np.float32))
+    dy = to_device(dy_host)
+    fwd = ["route", "permute", "gate_up", "down", "experts_shared", "combine"]
+    stages = [("fwd", n) for n in fwd] + [("bwd", n) for n in layer.BACKWARD_STAGES]
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        for i, (kind, name) in enumerate(stages):
+            if kind == "fwd":
+                getattr(layer, name)()
+            else:
+                getattr(layer, name)(dy)
+            if evs is not None:
+                evs[i + 1].record(stream)
+
+    log(f"train warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K)]
+    log(f"timing {K} training steps")
+    t_start = time.perf_counter()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t_start) * 1e3 / K
+    stage_ms = {name: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K
+                for j, (_, name) in enumerate(stages)}
+    M = cfg.T * cfg.k
+    d, ffn, s = cfg.d, cfg.ffn, cfg.elem_bytes
+    f_gu, f_dn, _ = expert_flops(cfg)
+    flops = {"gate_up": f_gu, "down": f_dn, "bwd_down": f_dn, "bwd_gate_up": f_gu,
+             "bwd_wgrad_down": f_dn, "bwd_wgrad_gate_up": f_gu}
+    peak = PEAK_MFMA[cfg.dtype]
+    stage_info = {}
+    for _, name in stages:
+        info = {"ms": round(stage_ms[name], 4)}
+        if name in flops:
+            rate = flops[name] / (stage_ms[name] * 1e-3)
+            info.update(flops=flops[name], TFLOPs=round(rate / 1e12, 1),
+                        mfma_frac=round(rate / peak, 4))
+        stage_info[name] = info
+    # Dominant backward kernel: the first product's weight gradient (one
+    # launch, 4 M d ffn FLOPs): dgu and the rows read once, every expert's
+    # dW13 written once.
+    gather = layer.x_perm is None
+    wg_ms = stage_ms["bwd_wgrad_gate_up"]
+    wg_bytes = (M * 2 * ffn * s + (cfg.T * d * s + 4 * M if gather else M * d * s)
+                + cfg.E * 2 * ffn * d * s)
+    intensity = f_gu / wg_bytes
+    ridge = peak / PEAK_HBM
+    flop_rate, byte_rate = f_gu / (wg_ms * 1e-3), wg_bytes / (wg_ms * 1e-3)
+    if intensity < ridge:
+        roof = {"bound": "hbm", "achieved": round(byte_rate / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": round(byte_rate / PEAK_HBM, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flop_rate / 1e12, 2), "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": round(flop_rate / peak, 4)}
+    fwd_ms = sum(stage_ms[n] for n in fwd)
+    bwd_ms = sum(stage_ms[n] for n in layer.BACKWARD_STAGES)
+    result = {
+        "metric": TRAIN_METRIC,
+        "value": cfg.T / (ms_step * 1e-3),
+        "unit": "tokens/s" if cfg.gating != "given" else "rows/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded numpy draws; random-init weights of the stated shapes)",
+        "config": {"workload": cfg.name, "T": cfg.T, "E": cfg.E, "k": cfg.k, "d": d, "ffn": ffn,
+                   "gating": cfg.gating, "shared_experts": int(cfg.shared), "path": args.path,
+                   "train": True},
+        "roofline": {"kernel": "moe_grouped_weight_grad: dW13 = dgu^T x rows (one launch)", **roof,
+                     "traffic": None, "algorithmic_bytes": wg_bytes, "algorithmic_flops": f_gu,
+                     "intensity_flop_per_byte": round(intensity, 1),
+                     "ridge_flop_per_byte": round(ridge, 1),
+                     "mfma_frac": round(flop_rate / peak, 4),
+                     "hbm_frac": round(byte_rate / PEAK_HBM, 4), "launch_ms": round(wg_ms, 4)},
+        "forward_ms": round(fwd_ms, 4), "backward_ms": round(bwd_ms, 4),
+        "backward_TFLOPs": round(2 * (f_gu + f_dn + (6 * cfg.T * d * ffn if cfg.shared else 0))
+                                 / (bwd_ms * 1e-3) / 1e12, 1),
+        "stages": stage_info,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle forward + backward)")
+        result["cpu_baseline"] = cpu_baseline_train(cfg, data, dy_host)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +344,9 @@ def main():
     ap.add_argument("--path", choices=("gather", "packed"), default="gather",
                     help="gather: the first expert product reads token rows through the "
                          "permutation; packed: the permute writes the packed copy X[order]")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step instead: the forward keeping the pre-activations, "
+                         "then the backward to dx, the weight gradients and dlogits (bf16 only)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -219,9 +382,13 @@ def main():
         wr_kw = dict(w_router=inputs.gen_router_weights(cfg),
                      bias=np.zeros(cfg.E, np.float32), bias_lr=args.bias_lr)
     layer = MoeLayer(cfg, x, w13, w2, logits=logits, sh_w13=sh[0], sh_w2=sh[1], **wr_kw,
-                     topk_ids=ids_in, topk_w=w_in, fused_gather=args.path == "gather")
+                     topk_ids=ids_in, topk_w=w_in, fused_gather=args.path == "gather",
+                     train=args.train)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    if args.train:
+        run_train(args, cfg, layer, (x, w13, w2, logits, sh, ids_in, w_in), stream)
+        return
 
     stages = ["route", "permute", "gate_up", "down", "experts_shared", "combine"]
     if router:

@@ -19,10 +19,10 @@
 // gfx950's transposing LDS read (ds_read_b64_tr_b16), which hands each lane
 // four K-consecutive values of one column.
 //
-// One kernel serves all three shapes: 4 waves, 128 x 128 output tiles, each
-// wave a 64 x 64 quarter (2 x 2 MFMA 32x32x16 blocks), K staged 64 at a
-// time through an S-stage ring filled by direct global-to-LDS buffer loads.
-// Accumulation is fp32; outputs are bf16, rounded to nearest even.
+// One kernel serves all three shapes: 2 WM waves, (64 WM) x 128 output
+// tiles, each wave a 64 x 64 part (2 x 2 MFMA 32x32x16 blocks), K staged 64
+// at a time through an S-stage ring filled by direct global-to-LDS buffer
+// loads.  Accumulation is fp32; outputs are bf16, rounded to nearest even.
 #include <type_traits>
 
 #include "common.hpp"
@@ -34,8 +34,8 @@ namespace {
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 128, kBN = 128, kKS = 64;   // tile rows, tile columns, K per slice
-constexpr int kThreads = 256;
+constexpr int kBN = 128;             // tile columns
+constexpr int kMaxG = 1024;          // experts per call (their offsets are staged in LDS)
 
 enum Mode { kDgradStore = 0, kDgradSwiglu = 1, kWgrad = 2 };
 
@@ -54,24 +54,34 @@ struct BwdParams {
 // K-contiguous tile (the dgrad's dY or dGU rows): 128 rows x 64 K = 8
 // chunks of 16 bytes per row, chunk cc of row r in slot cc ^ key(r) so an
 // operand read (32 rows at one chunk) spreads over all banks.
-__device__ __forceinline__ int kc_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int kc_slot(int r, int cc) { return r * 8 + (cc ^ kc_key(r)); }
+// With 64 K per slice a row is 8 chunks (128 bytes); with 32 K, 4 chunks
+// (64 bytes), and the key is (r / 4) % 4 so that 16 consecutive rows read at
+// one chunk cover all 16 bank positions of 256 bytes.
+template <int KS>
+__device__ __forceinline__ int kc_key(int r) {
+  if constexpr (KS == 64) return (r & 7) ^ ((r >> 3) & 1);
+  else return (r >> 2) & 3;
+}
+template <int KS>
+__device__ __forceinline__ int kc_slot(int r, int cc) { return r * (KS / 8) + (cc ^ kc_key<KS>(r)); }
 
-// Column-contiguous tile: 64 K-rows x 128 columns = 256 bytes per K-row,
-// four 64-byte segments (32 columns each).  Segment sg of K-row r is stored
-// at position sg ^ (r & 3): a transposing read takes 64 bytes from each of
-// four K-rows r .. r + 3 per half wave, which then land in four different
-// quarters of the 256-byte bank row.
+// Column-contiguous tile: 64 K-rows x W columns (W = 128 or 256), 2 W bytes
+// per K-row in 64-byte segments of 32 columns.  Segment sg of K-row r is
+// stored at position sg ^ (r & 3): a transposing read takes 64 bytes from
+// each of four K-rows r .. r + 3 per half wave, which then land in four
+// different quarters of the 256-byte bank row.
+template <int W>
 __device__ __forceinline__ int cc_byte(int r, int sg, int byte_in_seg) {
-  return r * 256 + ((sg ^ (r & 3)) << 6) + byte_in_seg;
+  return r * (2 * W) + ((sg ^ (r & 3)) << 6) + byte_in_seg;
 }
 
 // ---- operand fragments ---------------------------------------------------
 
 // MFMA 32x32x16 operand of 32 rows (row block rb) at k-group q from a
 // K-contiguous tile: lane l gives row l % 32, K 8 (l / 32) .. + 7.
+template <int KS>
 __device__ __forceinline__ u32x4 frag_kc(const u32x4 *stage, int rb, int q, int lane) {
-  return stage[kc_slot(rb * 32 + (lane & 31), 2 * q + (lane >> 5))];
+  return stage[kc_slot<KS>(rb * 32 + (lane & 31), 2 * q + (lane >> 5))];
 }
 
 // The same operand for 32 columns (column block cb) from a column-contiguous
@@ -81,12 +91,13 @@ __device__ __forceinline__ u32x4 frag_kc(const u32x4 *stage, int rb, int q, int 
 // 16 q + 8 (s / 32) + 4 h + (s % 16) / 4 at columns 16 ((s / 16) % 2) +
 // 4 (s % 4) of the block, and lane l receives column l % 32 at K-rows
 // 8 (l / 32) + 4 h .. + 3: half h = 0 gives the lane's K 0..3, h = 1 K 4..7.
+template <int W>
 __device__ __forceinline__ u32x4 frag_tr(const char *stage, int cb, int q, int lane) {
   u32x4 out;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int r = 16 * q + 8 * (lane >> 5) + 4 * h + ((lane & 15) >> 2);
-    const int byte = cc_byte(r, cb, (((lane >> 4) & 1) << 5) + ((lane & 3) << 3));
+    const int byte = cc_byte<W>(r, cb, (((lane >> 4) & 1) << 5) + ((lane & 3) << 3));
     const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) v4i16 *)(stage + byte));
     const u32x2 w = __builtin_bit_cast(u32x2, v);
@@ -105,191 +116,222 @@ __device__ __forceinline__ float bf16_at(const uint16_t *p, int64_t i) {
   return __uint_as_float((uint32_t)p[i] << 16);
 }
 
-template <int MODE, int S>
-__global__ __launch_bounds__(kThreads) void k_grouped_gemm_bwd(const BwdParams p) {
+// One output tile.
+struct TileB {
+  int e, lo, hi, m0, n0, KT;
+};
+
+// A column-contiguous stage of W columns (W = 128 or 256) is filled by
+// 1 KB DMA groups of 512 / W K-rows; lane l of group g fills K-row
+// g (512 / W) + l / (W / 8) at physical chunk l % (W / 8), which holds the
+// 16 bytes at this column of the tile (segment swizzle of cc_byte).
+template <int W>
+__device__ __forceinline__ void cc_lane(int g, int lane, int &krow, int &col) {
+  constexpr int LPR = W / 8;   // lanes per K-row
+  krow = g * (512 / W) + lane / LPR;
+  const int pc = lane % LPR;
+  col = (((pc >> 2) ^ (krow & 3)) << 5) + (pc & 3) * 8;
+}
+
+// The kernel is persistent: a workgroup walks its band of tiles and its
+// S-stage ring streams K slices continuously across tile boundaries, so the
+// next tile's first slices load while this tile finishes and stores.  The
+// expert offsets are copied to LDS first, so the tile lookups in the stream
+// read LDS and never wait behind loads in flight.
+template <int MODE, int WM, int S, int kKS, bool GATHER>
+__global__ __launch_bounds__(WM * 128) void k_grouped_gemm_bwd(const BwdParams p) {
   constexpr bool WGRAD = MODE == kWgrad;
-  constexpr int STAGE = kBM * kKS * 2 + kKS * kBN * 2;   // bytes: row operand, column operand
+  constexpr int NW = 2 * WM, BM = 64 * WM;
+  constexpr int A_BYTES = BM * kKS * 2, B_BYTES = kKS * kBN * 2, STAGE = A_BYTES + B_BYTES;
+  constexpr int A_PW = A_BYTES / 1024 / NW, B_PW = B_BYTES / 1024 / NW;   // DMA groups per wave
+  constexpr int LPS = A_PW + B_PW;                                       // loads per slice per wave
+  static_assert(A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES, "DMA split");
   __shared__ __attribute__((aligned(16))) char smem[S * STAGE];
+  __shared__ int32_t s_off[kMaxG + 1];
 
   const int lane = lane_id();
   const int wave = uniform(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  for (int i = threadIdx.x; i <= p.G; i += NW * 64) s_off[i] = clamp_row(p.offsets[i], p.R);
+  __syncthreads();
 
-  int e, lo, hi, m0, n0;
   const int ntn = p.N / kBN;
+  const int mtn = WGRAD ? p.Mdim / BM : 1;
   // XCD x (workgroups x, x + 8, ...) takes a contiguous band of tiles, so
-  // tiles that share operands run on one L2.  wgrad: the grid has a
-  // workgroup per tile; dgrad: a persistent grid walks the band.
-  int cur_e = 0, cur_base = 0;
+  // tiles that share operands run on one L2 at the same time.
+  const int64_t total = WGRAD ? (int64_t)p.G * mtn * ntn : (int64_t)count_tiles<BM>(s_off, p.G, p.R, ntn);
   const int xcd = blockIdx.x % kXcds, nj = gridDim.x / kXcds;
-  const int64_t total = WGRAD ? (int64_t)p.G * (p.Mdim / kBM) * ntn
-                              : (int64_t)count_tiles<kBM>(p.offsets, p.G, p.R, ntn);
-  int L = (int)(total * xcd / kXcds) + (int)(blockIdx.x / kXcds);
+  const int L0 = (int)(total * xcd / kXcds) + (int)(blockIdx.x / kXcds);
   const int band_end = (int)(total * (xcd + 1) / kXcds);
 
-  for (; L < band_end; L += nj) {
+  auto tile_at = [&](int L, int &e0, int &base) {
+    TileB t;
     if constexpr (WGRAD) {
-      const int per_e = (p.Mdim / kBM) * ntn;
-      e = L / per_e;
-      const int rem = L - e * per_e;
-      m0 = (rem / ntn) * kBM;
-      n0 = (rem % ntn) * kBN;
-      lo = clamp_row(p.offsets[e], p.R);
-      hi = clamp_row(p.offsets[e + 1], p.R);
-      if (hi < lo) hi = lo;
+      const int per_e = mtn * ntn;
+      t.e = L / per_e;
+      const int rem = L - t.e * per_e;
+      t.m0 = (rem / ntn) * BM;
+      t.n0 = (rem % ntn) * kBN;
+      t.lo = s_off[t.e];
+      t.hi = s_off[t.e + 1] > t.lo ? s_off[t.e + 1] : t.lo;
+      t.KT = (t.hi - t.lo + kKS - 1) / kKS;
     } else {
-      Tile t;
-      find_tile<kBM>(p.offsets, p.G, p.R, ntn, L, t, cur_e, cur_base);
-      e = t.expert;
-      lo = t.lo;
-      hi = t.hi;
-      m0 = t.m0;
-      n0 = t.n_tile * kBN;
+      Tile x;
+      find_tile<BM>(s_off, p.G, p.R, ntn, L, x, e0, base);
+      t.e = x.expert;
+      t.lo = x.lo;
+      t.hi = x.hi;
+      t.m0 = x.m0;
+      t.n0 = x.n_tile * kBN;
+      t.KT = p.K / kKS;
     }
-    const int KT = WGRAD ? (hi - lo + kKS - 1) / kKS : p.K / kKS;
+    return t;
+  };
 
-    // ---- loads: every wave fills 4 of the 16 DMA groups of each operand --
-    // Row operand.  dgrad: 16 groups of 8 rows x 128 bytes (K-contiguous),
-    // rows past the segment end re-read its last row (never stored).  wgrad:
-    // 16 groups of 4 K-rows x 256 bytes of A[lo + k, m0 ..], zero past the
-    // segment end (the buffer ends there), which zeroes their products.
-    // Column operand: 16 groups of 4 K-rows x 256 bytes.  dgrad: rows k of
-    // expert e's [K, N] matrix; wgrad: B rows of the segment (clamped to it).
-    const int kc_row = lane >> 3, kc_chunk = lane & 7;          // K-contiguous DMA lane map
-    const int cc_row = lane >> 4, cc_seg = (lane >> 2) & 3, cc_w = lane & 3;
-    const int cc_col = ((cc_seg ^ cc_row) << 5) + cc_w * 8;     // column of this lane's 16 bytes
+  // ---- issue cursor: the next K slice to load -----------------------------
+  int Li = L0, kti = 0, issued = 0, ie0 = 0, ibase = 0;
+  TileB ti{};
+  if (Li < band_end) ti = tile_at(Li, ie0, ibase);
+  auto settle = [&]() {   // skip to the next tile with a slice left
+    while (Li < band_end && kti >= ti.KT) {
+      Li += nj;
+      kti = 0;
+      if (Li < band_end) ti = tile_at(Li, ie0, ibase);
+    }
+  };
+  settle();
 
-    // (The buffer's bounds check leaves out the scalar offset, so the wgrad
-    // row operand keeps its whole offset, slice included, per lane.)
-    const char *a_base;
-    uint32_t a_bytes;
-    uint32_t a_off[4];
-    if constexpr (WGRAD) {
-      a_base = static_cast<const char *>(p.a) + (int64_t)lo * p.Mdim * 2;
-      a_bytes = (uint32_t)((int64_t)(hi - lo) * p.Mdim * 2);
+  // Row operand.  dgrad: 8 rows x 128 bytes (K-contiguous) per group, rows
+  // past the segment end re-read its last row (never stored).  wgrad: A's
+  // K-rows lo + k at columns m0 .., zero past the segment end (the buffer
+  // ends there, and its bounds check covers the per-lane offset only, so the
+  // whole offset is per lane), which zeroes their products.
+  // Column operand: expert e's [K, N] matrix (dgrad) or B's rows of the
+  // segment, clamped to it (wgrad).
+  auto issue = [&]() {
+    char *stage = smem + (issued % S) * STAGE;
+    u32x4 *sa = reinterpret_cast<u32x4 *>(stage);
+    u32x4 *sb = reinterpret_cast<u32x4 *>(stage + A_BYTES);
+    const int kt = kti;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        a_off[r] = (uint32_t)(((wave + 4 * r) * 4 + cc_row) * p.Mdim + m0 + cc_col) * 2u;
-    } else {
-      a_base = static_cast<const char *>(p.a);
-      a_bytes = (uint32_t)((int64_t)p.R * p.K * 2);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int g = wave + 4 * r;
-        int row = m0 + g * 8 + kc_row;
-        row = row < hi ? row : hi - 1;
-        const uint32_t key = kc_row ^ (g & 1);   // kc_key(8 g + kc_row)
-        a_off[r] = (uint32_t)row * (uint32_t)p.K * 2u + (((uint32_t)kc_chunk ^ key) << 4);
+    for (int r = 0; r < A_PW; ++r) {
+      const int g = wave + NW * r;
+      if constexpr (WGRAD) {
+        int krow, col;
+        cc_lane<BM>(g, lane, krow, col);
+        const uint32_t off = ((uint32_t)(kt * kKS + krow) * (uint32_t)p.Mdim + (uint32_t)(ti.m0 + col)) * 2u;
+        buffer_load_lds16(static_cast<const char *>(p.a) + (int64_t)ti.lo * p.Mdim * 2,
+                          (uint32_t)((int64_t)(ti.hi - ti.lo) * p.Mdim * 2), sa + g * 64, off, 0);
+      } else {
+        // One group: 1024 / (2 kKS) rows; lane l fills row l / CPR of it at
+        // slot l % CPR, which holds chunk (l % CPR) ^ key(row).
+        constexpr int CPR = kKS / 8, RPG = 64 / CPR;
+        const int lr = g * RPG + lane / CPR;
+        int row = ti.m0 + lr;
+        row = row < ti.hi ? row : ti.hi - 1;
+        const uint32_t chunk = (uint32_t)(lane % CPR) ^ (uint32_t)kc_key<kKS>(lr);
+        const uint32_t off = (uint32_t)row * (uint32_t)p.K * 2u + (chunk << 4);
+        buffer_load_lds16(p.a, (uint32_t)((int64_t)p.R * p.K * 2), sa + g * 64, off,
+                          (uint32_t)kt * kKS * 2u);
       }
     }
-    const char *b_base;
-    uint32_t b_bytes;
-    if constexpr (WGRAD) {
-      b_base = static_cast<const char *>(p.b);
-      b_bytes = (uint32_t)((int64_t)p.b_rows * p.N * 2);
-    } else {
-      b_base = static_cast<const char *>(p.b) + (int64_t)e * p.K * p.N * 2;
-      b_bytes = (uint32_t)((int64_t)p.K * p.N * 2);
-    }
-    auto issue = [&](int kt) {
-      char *stage = smem + (kt % S) * STAGE;
-      u32x4 *sa = reinterpret_cast<u32x4 *>(stage);
-      u32x4 *sb = reinterpret_cast<u32x4 *>(stage + kBM * kKS * 2);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int g = wave + 4 * r;
-        if constexpr (WGRAD)
-          buffer_load_lds16(a_base, a_bytes, sa + g * 64, a_off[r] + (uint32_t)kt * kKS * (uint32_t)p.Mdim * 2u, 0);
-        else
-          buffer_load_lds16(a_base, a_bytes, sa + g * 64, a_off[r], (uint32_t)kt * kKS * 2u);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int g = wave + 4 * r;
-        const int krow = kt * kKS + g * 4 + cc_row;
-        uint32_t off;
-        if constexpr (WGRAD) {
-          int row = lo + krow;
-          row = row < hi ? row : hi - 1;
-          uint32_t src = (uint32_t)row;
-          if (p.gather) {
-            src = (uint32_t)p.gather[row] / (uint32_t)p.gk;
-            src = src < (uint32_t)p.b_rows ? src : (uint32_t)p.b_rows - 1u;
-          }
-          off = (src * (uint32_t)p.N + (uint32_t)(n0 + cc_col)) * 2u;
-        } else {
-          off = ((uint32_t)krow * (uint32_t)p.N + (uint32_t)(n0 + cc_col)) * 2u;
+    for (int r = 0; r < B_PW; ++r) {
+      const int g = wave + NW * r;
+      int krow, col;
+      cc_lane<kBN>(g, lane, krow, col);
+      if constexpr (WGRAD) {
+        int row = ti.lo + kt * kKS + krow;
+        row = row < ti.hi ? row : ti.hi - 1;
+        uint32_t src = (uint32_t)row;
+        if constexpr (GATHER) {
+          src = (uint32_t)p.gather[row] / (uint32_t)p.gk;
+          src = src < (uint32_t)p.b_rows ? src : (uint32_t)p.b_rows - 1u;
         }
-        buffer_load_lds16(b_base, b_bytes, sb + g * 64, off, 0);
+        buffer_load_lds16(p.b, (uint32_t)((int64_t)p.b_rows * p.N * 2), sb + g * 64,
+                          (src * (uint32_t)p.N + (uint32_t)(ti.n0 + col)) * 2u, 0);
+      } else {
+        buffer_load_lds16(static_cast<const char *>(p.b) + (int64_t)ti.e * p.K * p.N * 2,
+                          (uint32_t)((int64_t)p.K * p.N * 2), sb + g * 64,
+                          ((uint32_t)(kt * kKS + krow) * (uint32_t)p.N + (uint32_t)(ti.n0 + col)) * 2u, 0);
       }
-    };
+    }
+    ++issued;
+    ++kti;
+    settle();
+  };
 
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  // ---- consume cursor: the tile being computed ----------------------------
+  int Lc = L0, ktc = 0, consumed = 0, ce0 = 0, cbase = 0;
+  TileB tc{};
+  if (Lc < band_end) tc = tile_at(Lc, ce0, cbase);
 
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s)
-      if (s < KT) issue(s);
+  for (int s = 0; s < S - 1; ++s)
+    if (Li < band_end) issue();
 
-    for (int kt = 0; kt < KT; ++kt) {
-      // This wave's 8 loads of slice kt are done once no more than its loads
-      // of the later slices already issued remain in flight; then one
-      // barrier makes the slice visible and frees the stage slice
-      // kt + S - 1 reuses (read in step kt - 1).
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const bool odd = lane & 1;
+  const int row_l = 4 * (lane >> 5);
+  while (Lc < band_end) {
+    if (ktc < tc.KT) {
+      // This wave's loads of the slice are done once no more than its loads
+      // of the slices issued after it remain in flight; one barrier then
+      // makes the slice visible and frees the stage the next issue reuses
+      // (read in the previous step).
       asm volatile("" ::: "memory");
-      wait_vmcnt(((kt + S - 2 < KT - 1 ? kt + S - 2 : KT - 1) - kt) * 8);
+      wait_vmcnt((issued - consumed - 1) * LPS);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      const char *stage = smem + (kt % S) * STAGE;
+      const char *stage = smem + (consumed % S) * STAGE;
       const u32x4 *sa = reinterpret_cast<const u32x4 *>(stage);
-      const char *sa_bytes = stage;
-      const char *sb = stage + kBM * kKS * 2;
+      const char *sb = stage + A_BYTES;
       u32x4 fa[2][2], fb[2][2];
       auto fetch = [&](int q, int buf) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           if constexpr (WGRAD)
-            fa[buf][i] = frag_tr(sa_bytes, 2 * wm + i, q, lane);
+            fa[buf][i] = frag_tr<BM>(stage, 2 * wm + i, q, lane);
           else
-            fa[buf][i] = frag_kc(sa, 2 * wm + i, q, lane);
-          fb[buf][i] = frag_tr(sb, 2 * wn + i, q, lane);
+            fa[buf][i] = frag_kc<kKS>(sa, 2 * wm + i, q, lane);
+          fb[buf][i] = frag_tr<kBN>(sb, 2 * wn + i, q, lane);
         }
       };
+      constexpr int NQ = kKS / 16;   // k-groups per slice
       fetch(0, 0);
-      if (kt + S - 1 < KT) issue(kt + S - 1);
+      if (Li < band_end) issue();
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (q < 3) fetch(q + 1, (q + 1) & 1);
+      for (int q = 0; q < NQ; ++q) {
+        if (q < NQ - 1) fetch(q + 1, (q + 1) & 1);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j) mma(fa[q & 1][i], fb[q & 1][j], acc[i][j]);
       }
+      ++consumed;
+      ++ktc;
     }
-    // Every wave is done with LDS before the next tile's loads land there.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    if (ktc < tc.KT) continue;
 
-    // ---- epilogue ----------------------------------------------------
+    // ---- epilogue of tile tc ----------------------------------------------
     // MFMA 32x32 output layout: lane l holds column l % 32 and, in register
     // v, row 8 (v / 4) + 4 (l / 32) + v % 4.  Adjacent lanes trade values so
     // each holds two adjacent columns of one row (even lanes rows v % 4 =
     // 0, 2, odd lanes 1, 3) and moves them with one 4-byte access.
-    const bool odd = lane & 1;
-    const int row_l = 4 * (lane >> 5);
-    const int row_hi = WGRAD ? m0 + kBM : hi;
+    const int row_hi = WGRAD ? tc.m0 + BM : tc.hi;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int rblk = m0 + (2 * wm + i) * 32;
+      const int rblk = tc.m0 + (2 * wm + i) * 32;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int c0 = (n0 + (2 * wn + j) * 32 + (lane & 31)) & ~1;
+        const int c0 = (tc.n0 + (2 * wn + j) * 32 + (lane & 31)) & ~1;
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
           const float mine = odd ? acc[i][j][v + 1] : acc[i][j][v];
@@ -313,36 +355,48 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gemm_bwd(const BwdParams p
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
               const float s = 1.0f / (1.0f + __expf(-g[c]));
-              const float silu_g = g[c] * s;
               dg[c] = dh[c] * u[c] * (s * (1.0f + g[c] * (1.0f - s)));
-              du[c] = dh[c] * silu_g;
+              du[c] = dh[c] * (g[c] * s);
             }
             uint16_t *out = static_cast<uint16_t *>(p.c);
             *reinterpret_cast<uint32_t *>(out + base) = pack_bf16x2(dg[0], dg[1]);
             *reinterpret_cast<uint32_t *>(out + base + p.N) = pack_bf16x2(du[0], du[1]);
           } else {
-            const int64_t base = WGRAD ? ((int64_t)e * p.Mdim + row) * p.N + c0 : (int64_t)row * p.N + c0;
+            const int64_t base =
+                WGRAD ? ((int64_t)tc.e * p.Mdim + row) * p.N + c0 : (int64_t)row * p.N + c0;
             *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(p.c) + base) = pack_bf16x2(x0, x1);
           }
         }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
       }
     }
+    Lc += nj;
+    ktc = 0;
+    if (Lc < band_end) tc = tile_at(Lc, ce0, cbase);
   }
 }
 
-constexpr int kStages = 2;
+#ifndef MOE_BWD_WM
+#define MOE_BWD_WM 2        // waves along M: 2 -> 128-row tiles, 4 -> 256-row tiles
+#endif
+#ifndef MOE_BWD_STAGES
+#define MOE_BWD_STAGES 2
+#endif
+#ifndef MOE_BWD_KS
+#define MOE_BWD_KS 64       // K per ring stage: 64 or 32
+#endif
+constexpr int kKS = MOE_BWD_KS;
 
-template <int MODE>
+constexpr int kTileM = 64 * MOE_BWD_WM;
+
+template <int MODE, bool GATHER = false>
 void launch(const BwdParams &prm, hipStream_t stream, int64_t tiles) {
-  auto kern = k_grouped_gemm_bwd<MODE, kStages>;
-  int grid;
-  if (MODE == kWgrad) {
-    grid = (int)((tiles + kXcds - 1) / kXcds * kXcds);
-  } else {
-    static int per_cu = 0;
-    grid = persistent_grid((const void *)kern, kThreads, per_cu, tiles);
-  }
-  kern<<<dim3(grid), dim3(kThreads), 0, stream>>>(prm);
+  constexpr int WM = MOE_BWD_WM, S = MOE_BWD_STAGES;
+  auto kern = k_grouped_gemm_bwd<MODE, WM, S, kKS, GATHER>;
+  static int per_cu = 0;
+  const int grid = persistent_grid((const void *)kern, WM * 128, per_cu, tiles);
+  kern<<<dim3(grid), dim3(WM * 128), 0, stream>>>(prm);
 }
 
 // Shape checks common to the entry points.  The kernels index their
@@ -351,7 +405,7 @@ moe_status check_bwd(moe_dtype dt, int M, int d, int ffn, int G) {
   if (M < 0 || G < 1 || d < 1 || ffn < 1) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (d % kBN != 0 || ffn % kBN != 0 || G > 4096) return MOE_ERR_UNSUPPORTED;
+  if (d % kBN != 0 || ffn % kBN != 0 || G > kMaxG) return MOE_ERR_UNSUPPORTED;
   const int64_t big = (int64_t)1 << 32;
   if ((int64_t)M * 2 * ffn * 2 >= big || (int64_t)M * d * 2 >= big || (int64_t)2 * ffn * d * 2 >= big)
     return MOE_ERR_UNSUPPORTED;
@@ -374,7 +428,7 @@ extern "C" moe_status moe_grouped_down_backward(const void *dy_perm, moe_dtype d
     return MOE_ERR_INVALID_ARG;
   // dh = dY Wd_e: K = d, N = ffn; Wd_e is [d, ffn], N-contiguous.
   BwdParams prm{dy_perm, w2, dgu, gu, offsets, nullptr, G, M, d, 0, ffn, 1, 0};
-  launch<kDgradSwiglu>(prm, stream, ((int64_t)M + kBM - 1) / kBM * (ffn / kBN) + (int64_t)G * (ffn / kBN));
+  launch<kDgradSwiglu>(prm, stream, ((int64_t)M + kTileM - 1) / kTileM * (ffn / kBN) + (int64_t)G * (ffn / kBN));
   return launch_status();
 }
 
@@ -388,7 +442,7 @@ extern "C" moe_status moe_grouped_gate_up_backward(const void *dgu, moe_dtype dt
   if (!aligned16(dgu) || !aligned16(w13) || !aligned16(dx_perm)) return MOE_ERR_INVALID_ARG;
   // dX = dGU W13_e: K = 2 ffn (gate rows, then up rows), N = d.
   BwdParams prm{dgu, w13, dx_perm, nullptr, offsets, nullptr, G, M, 2 * ffn, 0, d, 1, 0};
-  launch<kDgradStore>(prm, stream, ((int64_t)M + kBM - 1) / kBM * (d / kBN) + (int64_t)G * (d / kBN));
+  launch<kDgradStore>(prm, stream, ((int64_t)M + kTileM - 1) / kTileM * (d / kBN) + (int64_t)G * (d / kBN));
   return launch_status();
 }
 
@@ -399,7 +453,7 @@ extern "C" moe_status moe_grouped_weight_grad(const void *a, const void *b, moe_
   if (M < 0 || G < 1 || m_dim < 1 || n_dim < 1 || b_k < 1) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (m_dim % kBM != 0 || n_dim % kBN != 0 || G > 4096) return MOE_ERR_UNSUPPORTED;
+  if (m_dim % kTileM != 0 || n_dim % kBN != 0 || G > kMaxG) return MOE_ERR_UNSUPPORTED;
   if (!b_order) b_rows = M;
   if (b_rows < 1 && M > 0) return MOE_ERR_INVALID_ARG;
   const int64_t big = (int64_t)1 << 32;
@@ -410,6 +464,9 @@ extern "C" moe_status moe_grouped_weight_grad(const void *a, const void *b, moe_
   if (!offsets || !c || (M > 0 && (!a || !b))) return MOE_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return MOE_ERR_INVALID_ARG;
   BwdParams prm{a, b, c, nullptr, offsets, b_order, G, M, 0, m_dim, n_dim, b_k, b_rows};
-  launch<kWgrad>(prm, stream, (int64_t)G * (m_dim / kBM) * (n_dim / kBN));
+  if (b_order)
+    launch<kWgrad, true>(prm, stream, (int64_t)G * (m_dim / kTileM) * (n_dim / kBN));
+  else
+    launch<kWgrad>(prm, stream, (int64_t)G * (m_dim / kTileM) * (n_dim / kBN));
   return launch_status();
 }

@@ -287,63 +287,100 @@ class MoeLayer:
         self._grads = b
         return b
 
-    def backward(self, dy, stream=None):
-        """Gradients of the layer at its last forward, for the output gradient
-        dy [T, d].  Returns a dict of device tensors: dx, dw13, dw2, and when
-        present dgate and dlogits (through the gates), dsh_w13, dsh_w2 (shared
-        expert).
-        The buffers are reused by the next call."""
-        if not self.train:
-            raise MoeError("backward() needs a layer built with train=True")
-        c = self.cfg
-        b = self._grad_buffers()
-        M = c.T * c.k
+    # The backward's steps, in order (BACKWARD_STAGES); backward() runs them
+    # all.  Each takes the output gradient dy [T, d].
+    BACKWARD_STAGES = ("bwd_combine", "bwd_down", "bwd_gate_up", "bwd_wgrad_down",
+                       "bwd_wgrad_gate_up", "bwd_shared", "bwd_dx", "bwd_gates")
+
+    def _bwd_views(self):
         merged = self.merge_shared
-        dy_perm = b["dy_perm"][:M] if merged else b["dy_perm"]
-        # 1. Combine's backward: the gradient goes out to the expert rows.
+        return (self.offsets_all if merged else self.offsets, self.w13_all if merged else self.w13,
+                self.w2_all if merged else self.w2, self.order_all if merged else self.order)
+
+    def bwd_combine(self, dy, stream=None):
+        """The combine's backward: the gradient goes out to the expert rows
+        (scaled by the gates), the gate gradients come back."""
+        b, M = self._grad_buffers(), self.cfg.T * self.cfg.k
+        merged = self.merge_shared
         moe_combine_backward(dy, self.inv, self.topk_w, self.y_perm if "dgate" in b else None,
-                             dy_perm, b.get("dgate"), b["dy_perm"][M:] if merged else None,
-                             stream=stream, want_dgate="dgate" in b)
-        offsets = self.offsets_all if merged else self.offsets
-        w13 = self.w13_all if merged else self.w13
-        w2 = self.w2_all if merged else self.w2
-        order = self.order_all if merged else self.order
-        # 2. Second product and SwiGLU backward, 3. first product to the rows.
+                             b["dy_perm"][:M] if merged else b["dy_perm"], b.get("dgate"),
+                             b["dy_perm"][M:] if merged else None, stream=stream,
+                             want_dgate="dgate" in b)
+
+    def bwd_down(self, dy, stream=None):
+        """Second product's input gradient and the SwiGLU backward: dgu."""
+        b = self._grad_buffers()
+        offsets, _, w2, _ = self._bwd_views()
         moe_grouped_down_backward(b["dy_perm"], offsets, w2, self.gu, b["dgu"], stream=stream)
+
+    def bwd_gate_up(self, dy, stream=None):
+        """First product's input gradient: the packed rows' dx_perm."""
+        b = self._grad_buffers()
+        offsets, w13, _, _ = self._bwd_views()
         moe_grouped_gate_up_backward(b["dgu"], offsets, w13, b["dx_perm"], stream=stream)
-        # 4. Weight gradients of both products.
+
+    def bwd_wgrad_down(self, dy, stream=None):
+        """Weight gradient of the second product: dW_down,e = dy_perm^T h."""
+        b = self._grad_buffers()
+        offsets, _, _, _ = self._bwd_views()
         moe_grouped_weight_grad(b["dy_perm"], self.h, offsets, b["dw2"], stream=stream)
+
+    def bwd_wgrad_gate_up(self, dy, stream=None):
+        """Weight gradient of the first product: dW13,e = dgu^T x rows."""
+        b, c = self._grad_buffers(), self.cfg
+        offsets, _, _, order = self._bwd_views()
         if self.x_perm is not None:
             moe_grouped_weight_grad(b["dgu"], self.x_perm, offsets, b["dw13"], stream=stream)
         else:
             moe_grouped_weight_grad(b["dgu"], self.x, offsets, b["dw13"], b_order=order, b_k=c.k,
                                     stream=stream)
-        dx_sh = None
-        if c.shared and not merged:
-            moe_grouped_down_backward(dy, self.sh_offsets, self.sh_w2, self.sh_gu, b["sh_dgu"],
-                                      stream=stream)
-            dx_sh = moe_grouped_gate_up_backward(b["sh_dgu"], self.sh_offsets, self.sh_w13,
-                                                 b["dx_sh"], stream=stream)
-            moe_grouped_weight_grad(dy, self.sh_h, self.sh_offsets, b["dsh_w2"], stream=stream)
-            moe_grouped_weight_grad(b["sh_dgu"], self.x, self.sh_offsets, b["dsh_w13"],
-                                    stream=stream)
-        elif merged:
-            dx_sh = b["dx_perm"][M:]
-        # 5. The dispatch's gradient combined back into the tokens.
-        moe_unpermute_combine(b["dx_perm"][:M] if merged else b["dx_perm"], self.inv, None,
-                              dx_sh, b["dx"], stream=stream, k=c.k)
+
+    def bwd_shared(self, dy, stream=None):
+        """The shared expert's own backward launches (merged: nothing to do)."""
+        c, b = self.cfg, self._grad_buffers()
+        if not c.shared or self.merge_shared:
+            return
+        moe_grouped_down_backward(dy, self.sh_offsets, self.sh_w2, self.sh_gu, b["sh_dgu"],
+                                  stream=stream)
+        moe_grouped_gate_up_backward(b["sh_dgu"], self.sh_offsets, self.sh_w13, b["dx_sh"],
+                                     stream=stream)
+        moe_grouped_weight_grad(dy, self.sh_h, self.sh_offsets, b["dsh_w2"], stream=stream)
+        moe_grouped_weight_grad(b["sh_dgu"], self.x, self.sh_offsets, b["dsh_w13"], stream=stream)
+
+    def bwd_dx(self, dy, stream=None):
+        """The dispatch's gradient combined back into the tokens (+ shared)."""
+        c, b, M = self.cfg, self._grad_buffers(), self.cfg.T * self.cfg.k
+        if self.merge_shared:
+            rows, dx_sh = b["dx_perm"][:M], b["dx_perm"][M:]
+        else:
+            rows, dx_sh = b["dx_perm"], b["dx_sh"] if c.shared else None
+        moe_unpermute_combine(rows, self.inv, None, dx_sh, b["dx"], stream=stream, k=c.k)
+
+    def bwd_gates(self, dy, stream=None):
+        """The gates' backward to the logits (nothing when the gates are given)."""
+        c, b = self.cfg, self._grad_buffers()
+        if "dgate" in b:
+            moe_gate_backward(self.logits, self.topk_ids, self.topk_w, b["dgate"], c.gating,
+                              c.renormalize, b["dlogits"], stream=stream)
+
+    def backward(self, dy, stream=None):
+        """Gradients of the layer at its last forward, for the output gradient
+        dy [T, d].  Returns a dict of device tensors: dx, dw13, dw2, and when
+        present dgate and dlogits (through the gates), dsh_w13, dsh_w2 (shared
+        expert).  The buffers are reused by the next call."""
+        if not self.train:
+            raise MoeError("backward() needs a layer built with train=True")
+        for name in self.BACKWARD_STAGES:
+            getattr(self, name)(dy, stream)
+        c, b = self.cfg, self._grad_buffers()
         out = {"dx": b["dx"]}
-        if merged:
+        if self.merge_shared:
             out.update(dw13=b["dw13"][:c.E], dw2=b["dw2"][:c.E], dsh_w13=b["dw13"][c.E:],
                        dsh_w2=b["dw2"][c.E:])
         else:
             out.update(dw13=b["dw13"], dw2=b["dw2"])
             if c.shared:
                 out.update(dsh_w13=b["dsh_w13"], dsh_w2=b["dsh_w2"])
-        # 6. The gates' backward to the logits.
         if "dgate" in b:
-            moe_gate_backward(self.logits, self.topk_ids, self.topk_w, b["dgate"], c.gating,
-                              c.renormalize, b["dlogits"], stream=stream)
-            out["dlogits"] = b["dlogits"]
-            out["dgate"] = b["dgate"]
+            out.update(dlogits=b["dlogits"], dgate=b["dgate"])
         return out
