@@ -95,6 +95,10 @@ BWD_CASES = [
     (128, 128, [0, 0, 3]),
     (512, 256, [250, 0, 321, 97, 640, 1]),
     (256, 384, [65, 129, 0, 2]),
+    # the ping-pong tiles (more rows per expert, N a multiple of 256): the
+    # medium family above, the large one here, with ragged tails
+    (256, 512, [300, 0, 1000, 97]),
+    (512, 768, [200, 333, 260, 250]),
 ]
 
 

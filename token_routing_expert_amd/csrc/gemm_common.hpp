@@ -174,5 +174,70 @@ inline int persistent_grid(const void *kernel, int threads, int &per_cu, int64_t
   return (int)(g < kXcds ? kXcds : g);
 }
 
+// ---- column-contiguous operand tiles ------------------------------------
+// An operand stored along the output dimension ([K, N] row-major weights of
+// a backward product, or the rows of a weight gradient's operands) is staged
+// in LDS as it lies in memory and read back transposed for MFMA, which wants
+// every lane's values consecutive in K.
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Column-contiguous tile: K-rows of W columns (W = 128 or 256), 2 W bytes
+// per K-row in 64-byte segments of 32 columns.  Segment sg of K-row r is
+// stored at position sg ^ (r & 3): a transposing read takes 64 bytes from
+// each of four K-rows r .. r + 3 per half wave, which then land in four
+// different quarters of the 256-byte bank row.
+template <int W>
+__device__ __forceinline__ int cc_byte(int r, int sg, int byte_in_seg) {
+  return r * (2 * W) + ((sg ^ (r & 3)) << 6) + byte_in_seg;
+}
+
+// A column-contiguous stage of W columns (W = 128 or 256) is filled by
+// 1 KB DMA groups of 512 / W K-rows; lane l of group g fills K-row
+// g (512 / W) + l / (W / 8) at physical chunk l % (W / 8), which holds the
+// 16 bytes at this column of the tile (segment swizzle of cc_byte).
+template <int W>
+__device__ __forceinline__ void cc_lane(int g, int lane, int &krow, int &col) {
+  constexpr int LPR = W / 8;   // lanes per K-row
+  krow = g * (512 / W) + lane / LPR;
+  const int pc = lane % LPR;
+  col = (((pc >> 2) ^ (krow & 3)) << 5) + (pc & 3) * 8;
+}
+
+// The same operand for 32 columns (column block cb) from a column-contiguous
+// tile.  ds_read_b64_tr_b16 works on groups of 16 lanes: if lane 4 i + a of
+// a group addresses four consecutive 16-bit values, lane 4 a + b receives
+// value b of lanes a, 4 + a, 8 + a, 12 + a.  So lane s addresses K-row
+// 16 q + 8 (s / 32) + 4 h + (s % 16) / 4 at columns 16 ((s / 16) % 2) +
+// 4 (s % 4) of the block, and lane l receives column l % 32 at K-rows
+// 8 (l / 32) + 4 h .. + 3: half h = 0 gives the lane's K 0..3, h = 1 K 4..7.
+template <int W>
+__device__ __forceinline__ u32x4 frag_tr(const char *stage, int cb, int q, int lane) {
+  u32x4 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 16 * q + 8 * (lane >> 5) + 4 * h + ((lane & 15) >> 2);
+    const int byte = cc_byte<W>(r, cb, (((lane >> 4) & 1) << 5) + ((lane & 3) << 3));
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(stage + byte));
+    const u32x2 w = __builtin_bit_cast(u32x2, v);
+    out[2 * h] = w[0];
+    out[2 * h + 1] = w[1];
+  }
+  return out;
+}
+
 }  // namespace
+}  // namespace moe
+
+namespace moe {
+// The backward input-gradient products on the ping-pong tiles (defined in
+// grouped_gemm.hip): var 1 stores out = a W_e ([M, K] x [K, N] per expert
+// segment), var 2 applies the SwiGLU backward with the pre-activations gu
+// and writes dgu ([M, 2 N]).  Returns false, launching nothing, when the
+// shape is not one the ping-pong tiles serve (few rows per expert, N not a
+// multiple of 256); the caller then uses its own tiles.
+bool launch_dgrad_pp(int var, const void *a, int M, int K, int N, const int32_t *offsets, int G,
+                     const void *w, void *out, const void *gu, hipStream_t stream);
 }  // namespace moe

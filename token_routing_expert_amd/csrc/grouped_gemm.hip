@@ -339,8 +339,14 @@ __device__ __forceinline__ int swz_c(int r, int cc) {
     return r * 4 + (cc ^ ((r >> 2) & 3));   // 16 consecutive rows at one chunk: all banks once
 }
 
+// VAR selects the product: 0 the forward's (weights K-contiguous, [N, K]
+// per expert); 1 and 2 a backward input-gradient product, whose weights are
+// [K, N] per expert (N-contiguous) and are staged as column-contiguous tiles
+// read back transposed -- 1 stores the product, 2 is the down product's
+// backward, whose epilogue applies the SwiGLU backward with the forward's
+// pre-activations GU ([M, 2 N]) and writes dgu ([M, 2 N]) to C.
 template <bool BF16, int BM, int BR, int SA, int SB, int CPR, int DA, bool SWIGLU, bool SPLIT,
-          bool SAVE = false>
+          bool SAVE = false, int VAR = 0>
 __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     const u32x4 *__restrict__ A, int M, int kvec, const int32_t *__restrict__ offsets, int G,
     const u32x4 *__restrict__ B, int64_t b_expert_vec, int64_t b_up_vec, int ntiles, int N,
@@ -370,6 +376,8 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
   // MFMAs at least one phase earlier.
   constexpr bool kDrainLast = DA == SA - 1;
   static_assert(FM <= 5, "row blocks per wave");
+  static_assert(VAR == 0 || (BF16 && !SWIGLU && !SAVE), "backward products: bf16, plain tiles");
+  constexpr bool BT = VAR != 0;                  // weights [K, N]: column-contiguous stages
 
   __shared__ u32x4 smem[SA * ASTAGE + SB * BSTAGE];
   u32x4 *const a_ring = smem;
@@ -434,12 +442,22 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
 #pragma unroll
       for (int r = 0; r < NLB; ++r) {
         const int g = wq + 4 * r;
-        const int brow = g * RPI + ld_row;
-        off[r] = ((SWIGLU && brow >= BN ? (uint32_t)b_up_vec + (uint32_t)(n0 + brow - BN) * kvec
-                                        : (uint32_t)(n0 + brow) * (uint32_t)kvec) +
-                  ((uint32_t)ld_slot ^ key_of(g))) * 16u;
+        if constexpr (BT) {
+          // K-row krow of the slice, columns n0 + col .. + 7 of the [K, N]
+          // matrix; the slice's K position is the scalar offset.
+          int krow, col;
+          cc_lane<BR>(g, lane, krow, col);
+          off[r] = ((uint32_t)krow * (uint32_t)N + (uint32_t)(n0 + col)) * 2u;
+        } else {
+          const int brow = g * RPI + ld_row;
+          off[r] = ((SWIGLU && brow >= BN ? (uint32_t)b_up_vec + (uint32_t)(n0 + brow - BN) * kvec
+                                          : (uint32_t)(n0 + brow) * (uint32_t)kvec) +
+                    ((uint32_t)ld_slot ^ key_of(g))) * 16u;
+        }
       }
     };
+    // Bytes from one K slice to the next in the weight tile.
+    const uint32_t b_step = BT ? (uint32_t)(CPR * 8) * (uint32_t)N * 2u : (uint32_t)CPR * 16u;
     auto issue_a = [&](int kt, const uint32_t (&off)[NLA]) {
       u32x4 *stage = a_ring + (kt % SA) * ASTAGE;
 #pragma unroll
@@ -450,7 +468,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
       u32x4 *stage = b_ring + (kt % SB) * BSTAGE;
 #pragma unroll
       for (int r = 0; r < NLB; ++r)
-        buffer_load_lds16(b_base, b_bytes, stage + (wq + 4 * r) * 64, off[r], kt * CPR * 16);
+        buffer_load_lds16(b_base, b_bytes, stage + (wq + 4 * r) * 64, off[r], (uint32_t)kt * b_step);
     };
     // Waits for slice k of this wave's operand: the slices after it that are
     // already issued (up to k + SB - 2, or k + DA - 1 for the row tile) may
@@ -528,8 +546,14 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int cc = 2 * (2 * h + q) + (lane >> 5);
-          fb[q][0] = Bs[swz_c<CPR>(brow0 + (lane & 31), cc)];
-          fb[q][1] = Bs[swz_c<CPR>(brow1 + (lane & 31), cc)];
+          if constexpr (BT) {
+            const char *bsb = reinterpret_cast<const char *>(Bs);
+            fb[q][0] = frag_tr<BR>(bsb, brow0 / 32, 2 * h + q, lane);
+            fb[q][1] = frag_tr<BR>(bsb, brow1 / 32, 2 * h + q, lane);
+          } else {
+            fb[q][0] = Bs[swz_c<CPR>(brow0 + (lane & 31), cc)];
+            fb[q][1] = Bs[swz_c<CPR>(brow1 + (lane & 31), cc)];
+          }
 #pragma unroll
           for (int i = 0; i < NL; ++i)
             if (!DYN || i < live)
@@ -613,6 +637,40 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
         float val[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) val[v] = SWIGLU ? silu(acc[i][0][v]) * acc[i][1][v] : acc[i][j][v];
+        if constexpr (VAR == 2) {
+          // dh -> (dgate, dup) through h = SiLU(g) u:
+          //   dgate = dh u SiLU'(g), dup = dh SiLU(g),
+          //   SiLU'(g) = s (1 + g (1 - s)), s = 1 / (1 + e^-g).
+          // Adjacent lanes trade values so each holds two adjacent columns of
+          // one row, read as one 4-byte pair of g and of u.
+          const int c0 = col & ~1;
+          const uint16_t *gu = static_cast<const uint16_t *>(GU);
+          uint16_t *out = static_cast<uint16_t *>(C);
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {
+            const float mine = odd ? val[v + 1] : val[v];
+            const float give = odd ? val[v] : val[v + 1];
+            const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0xB1, 0xF, 0xF, false));
+            const float dh[2] = {odd ? got : mine, odd ? mine : got};   // columns c0, c0 + 1
+            const int row = rblk + 8 * (v >> 2) + row_l + (v & 3) + (odd ? 1 : 0);
+            if (row < hi) {
+              const int64_t base = (int64_t)row * 2 * N + c0;
+              const uint32_t gg = *reinterpret_cast<const uint32_t *>(gu + base);
+              const uint32_t uu = *reinterpret_cast<const uint32_t *>(gu + base + N);
+              const float g[2] = {bf16_lo(gg), bf16_hi(gg)}, u[2] = {bf16_lo(uu), bf16_hi(uu)};
+              float dg[2], du[2];
+#pragma unroll
+              for (int c = 0; c < 2; ++c) {
+                const float s = 1.0f / (1.0f + __expf(-g[c]));
+                dg[c] = dh[c] * u[c] * (s * (1.0f + g[c] * (1.0f - s)));
+                du[c] = dh[c] * (g[c] * s);
+              }
+              *reinterpret_cast<uint32_t *>(out + base) = pack_bf16x2(dg[0], dg[1]);
+              *reinterpret_cast<uint32_t *>(out + base + N) = pack_bf16x2(du[0], du[1]);
+            }
+          }
+          continue;
+        }
         put(C, N, rblk, col, val);
         if constexpr (SAVE && SWIGLU) {
           // Pre-activations for the backward: gate at column col, up at
@@ -791,6 +849,23 @@ void launch_down(Family f, const void *h, int M, int ffn, int d, const int32_t *
     launch_one<BF16, false, G2Large>(h, M, ffn, d, offsets, G, w2, y, stream);
 }
 
+// Backward input-gradient products on the ping-pong tiles (bf16).
+template <int VAR, typename Cfg>
+void launch_dgrad(const void *a, int M, int K, int N, const int32_t *offsets, int G, const void *w,
+                  void *out, const void *gu, hipStream_t stream) {
+  const int kvec = K * 2 / 16;
+  const int64_t b_expert = (int64_t)K * N * 2 / 16;
+  const int ntiles = N / Cfg::BR;
+  const int64_t mtiles_max = (M + Cfg::BM - 1) / Cfg::BM + G;
+  auto kern = k_grouped_gemm_pp<true, Cfg::BM, Cfg::BR, Cfg::SA, Cfg::SB, Cfg::CPR, Cfg::DA, false,
+                                Cfg::SPLIT, false, VAR>;
+  static int per_cu = 0;
+  const int grid = persistent_grid((const void *)kern, 512, per_cu, mtiles_max * ntiles);
+  kern<<<dim3(grid), dim3(512), 0, stream>>>(static_cast<const u32x4 *>(a), M, kvec, offsets, G,
+                                            static_cast<const u32x4 *>(w), b_expert, 0, ntiles, N,
+                                            out, nullptr, 1, 0, const_cast<void *>(gu));
+}
+
 // Argument checks shared by the three entry points (pointers are checked by
 // each).  Returns MOE_OK when the call may launch.
 moe_status check_shape(moe_dtype dt, int M, int d, int ffn, int G) {
@@ -808,6 +883,21 @@ moe_status check_shape(moe_dtype dt, int M, int d, int ffn, int G) {
 }
 
 }  // namespace
+
+bool launch_dgrad_pp(int var, const void *a, int M, int K, int N, const int32_t *offsets, int G,
+                     const void *w, void *out, const void *gu, hipStream_t stream) {
+  const Family f = family_of(M, G, K);
+  if (f == Family::Small || N % 256 != 0 || K % 64 != 0) return false;
+  if (f == Family::Medium) {
+    if (var == 2) launch_dgrad<2, G2Medium>(a, M, K, N, offsets, G, w, out, gu, stream);
+    else launch_dgrad<1, G2Medium>(a, M, K, N, offsets, G, w, out, gu, stream);
+  } else {
+    if (var == 2) launch_dgrad<2, G2Large>(a, M, K, N, offsets, G, w, out, gu, stream);
+    else launch_dgrad<1, G2Large>(a, M, K, N, offsets, G, w, out, gu, stream);
+  }
+  return true;
+}
+
 }  // namespace moe
 
 using namespace moe;

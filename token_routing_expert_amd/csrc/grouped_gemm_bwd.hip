@@ -31,8 +31,6 @@
 namespace moe {
 namespace {
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBN = 128;             // tile columns
 constexpr int kMaxG = 1024;          // experts per call (their offsets are staged in LDS)
@@ -65,16 +63,6 @@ __device__ __forceinline__ int kc_key(int r) {
 template <int KS>
 __device__ __forceinline__ int kc_slot(int r, int cc) { return r * (KS / 8) + (cc ^ kc_key<KS>(r)); }
 
-// Column-contiguous tile: 64 K-rows x W columns (W = 128 or 256), 2 W bytes
-// per K-row in 64-byte segments of 32 columns.  Segment sg of K-row r is
-// stored at position sg ^ (r & 3): a transposing read takes 64 bytes from
-// each of four K-rows r .. r + 3 per half wave, which then land in four
-// different quarters of the 256-byte bank row.
-template <int W>
-__device__ __forceinline__ int cc_byte(int r, int sg, int byte_in_seg) {
-  return r * (2 * W) + ((sg ^ (r & 3)) << 6) + byte_in_seg;
-}
-
 // ---- operand fragments ---------------------------------------------------
 
 // MFMA 32x32x16 operand of 32 rows (row block rb) at k-group q from a
@@ -82,29 +70,6 @@ __device__ __forceinline__ int cc_byte(int r, int sg, int byte_in_seg) {
 template <int KS>
 __device__ __forceinline__ u32x4 frag_kc(const u32x4 *stage, int rb, int q, int lane) {
   return stage[kc_slot<KS>(rb * 32 + (lane & 31), 2 * q + (lane >> 5))];
-}
-
-// The same operand for 32 columns (column block cb) from a column-contiguous
-// tile.  ds_read_b64_tr_b16 works on groups of 16 lanes: if lane 4 i + a of
-// a group addresses four consecutive 16-bit values, lane 4 a + b receives
-// value b of lanes a, 4 + a, 8 + a, 12 + a.  So lane s addresses K-row
-// 16 q + 8 (s / 32) + 4 h + (s % 16) / 4 at columns 16 ((s / 16) % 2) +
-// 4 (s % 4) of the block, and lane l receives column l % 32 at K-rows
-// 8 (l / 32) + 4 h .. + 3: half h = 0 gives the lane's K 0..3, h = 1 K 4..7.
-template <int W>
-__device__ __forceinline__ u32x4 frag_tr(const char *stage, int cb, int q, int lane) {
-  u32x4 out;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = 16 * q + 8 * (lane >> 5) + 4 * h + ((lane & 15) >> 2);
-    const int byte = cc_byte<W>(r, cb, (((lane >> 4) & 1) << 5) + ((lane & 3) << 3));
-    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16 *)(stage + byte));
-    const u32x2 w = __builtin_bit_cast(u32x2, v);
-    out[2 * h] = w[0];
-    out[2 * h + 1] = w[1];
-  }
-  return out;
 }
 
 __device__ __forceinline__ void mma(const u32x4 &a, const u32x4 &b, f32x16 &c) {
@@ -120,18 +85,6 @@ __device__ __forceinline__ float bf16_at(const uint16_t *p, int64_t i) {
 struct TileB {
   int e, lo, hi, m0, n0, KT;
 };
-
-// A column-contiguous stage of W columns (W = 128 or 256) is filled by
-// 1 KB DMA groups of 512 / W K-rows; lane l of group g fills K-row
-// g (512 / W) + l / (W / 8) at physical chunk l % (W / 8), which holds the
-// 16 bytes at this column of the tile (segment swizzle of cc_byte).
-template <int W>
-__device__ __forceinline__ void cc_lane(int g, int lane, int &krow, int &col) {
-  constexpr int LPR = W / 8;   // lanes per K-row
-  krow = g * (512 / W) + lane / LPR;
-  const int pc = lane % LPR;
-  col = (((pc >> 2) ^ (krow & 3)) << 5) + (pc & 3) * 8;
-}
 
 // The kernel is persistent: a workgroup walks its band of tiles and its
 // S-stage ring streams K slices continuously across tile boundaries, so the
@@ -427,6 +380,7 @@ extern "C" moe_status moe_grouped_down_backward(const void *dy_perm, moe_dtype d
   if (!aligned16(dy_perm) || !aligned16(w2) || !aligned16(gu) || !aligned16(dgu))
     return MOE_ERR_INVALID_ARG;
   // dh = dY Wd_e: K = d, N = ffn; Wd_e is [d, ffn], N-contiguous.
+  if (launch_dgrad_pp(2, dy_perm, M, d, ffn, offsets, G, w2, dgu, gu, stream)) return launch_status();
   BwdParams prm{dy_perm, w2, dgu, gu, offsets, nullptr, G, M, d, 0, ffn, 1, 0};
   launch<kDgradSwiglu>(prm, stream, ((int64_t)M + kTileM - 1) / kTileM * (ffn / kBN) + (int64_t)G * (ffn / kBN));
   return launch_status();
@@ -441,6 +395,8 @@ extern "C" moe_status moe_grouped_gate_up_backward(const void *dgu, moe_dtype dt
   if (!dgu || !offsets || !w13 || !dx_perm) return MOE_ERR_INVALID_ARG;
   if (!aligned16(dgu) || !aligned16(w13) || !aligned16(dx_perm)) return MOE_ERR_INVALID_ARG;
   // dX = dGU W13_e: K = 2 ffn (gate rows, then up rows), N = d.
+  if (launch_dgrad_pp(1, dgu, M, 2 * ffn, d, offsets, G, w13, dx_perm, nullptr, stream))
+    return launch_status();
   BwdParams prm{dgu, w13, dx_perm, nullptr, offsets, nullptr, G, M, 2 * ffn, 0, d, 1, 0};
   launch<kDgradStore>(prm, stream, ((int64_t)M + kTileM - 1) / kTileM * (d / kBN) + (int64_t)G * (d / kBN));
   return launch_status();
