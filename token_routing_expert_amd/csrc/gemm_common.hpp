@@ -240,4 +240,9 @@ namespace moe {
 // multiple of 256); the caller then uses its own tiles.
 bool launch_dgrad_pp(int var, const void *a, int M, int K, int N, const int32_t *offsets, int G,
                      const void *w, void *out, const void *gu, hipStream_t stream);
+// Weight gradients out[e] = a[seg e]^T b[seg e] ([G, m_dim, n_dim]) on the
+// ping-pong tiles; false (nothing launched) when m_dim or n_dim is not a
+// multiple of 256.
+bool launch_wgrad_pp(const void *a, const void *b, int M, int m_dim, int n_dim,
+                     const int32_t *offsets, int G, void *out, hipStream_t stream);
 }  // namespace moe

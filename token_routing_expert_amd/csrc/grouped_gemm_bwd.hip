@@ -419,6 +419,8 @@ extern "C" moe_status moe_grouped_weight_grad(const void *a, const void *b, moe_
   // With no rows the operands are never read (every expert's gradient is 0).
   if (!offsets || !c || (M > 0 && (!a || !b))) return MOE_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return MOE_ERR_INVALID_ARG;
+  if (!b_order && launch_wgrad_pp(a, b, M, m_dim, n_dim, offsets, G, c, stream))
+    return launch_status();
   BwdParams prm{a, b, c, nullptr, offsets, b_order, G, M, 0, m_dim, n_dim, b_k, b_rows};
   if (b_order)
     launch<kWgrad, true>(prm, stream, (int64_t)G * (m_dim / kTileM) * (n_dim / kBN));
