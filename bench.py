@@ -343,7 +343,9 @@ def main():
     ap.add_argument("--bias-lr", type=float, default=1e-3)
     ap.add_argument("--path", choices=("gather", "packed"), default="gather",
                     help="gather: the first expert product reads token rows through the "
-                         "permutation; packed: the permute writes the packed copy X[order]")
+                         "permutation; packed: the permute writes the packed copy X[order] "
+                         "(with --train the packed rows are kept either way, for the weight "
+                         "gradient)")
     ap.add_argument("--train", action="store_true",
                     help="time a training step instead: the forward keeping the pre-activations, "
                          "then the backward to dx, the weight gradients and dlogits (bf16 only)")

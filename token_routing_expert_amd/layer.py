@@ -71,7 +71,10 @@ class MoeLayer:
 
     train=True keeps what the backward needs: the first product also stores
     the pre-activations gu, and ``backward(dy)`` then returns the gradients
-    of the layer (bf16 only).  The backward is the forward's steps in
+    of the layer (bf16 only).  The packed rows X[order] are kept too (the
+    permute writes them even on the fused-gather path; not with
+    merge_shared): the first product's weight gradient reads them as
+    contiguous rows.  The backward is the forward's steps in
     reverse ("Expert parallelism", section "How many bytes move"): the
     combine's gradient goes out to the expert rows, through the two products
     (input and weight gradients), and back into the tokens.
@@ -127,7 +130,8 @@ class MoeLayer:
         self.send_counts = torch.empty((cfg.n_ep, cfg.n_ep), dtype=i32, device=dev) if cfg.n_ep else None
         self.counts = torch.empty(E, dtype=i32, device=dev)
         self.inv = torch.empty(M, dtype=i32, device=dev)
-        self.x_perm = None if fused_gather else torch.empty((M, d), dtype=act, device=dev)
+        keep_rows = not fused_gather or (self.train and not merge_shared)
+        self.x_perm = torch.empty((M, d), dtype=act, device=dev) if keep_rows else None
         self.workspace = torch.empty(max(16, moe_permute_workspace_bytes(T, k, E)), dtype=torch.uint8,
                                      device=dev)
         self.y = torch.empty((T, d), dtype=act, device=dev)
@@ -182,7 +186,7 @@ class MoeLayer:
     def permute(self, stream=None):
         moe_permute(self.x, self.topk_ids, self.cfg.E, self.counts, self.offsets, self.order,
                     self.inv, self.x_perm, self.workspace, stream=stream,
-                    rows=not self.fused_gather)
+                    rows=self.x_perm is not None)
 
     def experts_routed(self, stream=None):
         if self.fused_gather or self.train:
@@ -329,7 +333,7 @@ class MoeLayer:
         """Weight gradient of the first product: dW13,e = dgu^T x rows."""
         b, c = self._grad_buffers(), self.cfg
         offsets, _, _, order = self._bwd_views()
-        if self.x_perm is not None:
+        if self.x_perm is not None and not self.merge_shared:
             moe_grouped_weight_grad(b["dgu"], self.x_perm, offsets, b["dw13"], stream=stream)
         else:
             moe_grouped_weight_grad(b["dgu"], self.x, offsets, b["dw13"], b_order=order, b_k=c.k,
