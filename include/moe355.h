@@ -388,6 +388,23 @@ moe_status moe_grouped_weight_grad(const void *a, const void *b, moe_dtype dt, i
                                    const int32_t *b_order, int b_k, int b_rows, void *c,
                                    hipStream_t stream);
 
+/*
+ * Backward of the router product (logits = x w_router^T, moe_router_logits):
+ *     dx        += dlogits w_router          [T, E] x [E, d]   (dx: [T, d], added to)
+ *     dw_router  = dlogits^T x               [E, T] x [T, d]   (overwritten)
+ * dlogits [T, E] fp32 (moe_gate_backward) is rounded once to bf16, the
+ * products' operand type, into the workspace (moe_router_backward_workspace_bytes
+ * bytes, which also holds the products' one-segment offsets); fp32
+ * accumulation, bf16 results.  Either output may be NULL (not computed).
+ * Errors: INVALID_ARG for NULL or misaligned pointers, a small workspace,
+ * T < 0, d < 1, E < 1; UNSUPPORTED for fp32, E or d not a multiple of 256,
+ * 0 < T < 96, or operands of 4 GiB or more.
+ */
+size_t moe_router_backward_workspace_bytes(int T, int E);
+moe_status moe_router_backward(const float *dlogits, const void *x, moe_dtype dt, int T, int d,
+                               const void *w_router, int E, void *dx, void *dw_router,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

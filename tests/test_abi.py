@@ -217,6 +217,20 @@ def test_backward_validation(lib):
     assert g(a, mis, 1, 64, 128, 256, a, 4, NULL, 1, 0, a, NULL) == INVALID     # misaligned b
 
 
+def test_router_backward_validation(lib):
+    a = ctypes.c_void_p(16)
+    ws = lib.moe_router_backward_workspace_bytes(512, 256)
+    assert ws >= 512 * 256 * 2
+    f = lib.moe_router_backward
+    #       dl x  dt T    d    wr E    dx dw ws bytes stream
+    assert f(a, a, 0, 512, 512, a, 256, a, a, a, ws, NULL) == UNSUPPORTED    # fp32
+    assert f(a, a, 1, 512, 512, a, 8, a, a, a, ws, NULL) == UNSUPPORTED      # E % 256
+    assert f(a, a, 1, 50, 512, a, 256, a, a, a, ws, NULL) == UNSUPPORTED     # T < 96
+    assert f(a, a, 1, 512, 512, a, 256, a, a, a, ws - 1, NULL) == INVALID    # small workspace
+    assert f(a, a, 1, 512, 512, NULL, 256, a, a, a, ws, NULL) == INVALID     # null weights
+    assert f(a, a, 1, 512, 512, a, 256, NULL, NULL, NULL, 0, NULL) == 0      # nothing asked
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(moe.MoeError):
         moe.load_library(str(tmp_path / "missing.so"))

@@ -346,3 +346,51 @@ def test_layer_backward_matches_oracle(lib, case):
                                         ref["dsh_w13"].reshape(-1, ffn, d), 2e-2, "dsh_w13")
         worst["dsh_w2"] = blocks_close(host(g["dsh_w2"]), ref["dsh_w2"], 2e-2, "dsh_w2")
     print(name, {k_: f"{v:.2e}" for k_, v in worst.items()}, flush=True)
+
+
+def test_router_backward(lib):
+    """dx += dlogits w_router and dw_router = dlogits^T x against the oracle's
+    B0 (the GPU rounds dlogits to bf16 once, inside the 2e-2 bar)."""
+    T, E, d = 700, 256, 512
+    rng = np.random.default_rng(31)
+    dl = (1e-2 * rng.standard_normal((T, E))).astype(np.float32)
+    x = to_bf16(rng.standard_normal((T, d)))
+    wr = to_bf16(rng.standard_normal((E, d)) / np.sqrt(d))
+    dx0 = to_bf16(rng.standard_normal((T, d)))
+    dx = dev(dx0)
+    dwr = lib.moe_router_backward(dev(dl), dev(x), dev(wr), dx)
+    torch.cuda.synchronize()
+    ref_dx, ref_dw = oracle.router_backward(x, wr, dl)
+    rows_close(host(dx), ref_dx + f64(dx0), 2e-2, "dx")
+    rows_close(host(dwr), ref_dw, 2e-2, "dw_router")
+    for T_, E_, d_ in ((50, 256, 512), (700, 8, 512), (700, 256, 384)):
+        with pytest.raises(lib.MoeError):
+            lib.moe_router_backward(torch.zeros((T_, E_), device="cuda"),
+                                    torch.zeros((T_, d_), dtype=torch.bfloat16, device="cuda"),
+                                    torch.zeros((E_, d_), dtype=torch.bfloat16, device="cuda"))
+
+
+def test_layer_backward_with_router(lib):
+    """A training step with the router product in front: dx includes the
+    router's part, dw_router its weight gradient; the oracle takes the GPU's
+    logits (the route is bit-exact on them) and the same router weights."""
+    from token_routing_expert_amd.layer import MoeLayer
+    cfg = inputs.MoeConfig("router_train", 23, T=512, E=256, k=8, d=256, ffn=256, dtype="bf16",
+                           gating="sigmoid", renormalize=1, n_groups=8, topk_groups=4, w_std=0.05)
+    x = inputs.gen_x(cfg)
+    w13, w2 = inputs.gen_expert_weights(cfg)
+    wr = inputs.gen_router_weights(cfg)
+    dy = to_bf16(np.random.default_rng(4).standard_normal((cfg.T, cfg.d)))
+    layer = MoeLayer(cfg, x, w13, w2, device="cuda", fused_gather=True, w_router=wr, train=True)
+    layer.forward()
+    g = layer.backward(dev(dy))
+    torch.cuda.synchronize()
+    logits = host(layer.logits)
+    ids, w = oracle.route(logits, cfg.k, cfg.gating, 1, 8, 4)
+    assert np.array_equal(host(layer.topk_ids), ids)
+    ref = oracle.layer_backward(x, logits, ids, w, w13, w2, dy, "sigmoid", 1, wg=wr)
+    worst = {"dx": rows_close(host(g["dx"]), ref["dx"], 2e-2, "dx"),
+             "dw_router": rows_close(host(g["dw_router"]), ref["dwg"], 2e-2, "dw_router"),
+             "dw13": blocks_close(host(g["dw13"]).reshape(-1, cfg.ffn, cfg.d),
+                                  ref["dw13"].reshape(-1, cfg.ffn, cfg.d), 2e-2, "dw13")}
+    print("router_train", {k_: f"{v:.2e}" for k_, v in worst.items()}, flush=True)

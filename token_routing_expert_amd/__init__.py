@@ -25,7 +25,8 @@ EXPORTS = ("moe_status_string", "moe_route_topk", "moe_route_topk_biased", "moe_
            "moe_grouped_gate_up", "moe_grouped_gate_up_gather", "moe_grouped_down",
            "moe_unpermute_combine", "moe_grouped_gate_up_save", "moe_combine_backward",
            "moe_gate_backward", "moe_grouped_down_backward", "moe_grouped_gate_up_backward",
-           "moe_grouped_weight_grad")
+           "moe_grouped_weight_grad", "moe_router_backward_workspace_bytes",
+           "moe_router_backward")
 
 
 class MoeError(RuntimeError):
@@ -66,12 +67,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_grouped_down_backward.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P, P]
     lib.moe_grouped_gate_up_backward.argtypes = [P, i32, i32, i32, i32, P, i32, P, P, P]
     lib.moe_grouped_weight_grad.argtypes = [P, P, i32, i32, i32, i32, P, i32, P, i32, i32, P, P]
+    lib.moe_router_backward_workspace_bytes.argtypes = [i32, i32]
+    lib.moe_router_backward_workspace_bytes.restype = sz
+    lib.moe_router_backward.argtypes = [P, P, i32, i32, i32, P, i32, P, P, P, sz, P]
     for name in ("moe_route_topk", "moe_route_topk_biased", "moe_router_logits",
                  "moe_router_bias_update", "moe_sigmoid_pinned", "moe_send_counts", "moe_permute",
                  "moe_grouped_swiglu", "moe_grouped_gate_up", "moe_grouped_gate_up_gather",
                  "moe_grouped_down", "moe_unpermute_combine", "moe_grouped_gate_up_save",
                  "moe_combine_backward", "moe_gate_backward", "moe_grouped_down_backward",
-                 "moe_grouped_gate_up_backward", "moe_grouped_weight_grad"):
+                 "moe_grouped_gate_up_backward", "moe_grouped_weight_grad", "moe_router_backward"):
         getattr(lib, name).restype = i32
     if path == LIB_PATH:
         _lib = lib
@@ -493,3 +497,34 @@ def moe_grouped_weight_grad(a, b, offsets, out=None, b_order=None, b_k=1, stream
         _ptr(a), _ptr(b), _dtype_code(a), M, m, n, _ptr(offsets), G, _ptr(b_order), b_k, b_rows,
         _ptr(out), _stream(stream)), "moe_grouped_weight_grad")
     return out
+
+
+def moe_router_backward_workspace_bytes(T, E) -> int:
+    return int(load_library().moe_router_backward_workspace_bytes(T, E))
+
+
+def moe_router_backward(dlogits, x, w_router, dx=None, dw_router=None, workspace=None,
+                        stream=None):
+    """The router product's backward: dx [T, d] += dlogits w_router (when dx
+    is given) and dw_router [E, d] = dlogits^T x (allocated when None).
+    Returns dw_router."""
+    torch = _torch()
+    _dev(dlogits, "dlogits", (torch.float32,))
+    _dev(x, "x", _act_dtypes())
+    _dev(w_router, "w_router", (x.dtype,))
+    T, d = x.shape
+    E = w_router.shape[0]
+    if tuple(dlogits.shape) != (T, E) or w_router.shape[1] != d:
+        raise MoeError("moe_router_backward: inconsistent shapes")
+    if dx is not None:
+        _dev(dx, "dx", (x.dtype,))
+    dw_router = torch.empty((E, d), dtype=x.dtype, device=x.device) if dw_router is None \
+        else dw_router
+    _dev(dw_router, "dw_router", (x.dtype,))
+    nbytes = moe_router_backward_workspace_bytes(T, E)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _check(load_library().moe_router_backward(
+        _ptr(dlogits), _ptr(x), _dtype_code(x), T, d, _ptr(w_router), E, _ptr(dx), _ptr(dw_router),
+        _ptr(workspace), workspace.numel(), _stream(stream)), "moe_router_backward")
+    return dw_router

@@ -11,8 +11,10 @@
 // and the gate gradient reaches the logits through the gate formula of the
 // route (the choice itself is piecewise constant, and the balancing bias is
 // outside the gradient: "05 - Expert Parallelism (MoE)", section "Load
-// balancing").
+// balancing"), and from the logits through the router product,
+// logits = x w_router^T, to x and w_router.
 #include "common.hpp"
+#include "gemm_common.hpp"
 
 namespace moe {
 namespace {
@@ -193,10 +195,64 @@ __global__ __launch_bounds__(kThreads) void k_gate_bwd(const float *__restrict__
   }
 }
 
+// The router product's backward starts from a bf16 copy of dlogits (the
+// products' operand type); the same launch writes the one-segment offsets
+// [0, T] the grouped products take.
+__global__ __launch_bounds__(kThreads) void k_dlogits_bf16(const float *__restrict__ dl, int64_t n,
+                                                           int T, uint16_t *__restrict__ out,
+                                                           int32_t *__restrict__ offsets) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) out[i] = (uint16_t)f32_to_bf16_rne(dl[i]);
+  if (i == 0) {
+    offsets[0] = 0;
+    offsets[1] = T;
+  }
+}
+
+inline size_t router_ws_split(int T, int E) {   // bytes of the bf16 copy, rounded up to 256
+  return (((size_t)T * E * 2) + 255) / 256 * 256;
+}
+
 }  // namespace
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" size_t moe_router_backward_workspace_bytes(int T, int E) {
+  if (T < 0 || E < 1) return 0;
+  return router_ws_split(T, E) + 256;
+}
+
+extern "C" moe_status moe_router_backward(const float *dlogits, const void *x, moe_dtype dt, int T,
+                                          int d, const void *w_router, int E, void *dx,
+                                          void *dw_router, void *workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+  if (T < 0 || d < 1 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  // The ping-pong product tiles: 256-wide E and d, at least 96 tokens.
+  if (E % 256 != 0 || d % 256 != 0 || (T > 0 && T < 96)) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * d * 2 >= ((int64_t)1 << 32) || (int64_t)T * E * 2 >= ((int64_t)1 << 32))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0 || (!dx && !dw_router)) return MOE_OK;
+  if (!dlogits || !x || !w_router || !workspace) return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < moe_router_backward_workspace_bytes(T, E)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(workspace) || (dx && !aligned16(dx)) ||
+      (dw_router && !aligned16(dw_router)))
+    return MOE_ERR_INVALID_ARG;
+  uint16_t *dl = static_cast<uint16_t *>(workspace);
+  int32_t *offsets = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + router_ws_split(T, E));
+  const int64_t n = (int64_t)T * E;
+  k_dlogits_bf16<<<dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(
+      dlogits, n, T, dl, offsets);
+  // dx += dlogits w_router: [T, E] x [E, d] (w_router row-major is [K, N]).
+  if (dx && !launch_dgrad_pp(4, dl, T, E, d, offsets, 1, w_router, dx, nullptr, stream))
+    return MOE_ERR_UNSUPPORTED;
+  // dw_router = dlogits^T x: one segment of T rows, [E, d].
+  if (dw_router && !launch_wgrad_pp(dl, x, T, E, d, offsets, 1, dw_router, stream))
+    return MOE_ERR_UNSUPPORTED;
+  return launch_status();
+}
 
 extern "C" moe_status moe_combine_backward(const void *dy, moe_dtype dt, int T, int k, int d,
                                            const int32_t *inv, const float *topk_w,

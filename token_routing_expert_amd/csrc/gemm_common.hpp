@@ -235,7 +235,7 @@ namespace moe {
 // The backward input-gradient products on the ping-pong tiles (defined in
 // grouped_gemm.hip): var 1 stores out = a W_e ([M, K] x [K, N] per expert
 // segment), var 2 applies the SwiGLU backward with the pre-activations gu
-// and writes dgu ([M, 2 N]).  Returns false, launching nothing, when the
+// and writes dgu ([M, 2 N]), var 4 adds the product to out.  Returns false, launching nothing, when the
 // shape is not one the ping-pong tiles serve (few rows per expert, N not a
 // multiple of 256); the caller then uses its own tiles.
 bool launch_dgrad_pp(int var, const void *a, int M, int K, int N, const int32_t *offsets, int G,

@@ -347,7 +347,7 @@ __device__ __forceinline__ int swz_c(int r, int cc) {
 // pre-activations GU ([M, 2 N]) and writes dgu ([M, 2 N]) to C.  3 is a
 // weight gradient, C[e] = A[seg e]^T B[seg e] ([G, Mdim, N], Mdim passed as
 // a_rows): both operands are the segment's rows, staged column-contiguous,
-// and the reduction runs over the segment.
+// and the reduction runs over the segment.  4 is 1 adding the product to C.
 template <bool BF16, int BM, int BR, int SA, int SB, int CPR, int DA, bool SWIGLU, bool SPLIT,
           bool SAVE = false, int VAR = 0>
 __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
@@ -724,6 +724,24 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
           put(static_cast<uint16_t *>(C) + (int64_t)tile.expert * a_rows * N, N, rblk, col, val);
           continue;
         }
+        if constexpr (VAR == 4) {
+          // C += product: each lane reads the pair of columns it then writes.
+          const int c0 = col & ~1;
+          uint32_t *out = static_cast<uint32_t *>(C);
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {
+            const float mine = odd ? val[v + 1] : val[v];
+            const float give = odd ? val[v] : val[v + 1];
+            const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0xB1, 0xF, 0xF, false));
+            const int row = rblk + 8 * (v >> 2) + row_l + (v & 3) + (odd ? 1 : 0);
+            if (row < hi) {
+              const int64_t at = ((int64_t)row * N + c0) >> 1;
+              const uint32_t old = out[at];
+              out[at] = pack_bf16x2(bf16_lo(old) + (odd ? got : mine), bf16_hi(old) + (odd ? mine : got));
+            }
+          }
+          continue;
+        }
         put(C, N, rblk, col, val);
         if constexpr (SAVE && SWIGLU) {
           // Pre-activations for the backward: gate at column col, up at
@@ -965,9 +983,11 @@ bool launch_dgrad_pp(int var, const void *a, int M, int K, int N, const int32_t 
   if (f == Family::Small || N % 256 != 0 || K % 64 != 0) return false;
   if (f == Family::Medium) {
     if (var == 2) launch_dgrad<2, G2Medium>(a, M, K, N, offsets, G, w, out, gu, stream);
+    else if (var == 4) launch_dgrad<4, G2Medium>(a, M, K, N, offsets, G, w, out, gu, stream);
     else launch_dgrad<1, G2Medium>(a, M, K, N, offsets, G, w, out, gu, stream);
   } else {
     if (var == 2) launch_dgrad<2, G2Large>(a, M, K, N, offsets, G, w, out, gu, stream);
+    else if (var == 4) launch_dgrad<4, G2Large>(a, M, K, N, offsets, G, w, out, gu, stream);
     else launch_dgrad<1, G2Large>(a, M, K, N, offsets, G, w, out, gu, stream);
   }
   return true;

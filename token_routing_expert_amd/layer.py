@@ -11,6 +11,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import (MoeError, moe_combine_backward, moe_gate_backward, moe_grouped_down,
+               moe_router_backward,
                moe_grouped_down_backward, moe_grouped_gate_up, moe_grouped_gate_up_backward,
                moe_grouped_gate_up_gather, moe_grouped_gate_up_save, moe_grouped_swiglu,
                moe_grouped_weight_grad, moe_permute, moe_permute_workspace_bytes, moe_route_topk,
@@ -86,8 +87,6 @@ class MoeLayer:
         import torch
         self.cfg = cfg
         self.train = bool(train)
-        if self.train and w_router is not None:
-            raise MoeError("train=True with a router product: its backward is not built")
         self.fused_gather = fused_gather
         if merge_shared and not (fused_gather and cfg.shared):
             raise ValueError("merge_shared needs the fused-gather path and a shared expert")
@@ -283,6 +282,11 @@ class MoeLayer:
         if c.gating != "given":
             b["dgate"] = torch.empty((T, k), dtype=torch.float32, device=dev)
             b["dlogits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+        if self.w_router is not None:
+            from . import moe_router_backward_workspace_bytes
+            b["dw_router"] = torch.empty((E, d), dtype=act, device=dev)
+            b["router_ws"] = torch.empty(max(16, moe_router_backward_workspace_bytes(T, E)),
+                                         dtype=torch.uint8, device=dev)
         if c.shared and not self.merge_shared:
             b["sh_dgu"] = torch.empty((T, 2 * ffn), dtype=act, device=dev)
             b["dx_sh"] = torch.empty((T, d), dtype=act, device=dev)
@@ -294,7 +298,7 @@ class MoeLayer:
     # The backward's steps, in order (BACKWARD_STAGES); backward() runs them
     # all.  Each takes the output gradient dy [T, d].
     BACKWARD_STAGES = ("bwd_combine", "bwd_down", "bwd_gate_up", "bwd_wgrad_down",
-                       "bwd_wgrad_gate_up", "bwd_shared", "bwd_dx", "bwd_gates")
+                       "bwd_wgrad_gate_up", "bwd_shared", "bwd_dx", "bwd_gates", "bwd_router")
 
     def _bwd_views(self):
         merged = self.merge_shared
@@ -367,11 +371,21 @@ class MoeLayer:
             moe_gate_backward(self.logits, self.topk_ids, self.topk_w, b["dgate"], c.gating,
                               c.renormalize, b["dlogits"], stream=stream)
 
+    def bwd_router(self, dy, stream=None):
+        """The router product's backward: dx += dlogits w_router, dw_router
+        (nothing without a router)."""
+        if self.w_router is None:
+            return
+        b = self._grad_buffers()
+        moe_router_backward(b["dlogits"], self.x, self.w_router, b["dx"], b["dw_router"],
+                            b["router_ws"], stream=stream)
+
     def backward(self, dy, stream=None):
         """Gradients of the layer at its last forward, for the output gradient
         dy [T, d].  Returns a dict of device tensors: dx, dw13, dw2, and when
         present dgate and dlogits (through the gates), dsh_w13, dsh_w2 (shared
-        expert).  The buffers are reused by the next call."""
+        expert), dw_router (router product; dx then includes its part).  The
+        buffers are reused by the next call."""
         if not self.train:
             raise MoeError("backward() needs a layer built with train=True")
         for name in self.BACKWARD_STAGES:
@@ -387,4 +401,6 @@ class MoeLayer:
                 out.update(dsh_w13=b["dsh_w13"], dsh_w2=b["dsh_w2"])
         if "dgate" in b:
             out.update(dlogits=b["dlogits"], dgate=b["dgate"])
+        if "dw_router" in b:
+            out["dw_router"] = b["dw_router"]
         return out
