@@ -394,3 +394,41 @@ def test_layer_backward_with_router(lib):
              "dw13": blocks_close(host(g["dw13"]).reshape(-1, cfg.ffn, cfg.d),
                                   ref["dw13"].reshape(-1, cfg.ffn, cfg.d), 2e-2, "dw13")}
     print("router_train", {k_: f"{v:.2e}" for k_, v in worst.items()}, flush=True)
+
+
+def test_training_step_graph_replays_bitwise(lib):
+    """Forward + backward captured in one HIP graph (no call allocates,
+    synchronises or writes with a memset once the buffers exist) replays to
+    the eager step's bits, with eager work between the replays."""
+    from token_routing_expert_amd.layer import MoeLayer
+    cfg = inputs.MoeConfig("graph_train", 25, T=512, E=256, k=8, d=256, ffn=256, dtype="bf16",
+                           gating="sigmoid", renormalize=1, n_groups=8, topk_groups=4, shared=True,
+                           w_std=0.05)
+    w13, w2 = inputs.gen_expert_weights(cfg)
+    sh = inputs.gen_expert_weights(cfg, shared=True)
+    L = MoeLayer(cfg, inputs.gen_x(cfg), w13, w2, sh_w13=sh[0], sh_w2=sh[1], device="cuda",
+                 fused_gather=True, w_router=inputs.gen_router_weights(cfg), train=True)
+    dy = dev(to_bf16(np.random.default_rng(6).standard_normal((cfg.T, cfg.d))))
+
+    def step():
+        L.forward()
+        return L.backward(dy)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in out.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        for v in out.values():
+            v.zero_()                # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in out.items():
+            assert torch.equal(v, ref[k]), (i, k)
