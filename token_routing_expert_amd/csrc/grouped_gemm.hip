@@ -961,6 +961,10 @@ moe_status check_shape(moe_dtype dt, int M, int d, int ffn, int G) {
 
 }  // namespace
 
+#ifndef MOE_DGRAD_LONGK
+#define MOE_DGRAD_LONGK 4096   // reduction length from which var 1 uses medium tiles
+#endif
+
 bool launch_wgrad_pp(const void *a, const void *b, int M, int m_dim, int n_dim,
                      const int32_t *offsets, int G, void *out, hipStream_t stream) {
   using Cfg = G2Wgrad;
@@ -981,7 +985,12 @@ bool launch_dgrad_pp(int var, const void *a, int M, int K, int N, const int32_t 
                      const void *w, void *out, const void *gu, hipStream_t stream) {
   const Family f = family_of(M, G, K);
   if (f == Family::Small || N % 256 != 0 || K % 64 != 0) return false;
-  if (f == Family::Medium) {
+  // Like the forward's down product, the first product's input gradient
+  // (var 1: N = d wide, K = 2 ffn) runs faster on the medium tiles' deeper
+  // rings of narrower slices once K is long; the down product's (var 2, with
+  // the SwiGLU epilogue) stays on the large tiles (measured at Mixtral and
+  // EP64-share shapes).
+  if (f == Family::Medium || (var == 1 && K >= MOE_DGRAD_LONGK)) {
     if (var == 2) launch_dgrad<2, G2Medium>(a, M, K, N, offsets, G, w, out, gu, stream);
     else if (var == 4) launch_dgrad<4, G2Medium>(a, M, K, N, offsets, G, w, out, gu, stream);
     else launch_dgrad<1, G2Medium>(a, M, K, N, offsets, G, w, out, gu, stream);
