@@ -402,11 +402,33 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
   // tiles are (expert, m tile, n tile) with n fastest.
   const int mtn = VAR == 3 ? a_rows / BM : 1;
   const int total = VAR == 3 ? G * mtn * ntiles : count_tiles<BM>(offsets, G, M, ntiles);
-  const int band_end = (int)((int64_t)total * (xcd + 1) / kXcds);
+  // Weight gradients (VAR 3) of few experts, or of one expert with far more
+  // rows than the mean, walk the tiles round-robin over the XCDs instead: an
+  // expert's tiles (whose reduction length is its row count) then spread
+  // over every XCD, which keeps the XCDs evenly loaded; consecutive tiles of
+  // an XCD still belong to one expert, since such experts have many tiles.
+  // With many balanced experts the bands keep each expert's rows in one L2.
+  bool rr = false;
+  if constexpr (VAR == 3) {
+    int mx = 0;
+    for (int e = lane_id(); e < G; e += kWave) {
+      const int n = clamp_row(offsets[e + 1], M) - clamp_row(offsets[e], M);
+      mx = n > mx ? n : mx;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const int o = __shfl_xor(mx, off);
+      mx = o > mx ? o : mx;
+    }
+    rr = G <= 16 || (int64_t)uniform(mx) * G > 2 * (int64_t)M;
+  }
+  const int band_end = rr ? total : (int)((int64_t)total * (xcd + 1) / kXcds);
+  const int L0 = rr ? (int)blockIdx.x : (int)((int64_t)total * xcd / kXcds) + (int)(blockIdx.x / kXcds);
+  const int Lstep = rr ? (int)gridDim.x : nj;
 
   int cur_e = 0, cur_base = 0;   // search cursor of find_tile
-  for (int L = (int)((int64_t)total * xcd / kXcds) + (int)(blockIdx.x / kXcds); L < band_end;
-       L += nj) {
+  for (int L = L0; L < band_end;
+       L += Lstep) {
     Tile tile;
     int seg_lo = 0, seg_hi = 0;   // VAR 3: the expert's rows, the reduction of its tile
     if constexpr (VAR == 3) {
