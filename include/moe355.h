@@ -355,7 +355,7 @@ moe_status moe_gate_backward(const float *logits, const int32_t *topk_ids, const
  * s = 1/(1+e^-g); dgu [M, 2 ffn], gate columns then up columns.
  * bf16 only (fp32 accumulation, RNE output).  Errors: INVALID_ARG for NULL
  * or misaligned pointers, M < 0, G < 1; UNSUPPORTED for fp32, d or ffn not
- * a multiple of 128, G > 4096, or operands of 4 GiB or more.
+ * a multiple of 128, G > 1024, or operands of 4 GiB or more.
  */
 moe_status moe_grouped_down_backward(const void *dy_perm, moe_dtype dt, int M, int d, int ffn,
                                      const int32_t *offsets, int G, const void *w2,
@@ -380,7 +380,7 @@ moe_status moe_grouped_gate_up_backward(const void *dgu, moe_dtype dt, int M, in
  * dW_down = weight_grad(dy_perm, h), dW13 = weight_grad(dgu, x, order, k)
  * (the second is [G, 2 ffn, d] = w13's layout).  bf16 only.  Errors:
  * INVALID_ARG for NULL or misaligned pointers, M < 0, G < 1, b_k < 1;
- * UNSUPPORTED for fp32, m_dim or n_dim not a multiple of 128, G > 4096, or
+ * UNSUPPORTED for fp32, m_dim or n_dim not a multiple of 128, G > 1024, or
  * operands of 4 GiB or more.
  */
 moe_status moe_grouped_weight_grad(const void *a, const void *b, moe_dtype dt, int M, int m_dim,

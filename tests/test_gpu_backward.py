@@ -280,6 +280,29 @@ def test_weight_grad_of_no_rows_is_zero(lib):
     assert torch.count_nonzero(out).item() == 0
 
 
+@pytest.mark.parametrize("m,n", [(128, 256), (256, 512)])
+def test_weight_grad_of_empty_segments_is_zero_on_both_kernels(lib, m, n):
+    """Experts with no rows get zero gradients on the 4-wave tiles (m = 128)
+    and on the ping-pong tiles (m, n multiples of 256), next to experts that
+    have rows."""
+    sizes = [0, 70, 0, 300, 0]
+    M = sum(sizes)
+    rng = np.random.default_rng(17)
+    a = to_bf16(rng.standard_normal((M, m)))
+    b = to_bf16(rng.standard_normal((M, n)))
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    out = torch.full((len(sizes), m, n), 3.0, dtype=torch.bfloat16, device="cuda")
+    lib.moe_grouped_weight_grad(dev(a), dev(b), dev(offsets), out)
+    torch.cuda.synchronize()
+    got = host(out)
+    ref = oracle.weight_grad(a, b, offsets)
+    for e, k in enumerate(sizes):
+        if k == 0:
+            assert np.all(got[e] == 0)
+        else:
+            rows_close(got[e], ref[e], 2e-2, f"dW[{e}]")
+
+
 def test_unit_gate_combine_sums_rows(lib):
     """moe_unpermute_combine with no gates is the permute's backward: each
     token gets the sum of its k rows (plus the shared row)."""
