@@ -353,9 +353,10 @@ moe_status moe_gate_backward(const float *logits, const int32_t *topk_ids, const
  * forward's pre-activations (moe_grouped_gate_up_save),
  *     dgu[p] = (dh u SiLU'(g), dh SiLU(g)),   SiLU'(g) = s (1 + g (1 - s)),
  * s = 1/(1+e^-g); dgu [M, 2 ffn], gate columns then up columns.
- * bf16 only (fp32 accumulation, RNE output).  Errors: INVALID_ARG for NULL
- * or misaligned pointers, M < 0, G < 1; UNSUPPORTED for fp32, d or ffn not
- * a multiple of 128, G > 1024, or operands of 4 GiB or more.
+ * bf16 or fp32 (fp32 accumulation; bf16 outputs rounded to nearest even).
+ * Errors: INVALID_ARG for NULL or misaligned pointers, M < 0, G < 1, an
+ * unknown dtype; UNSUPPORTED for d or ffn not a multiple of 128, G > 1024,
+ * or operands of 4 GiB or more.
  */
 moe_status moe_grouped_down_backward(const void *dy_perm, moe_dtype dt, int M, int d, int ffn,
                                      const int32_t *offsets, int G, const void *w2,
@@ -366,7 +367,7 @@ moe_status moe_grouped_down_backward(const void *dy_perm, moe_dtype dt, int M, i
  * dgu [M, 2 ffn] W13,e per segment, with W13,e = w13[e] read as [2 ffn, d]
  * (gate rows then up rows).  The token gradient is then
  * moe_unpermute_combine(dx_perm, inv, NULL gates) (+ the shared expert's).
- * bf16 only; errors as moe_grouped_down_backward.
+ * bf16 or fp32; errors as moe_grouped_down_backward.
  */
 moe_status moe_grouped_gate_up_backward(const void *dgu, moe_dtype dt, int M, int d, int ffn,
                                         const int32_t *offsets, int G, const void *w13,
@@ -378,10 +379,10 @@ moe_status moe_grouped_gate_up_backward(const void *dgu, moe_dtype dt, int M, in
  * where row p of b is b[b_order[p] / b_k] (b has b_rows rows), or b[p] when
  * b_order is NULL (then b has M rows).  An empty segment gives zeros.  Uses:
  * dW_down = weight_grad(dy_perm, h), dW13 = weight_grad(dgu, x, order, k)
- * (the second is [G, 2 ffn, d] = w13's layout).  bf16 only.  Errors:
- * INVALID_ARG for NULL or misaligned pointers, M < 0, G < 1, b_k < 1;
- * UNSUPPORTED for fp32, m_dim or n_dim not a multiple of 128, G > 1024, or
- * operands of 4 GiB or more.
+ * (the second is [G, 2 ffn, d] = w13's layout).  bf16 or fp32.  Errors:
+ * INVALID_ARG for NULL or misaligned pointers, M < 0, G < 1, b_k < 1, an
+ * unknown dtype; UNSUPPORTED for m_dim or n_dim not a multiple of 128,
+ * G > 1024, or operands of 4 GiB or more.
  */
 moe_status moe_grouped_weight_grad(const void *a, const void *b, moe_dtype dt, int M, int m_dim,
                                    int n_dim, const int32_t *offsets, int G,

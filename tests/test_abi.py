@@ -200,7 +200,7 @@ def test_backward_validation(lib):
     for g in (lib.moe_grouped_down_backward, lib.moe_grouped_gate_up_backward):
         extra = (a,) if g is lib.moe_grouped_down_backward else ()
         #          a  dt M   d    ffn  off G  w  [gu] out stream
-        assert g(a, 0, 64, 128, 256, a, 4, a, *extra, a, NULL) == UNSUPPORTED   # fp32
+        assert g(a, 7, 64, 128, 256, a, 4, a, *extra, a, NULL) == INVALID       # dtype
         assert g(a, 1, 64, 96, 256, a, 4, a, *extra, a, NULL) == UNSUPPORTED    # d % 128
         assert g(a, 1, 64, 128, 200, a, 4, a, *extra, a, NULL) == UNSUPPORTED   # ffn % 128
         assert g(a, 1, 64, 128, 256, a, 0, a, *extra, a, NULL) == INVALID       # G < 1
@@ -209,7 +209,7 @@ def test_backward_validation(lib):
         assert g(a, 1, 0, 128, 256, NULL, 4, NULL, *((NULL,) if extra else ()), NULL, NULL) == 0
     g = lib.moe_grouped_weight_grad
     #       a  b  dt M   m    n    off G  order bk brows c  stream
-    assert g(a, a, 0, 64, 128, 256, a, 4, NULL, 1, 0, a, NULL) == UNSUPPORTED   # fp32
+    assert g(a, a, 7, 64, 128, 256, a, 4, NULL, 1, 0, a, NULL) == INVALID       # dtype
     assert g(a, a, 1, 64, 96, 256, a, 4, NULL, 1, 0, a, NULL) == UNSUPPORTED    # m % 128
     assert g(a, a, 1, 64, 128, 256, a, 4, NULL, 0, 0, a, NULL) == INVALID       # b_k < 1
     assert g(a, a, 1, 64, 128, 256, a, 4, a, 2, 0, a, NULL) == INVALID          # b_rows < 1

@@ -82,8 +82,8 @@ def _segments_problem(seed, d, ffn, sizes, dt="bf16"):
     w13, w2 = inputs.gen_expert_weights(cfg)
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     expert = np.repeat(np.arange(G, dtype=np.int32), sizes)
-    dy = to_bf16(np.random.default_rng(seed + 7).standard_normal((M, d)))
-    return x, w13, w2, offsets, expert, dy
+    dy = np.random.default_rng(seed + 7).standard_normal((M, d)).astype(np.float32)
+    return x, w13, w2, offsets, expert, to_bf16(dy) if dt == "bf16" else dy
 
 
 BWD_CASES = [
@@ -197,13 +197,15 @@ def blocks_close(gpu, ref, rel, what=""):
                       rel, what)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("case", BWD_CASES)
-def test_expert_backward_stages(lib, case):
+def test_expert_backward_stages(lib, case, dt):
     """Each backward product against the oracle's step (B4a, B4b, B4c) fed
     the very inputs the GPU step read: the pre-activations, dgu and h that
-    the GPU produced (bf16), the same dy and weights."""
+    the GPU produced, the same dy and weights (fp32: the 4-wave tiles)."""
     d, ffn, sizes = case
-    x, w13, w2, offsets, expert, dy = _segments_problem(11, d, ffn, sizes)
+    bar = 1e-4 if dt == "f32" else 2e-2
+    x, w13, w2, offsets, expert, dy = _segments_problem(11, d, ffn, sizes, dt)
     G = len(sizes)
     xd, w13d, w2d, offd = dev(x), dev(w13), dev(w2), dev(offsets)
     h, gu = lib.moe_grouped_gate_up_save(xd, offd, w13d)
@@ -214,13 +216,13 @@ def test_expert_backward_stages(lib, case):
     torch.cuda.synchronize()
     gu_h, dgu_h, h_h = host(gu), host(dgu), host(h)
     worst = {
-        "dgu": rows_close(dgu_h, oracle.down_backward_rows(dy, expert, w2, gu_h), 2e-2, "dgu"),
-        "dx": rows_close(host(dx), oracle.gate_up_backward_rows(dgu_h, expert, w13), 2e-2, "dx"),
+        "dgu": rows_close(dgu_h, oracle.down_backward_rows(dy, expert, w2, gu_h), bar, "dgu"),
+        "dx": rows_close(host(dx), oracle.gate_up_backward_rows(dgu_h, expert, w13), bar, "dx"),
         "dw2": rows_close(host(dw2).reshape(-1, ffn),
-                          oracle.weight_grad(dy, h_h, offsets).reshape(-1, ffn), 2e-2, "dw2"),
+                          oracle.weight_grad(dy, h_h, offsets).reshape(-1, ffn), bar, "dw2"),
         "dw13": rows_close(host(dw13).reshape(-1, d),
-                           oracle.weight_grad(dgu_h, x, offsets).reshape(-1, d), 2e-2, "dw13")}
-    print(case[:2], {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
+                           oracle.weight_grad(dgu_h, x, offsets).reshape(-1, d), bar, "dw13")}
+    print(dt, case[:2], {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
     empty = [e for e, n in enumerate(sizes) if n == 0]
     assert all(np.all(host(dw2)[e] == 0) and np.all(host(dw13)[e] == 0) for e in empty)
     assert dw13.shape == (G, 2 * ffn, d)
@@ -316,6 +318,31 @@ def test_unit_gate_combine_sums_rows(lib):
     torch.cuda.synchronize()
     ref = oracle.combine(rows, inv, np.ones((T, k), np.float32), sh)
     rows_close(host(y), ref, 2.0 ** -8, "dx")
+
+
+def test_layer_backward_small_fp32(lib):
+    """The small fp32 layer (1,024 tokens, 8 experts, top-2 softmax) trained:
+    every gradient within the fp32 bar of 1e-4 per row (weight gradients per
+    output row) of the oracle's fp64 backward."""
+    from token_routing_expert_amd.layer import MoeLayer
+    cfg = inputs.CONFIGS["small_fp32"]
+    x, logits = inputs.gen_x(cfg), inputs.gen_logits(cfg)
+    w13, w2 = inputs.gen_expert_weights(cfg)
+    dy = np.random.default_rng(8).standard_normal((cfg.T, cfg.d)).astype(np.float32)
+    layer = MoeLayer(cfg, x, w13, w2, logits=logits, device="cuda", fused_gather=True, train=True)
+    layer.forward()
+    g = layer.backward(dev(dy))
+    torch.cuda.synchronize()
+    ids, w = oracle.route(logits, cfg.k, cfg.gating, cfg.renormalize)
+    ref = oracle.layer_backward(x, logits, ids, w, w13, w2, dy, cfg.gating, cfg.renormalize)
+    worst = {"dx": rows_close(host(g["dx"]), ref["dx"], 1e-4, "dx"),
+             "dw13": rows_close(host(g["dw13"]).reshape(-1, cfg.d), ref["dw13"].reshape(-1, cfg.d),
+                                1e-4, "dw13"),
+             "dw2": rows_close(host(g["dw2"]).reshape(-1, cfg.ffn), ref["dw2"].reshape(-1, cfg.ffn),
+                               1e-4, "dw2"),
+             "dlogits": gate_grad_close(host(g["dlogits"]), ref["dlogits"], w,
+                                        host(g["dgate"]).astype(np.float64), 1e-4)}
+    print("small_fp32", {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
 
 
 LAYER_CASES = [

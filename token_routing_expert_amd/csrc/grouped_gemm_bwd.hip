@@ -52,33 +52,57 @@ struct BwdParams {
 // K-contiguous tile (the dgrad's dY or dGU rows): 128 rows x 64 K = 8
 // chunks of 16 bytes per row, chunk cc of row r in slot cc ^ key(r) so an
 // operand read (32 rows at one chunk) spreads over all banks.
-// With 64 K per slice a row is 8 chunks (128 bytes); with 32 K, 4 chunks
-// (64 bytes), and the key is (r / 4) % 4 so that 16 consecutive rows read at
-// one chunk cover all 16 bank positions of 256 bytes.
-template <int KS>
+// A row of a slice is CPR chunks: 8 (128 bytes: 64 bf16 or 32 fp32 of K) or
+// 4 (64 bytes), where the key is (r / 4) % 4 so that 16 consecutive rows read
+// at one chunk cover all 16 bank positions of 256 bytes.
+template <int CPR>
 __device__ __forceinline__ int kc_key(int r) {
-  if constexpr (KS == 64) return (r & 7) ^ ((r >> 3) & 1);
+  if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
   else return (r >> 2) & 3;
 }
-template <int KS>
-__device__ __forceinline__ int kc_slot(int r, int cc) { return r * (KS / 8) + (cc ^ kc_key<KS>(r)); }
+template <int CPR>
+__device__ __forceinline__ int kc_slot(int r, int cc) { return r * CPR + (cc ^ kc_key<CPR>(r)); }
 
 // ---- operand fragments ---------------------------------------------------
 
-// MFMA 32x32x16 operand of 32 rows (row block rb) at k-group q from a
-// K-contiguous tile: lane l gives row l % 32, K 8 (l / 32) .. + 7.
-template <int KS>
+// MFMA operand of 32 rows (row block rb) at k-group q from a K-contiguous
+// tile: lane l gives row l % 32 and the 16-byte chunk 2 q + l / 32 (8 bf16
+// or 4 fp32 K values).
+template <int CPR>
 __device__ __forceinline__ u32x4 frag_kc(const u32x4 *stage, int rb, int q, int lane) {
-  return stage[kc_slot<KS>(rb * 32 + (lane & 31), 2 * q + (lane >> 5))];
+  return stage[kc_slot<CPR>(rb * 32 + (lane & 31), 2 * q + (lane >> 5))];
 }
 
+// fp32: the same operand for 32 columns (block cb) of a column-contiguous
+// tile of W fp32 columns (4 W bytes per K-row, the segment swizzle of
+// cc_byte): lane l gives column l % 32 at the K rows of its chunk,
+// 4 (2 q + l / 32) + i for i = 0..3, read one 4-byte value at a time.
+template <int W>
+__device__ __forceinline__ u32x4 frag_col32(const char *stage, int cb, int q, int lane) {
+  const int col = cb * 32 + (lane & 31);
+  const int sg = col >> 4, in_seg = (col & 15) * 4;
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * (2 * q + (lane >> 5)) + i;
+    out[i] = *reinterpret_cast<const uint32_t *>(stage + r * (4 * W) + ((sg ^ (r & 3)) << 6) + in_seg);
+  }
+  return out;
+}
+
+// c += a b^T over one 16-byte chunk per lane: one bf16 MFMA, or four fp32
+// MFMAs whose K positions are the chunk's four values (the same assignment
+// on both operands, so the sum over K is unchanged).
+template <bool BF16>
 __device__ __forceinline__ void mma(const u32x4 &a, const u32x4 &b, f32x16 &c) {
-  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                              __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float bf16_at(const uint16_t *p, int64_t i) {
-  return __uint_as_float((uint32_t)p[i] << 16);
+  if constexpr (BF16) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[i]), __uint_as_float(b[i]), c, 0, 0, 0);
+  }
 }
 
 // One output tile.
@@ -91,11 +115,14 @@ struct TileB {
 // next tile's first slices load while this tile finishes and stores.  The
 // expert offsets are copied to LDS first, so the tile lookups in the stream
 // read LDS and never wait behind loads in flight.
-template <int MODE, int WM, int S, int kKS, bool GATHER>
+template <int MODE, int WM, int S, int KS, bool GATHER, bool BF16>
 __global__ __launch_bounds__(WM * 128) void k_grouped_gemm_bwd(const BwdParams p) {
   constexpr bool WGRAD = MODE == kWgrad;
+  constexpr int ES = BF16 ? 2 : 4;                    // element bytes
+  constexpr int kKS = BF16 ? KS : KS / 2;             // K per slice: the same bytes per row
+  constexpr int CPR = kKS * ES / 16;                  // chunks per K-contiguous row
   constexpr int NW = 2 * WM, BM = 64 * WM;
-  constexpr int A_BYTES = BM * kKS * 2, B_BYTES = kKS * kBN * 2, STAGE = A_BYTES + B_BYTES;
+  constexpr int A_BYTES = BM * kKS * ES, B_BYTES = kKS * kBN * ES, STAGE = A_BYTES + B_BYTES;
   constexpr int A_PW = A_BYTES / 1024 / NW, B_PW = B_BYTES / 1024 / NW;   // DMA groups per wave
   constexpr int LPS = A_PW + B_PW;                                       // loads per slice per wave
   static_assert(A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES, "DMA split");
@@ -170,29 +197,33 @@ __global__ __launch_bounds__(WM * 128) void k_grouped_gemm_bwd(const BwdParams p
     for (int r = 0; r < A_PW; ++r) {
       const int g = wave + NW * r;
       if constexpr (WGRAD) {
+        // Column-contiguous stage of BM columns: cc_lane in 2-byte units of
+        // BM ES / 2 columns, so the element column is col 2 / ES.
         int krow, col;
-        cc_lane<BM>(g, lane, krow, col);
-        const uint32_t off = ((uint32_t)(kt * kKS + krow) * (uint32_t)p.Mdim + (uint32_t)(ti.m0 + col)) * 2u;
-        buffer_load_lds16(static_cast<const char *>(p.a) + (int64_t)ti.lo * p.Mdim * 2,
-                          (uint32_t)((int64_t)(ti.hi - ti.lo) * p.Mdim * 2), sa + g * 64, off, 0);
+        cc_lane<BM * ES / 2>(g, lane, krow, col);
+        col = col * 2 / ES;
+        const uint32_t off = ((uint32_t)(kt * kKS + krow) * (uint32_t)p.Mdim + (uint32_t)(ti.m0 + col)) * (uint32_t)ES;
+        buffer_load_lds16(static_cast<const char *>(p.a) + (int64_t)ti.lo * p.Mdim * ES,
+                          (uint32_t)((int64_t)(ti.hi - ti.lo) * p.Mdim * ES), sa + g * 64, off, 0);
       } else {
-        // One group: 1024 / (2 kKS) rows; lane l fills row l / CPR of it at
+        // One group: 1024 / (16 CPR) rows; lane l fills row l / CPR of it at
         // slot l % CPR, which holds chunk (l % CPR) ^ key(row).
-        constexpr int CPR = kKS / 8, RPG = 64 / CPR;
+        constexpr int RPG = 64 / CPR;
         const int lr = g * RPG + lane / CPR;
         int row = ti.m0 + lr;
         row = row < ti.hi ? row : ti.hi - 1;
-        const uint32_t chunk = (uint32_t)(lane % CPR) ^ (uint32_t)kc_key<kKS>(lr);
-        const uint32_t off = (uint32_t)row * (uint32_t)p.K * 2u + (chunk << 4);
-        buffer_load_lds16(p.a, (uint32_t)((int64_t)p.R * p.K * 2), sa + g * 64, off,
-                          (uint32_t)kt * kKS * 2u);
+        const uint32_t chunk = (uint32_t)(lane % CPR) ^ (uint32_t)kc_key<CPR>(lr);
+        const uint32_t off = (uint32_t)row * (uint32_t)p.K * (uint32_t)ES + (chunk << 4);
+        buffer_load_lds16(p.a, (uint32_t)((int64_t)p.R * p.K * ES), sa + g * 64, off,
+                          (uint32_t)kt * kKS * (uint32_t)ES);
       }
     }
 #pragma unroll
     for (int r = 0; r < B_PW; ++r) {
       const int g = wave + NW * r;
       int krow, col;
-      cc_lane<kBN>(g, lane, krow, col);
+      cc_lane<kBN * ES / 2>(g, lane, krow, col);
+      col = col * 2 / ES;
       if constexpr (WGRAD) {
         int row = ti.lo + kt * kKS + krow;
         row = row < ti.hi ? row : ti.hi - 1;
@@ -201,12 +232,12 @@ __global__ __launch_bounds__(WM * 128) void k_grouped_gemm_bwd(const BwdParams p
           src = (uint32_t)p.gather[row] / (uint32_t)p.gk;
           src = src < (uint32_t)p.b_rows ? src : (uint32_t)p.b_rows - 1u;
         }
-        buffer_load_lds16(p.b, (uint32_t)((int64_t)p.b_rows * p.N * 2), sb + g * 64,
-                          (src * (uint32_t)p.N + (uint32_t)(ti.n0 + col)) * 2u, 0);
+        buffer_load_lds16(p.b, (uint32_t)((int64_t)p.b_rows * p.N * ES), sb + g * 64,
+                          (src * (uint32_t)p.N + (uint32_t)(ti.n0 + col)) * (uint32_t)ES, 0);
       } else {
-        buffer_load_lds16(static_cast<const char *>(p.b) + (int64_t)ti.e * p.K * p.N * 2,
-                          (uint32_t)((int64_t)p.K * p.N * 2), sb + g * 64,
-                          ((uint32_t)(kt * kKS + krow) * (uint32_t)p.N + (uint32_t)(ti.n0 + col)) * 2u, 0);
+        buffer_load_lds16(static_cast<const char *>(p.b) + (int64_t)ti.e * p.K * p.N * ES,
+                          (uint32_t)((int64_t)p.K * p.N * ES), sb + g * 64,
+                          ((uint32_t)(kt * kKS + krow) * (uint32_t)p.N + (uint32_t)(ti.n0 + col)) * (uint32_t)ES, 0);
       }
     }
     ++issued;
@@ -251,13 +282,15 @@ __global__ __launch_bounds__(WM * 128) void k_grouped_gemm_bwd(const BwdParams p
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           if constexpr (WGRAD)
-            fa[buf][i] = frag_tr<BM>(stage, 2 * wm + i, q, lane);
+            fa[buf][i] = BF16 ? frag_tr<BM>(stage, 2 * wm + i, q, lane)
+                              : frag_col32<BM>(stage, 2 * wm + i, q, lane);
           else
-            fa[buf][i] = frag_kc<kKS>(sa, 2 * wm + i, q, lane);
-          fb[buf][i] = frag_tr<kBN>(sb, 2 * wn + i, q, lane);
+            fa[buf][i] = frag_kc<CPR>(sa, 2 * wm + i, q, lane);
+          fb[buf][i] = BF16 ? frag_tr<kBN>(sb, 2 * wn + i, q, lane)
+                            : frag_col32<kBN>(sb, 2 * wn + i, q, lane);
         }
       };
-      constexpr int NQ = kKS / 16;   // k-groups per slice
+      constexpr int NQ = kKS * ES / 32;   // k-groups (one 16-byte chunk per lane) per slice
       fetch(0, 0);
       if (Li < band_end) issue();
 #pragma unroll
@@ -266,7 +299,7 @@ __global__ __launch_bounds__(WM * 128) void k_grouped_gemm_bwd(const BwdParams p
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) mma(fa[q & 1][i], fb[q & 1][j], acc[i][j]);
+          for (int j = 0; j < 2; ++j) mma<BF16>(fa[q & 1][i], fb[q & 1][j], acc[i][j]);
       }
       ++consumed;
       ++ktc;
@@ -279,8 +312,39 @@ __global__ __launch_bounds__(WM * 128) void k_grouped_gemm_bwd(const BwdParams p
     // each holds two adjacent columns of one row (even lanes rows v % 4 =
     // 0, 2, odd lanes 1, 3) and moves them with one 4-byte access.
     const int row_hi = WGRAD ? tc.m0 + BM : tc.hi;
+    if constexpr (!BF16) {
+      // fp32: every lane stores its own values.
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 2; ++i) {
+        const int rblk = tc.m0 + (2 * wm + i) * 32;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = tc.n0 + (2 * wn + j) * 32 + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = rblk + 8 * (v >> 2) + row_l + (v & 3);
+            if (row < row_hi) {
+              const float x = acc[i][j][v];
+              if constexpr (MODE == kDgradSwiglu) {
+                const int64_t base = (int64_t)row * 2 * p.N + col;
+                const float g = static_cast<const float *>(p.gu)[base];
+                const float u = static_cast<const float *>(p.gu)[base + p.N];
+                const float s = 1.0f / (1.0f + __expf(-g));
+                static_cast<float *>(p.c)[base] = x * u * (s * (1.0f + g * (1.0f - s)));
+                static_cast<float *>(p.c)[base + p.N] = x * (g * s);
+              } else {
+                const int64_t base =
+                    WGRAD ? ((int64_t)tc.e * p.Mdim + row) * p.N + col : (int64_t)row * p.N + col;
+                static_cast<float *>(p.c)[base] = x;
+              }
+            }
+            acc[i][j][v] = 0.0f;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < (BF16 ? 2 : 0); ++i) {
       const int rblk = tc.m0 + (2 * wm + i) * 32;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -343,13 +407,21 @@ constexpr int kKS = MOE_BWD_KS;
 
 constexpr int kTileM = 64 * MOE_BWD_WM;
 
-template <int MODE, bool GATHER = false>
-void launch(const BwdParams &prm, hipStream_t stream, int64_t tiles) {
+template <int MODE, bool GATHER, bool BF16>
+void launch_t(const BwdParams &prm, hipStream_t stream, int64_t tiles) {
   constexpr int WM = MOE_BWD_WM, S = MOE_BWD_STAGES;
-  auto kern = k_grouped_gemm_bwd<MODE, WM, S, kKS, GATHER>;
+  auto kern = k_grouped_gemm_bwd<MODE, WM, S, kKS, GATHER, BF16>;
   static int per_cu = 0;
   const int grid = persistent_grid((const void *)kern, WM * 128, per_cu, tiles);
   kern<<<dim3(grid), dim3(WM * 128), 0, stream>>>(prm);
+}
+
+template <int MODE, bool GATHER = false>
+void launch(const BwdParams &prm, hipStream_t stream, int64_t tiles, bool bf16) {
+  if (bf16)
+    launch_t<MODE, GATHER, true>(prm, stream, tiles);
+  else
+    launch_t<MODE, GATHER, false>(prm, stream, tiles);
 }
 
 // Shape checks common to the entry points.  The kernels index their
@@ -357,10 +429,9 @@ void launch(const BwdParams &prm, hipStream_t stream, int64_t tiles) {
 moe_status check_bwd(moe_dtype dt, int M, int d, int ffn, int G) {
   if (M < 0 || G < 1 || d < 1 || ffn < 1) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d % kBN != 0 || ffn % kBN != 0 || G > kMaxG) return MOE_ERR_UNSUPPORTED;
-  const int64_t big = (int64_t)1 << 32;
-  if ((int64_t)M * 2 * ffn * 2 >= big || (int64_t)M * d * 2 >= big || (int64_t)2 * ffn * d * 2 >= big)
+  const int64_t big = (int64_t)1 << 32, es = dt == MOE_F32 ? 4 : 2;
+  if ((int64_t)M * 2 * ffn * es >= big || (int64_t)M * d * es >= big || (int64_t)2 * ffn * d * es >= big)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -380,9 +451,12 @@ extern "C" moe_status moe_grouped_down_backward(const void *dy_perm, moe_dtype d
   if (!aligned16(dy_perm) || !aligned16(w2) || !aligned16(gu) || !aligned16(dgu))
     return MOE_ERR_INVALID_ARG;
   // dh = dY Wd_e: K = d, N = ffn; Wd_e is [d, ffn], N-contiguous.
-  if (launch_dgrad_pp(2, dy_perm, M, d, ffn, offsets, G, w2, dgu, gu, stream)) return launch_status();
+  const bool bf16 = dt == MOE_BF16;
+  if (bf16 && launch_dgrad_pp(2, dy_perm, M, d, ffn, offsets, G, w2, dgu, gu, stream))
+    return launch_status();
   BwdParams prm{dy_perm, w2, dgu, gu, offsets, nullptr, G, M, d, 0, ffn, 1, 0};
-  launch<kDgradSwiglu>(prm, stream, ((int64_t)M + kTileM - 1) / kTileM * (ffn / kBN) + (int64_t)G * (ffn / kBN));
+  launch<kDgradSwiglu>(prm, stream, ((int64_t)M + kTileM - 1) / kTileM * (ffn / kBN) + (int64_t)G * (ffn / kBN),
+                       bf16);
   return launch_status();
 }
 
@@ -395,10 +469,12 @@ extern "C" moe_status moe_grouped_gate_up_backward(const void *dgu, moe_dtype dt
   if (!dgu || !offsets || !w13 || !dx_perm) return MOE_ERR_INVALID_ARG;
   if (!aligned16(dgu) || !aligned16(w13) || !aligned16(dx_perm)) return MOE_ERR_INVALID_ARG;
   // dX = dGU W13_e: K = 2 ffn (gate rows, then up rows), N = d.
-  if (launch_dgrad_pp(1, dgu, M, 2 * ffn, d, offsets, G, w13, dx_perm, nullptr, stream))
+  const bool bf16 = dt == MOE_BF16;
+  if (bf16 && launch_dgrad_pp(1, dgu, M, 2 * ffn, d, offsets, G, w13, dx_perm, nullptr, stream))
     return launch_status();
   BwdParams prm{dgu, w13, dx_perm, nullptr, offsets, nullptr, G, M, 2 * ffn, 0, d, 1, 0};
-  launch<kDgradStore>(prm, stream, ((int64_t)M + kTileM - 1) / kTileM * (d / kBN) + (int64_t)G * (d / kBN));
+  launch<kDgradStore>(prm, stream, ((int64_t)M + kTileM - 1) / kTileM * (d / kBN) + (int64_t)G * (d / kBN),
+                      bf16);
   return launch_status();
 }
 
@@ -408,23 +484,23 @@ extern "C" moe_status moe_grouped_weight_grad(const void *a, const void *b, moe_
                                               void *c, hipStream_t stream) {
   if (M < 0 || G < 1 || m_dim < 1 || n_dim < 1 || b_k < 1) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (m_dim % kTileM != 0 || n_dim % kBN != 0 || G > kMaxG) return MOE_ERR_UNSUPPORTED;
   if (!b_order) b_rows = M;
   if (b_rows < 1 && M > 0) return MOE_ERR_INVALID_ARG;
-  const int64_t big = (int64_t)1 << 32;
-  if ((int64_t)(M + kKS) * m_dim * 2 >= big || (int64_t)b_rows * n_dim * 2 >= big ||
+  const int64_t big = (int64_t)1 << 32, es = dt == MOE_F32 ? 4 : 2;
+  if ((int64_t)(M + kKS) * m_dim * es >= big || (int64_t)b_rows * n_dim * es >= big ||
       (int64_t)G * m_dim * n_dim >= ((int64_t)1 << 40))
     return MOE_ERR_UNSUPPORTED;
   // With no rows the operands are never read (every expert's gradient is 0).
   if (!offsets || !c || (M > 0 && (!a || !b))) return MOE_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return MOE_ERR_INVALID_ARG;
-  if (!b_order && launch_wgrad_pp(a, b, M, m_dim, n_dim, offsets, G, c, stream))
+  const bool bf16 = dt == MOE_BF16;
+  if (bf16 && !b_order && launch_wgrad_pp(a, b, M, m_dim, n_dim, offsets, G, c, stream))
     return launch_status();
   BwdParams prm{a, b, c, nullptr, offsets, b_order, G, M, 0, m_dim, n_dim, b_k, b_rows};
   if (b_order)
-    launch<kWgrad, true>(prm, stream, (int64_t)G * (m_dim / kTileM) * (n_dim / kBN));
+    launch<kWgrad, true>(prm, stream, (int64_t)G * (m_dim / kTileM) * (n_dim / kBN), bf16);
   else
-    launch<kWgrad>(prm, stream, (int64_t)G * (m_dim / kTileM) * (n_dim / kBN));
+    launch<kWgrad>(prm, stream, (int64_t)G * (m_dim / kTileM) * (n_dim / kBN), bf16);
   return launch_status();
 }

@@ -72,7 +72,8 @@ class MoeLayer:
 
     train=True keeps what the backward needs: the first product also stores
     the pre-activations gu, and ``backward(dy)`` then returns the gradients
-    of the layer (bf16 only).  The packed rows X[order] are kept too (the
+    of the layer (bf16 or fp32; with a router product bf16).  The packed
+    rows X[order] are kept too (the
     permute writes them even on the fused-gather path; not with
     merge_shared): the first product's weight gradient reads them as
     contiguous rows.  The backward is the forward's steps in
@@ -162,8 +163,8 @@ class MoeLayer:
         else:
             self.y_sh = None
         if self.train:
-            if act != torch.bfloat16:
-                raise MoeError("train=True needs bf16 activations and weights")
+            if act != torch.bfloat16 and self.w_router is not None:
+                raise MoeError("train=True with a router product needs bf16")
             self.gu = torch.empty((self.h.shape[0], 2 * ffn), dtype=act, device=dev)
             if cfg.shared and not self.merge_shared:
                 self.sh_gu = torch.empty((T, 2 * ffn), dtype=act, device=dev)
