@@ -169,6 +169,27 @@ def cpu_baseline(cfg, data, budget_s=15.0, max_tokens=2048):
     }
 
 
+TRAIN_TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                  "dsv3_prefill_train_wgrad_traffic.json")
+
+
+def measured_train_traffic(workload):
+    """HBM bytes per launch of the first product's weight gradient (dW13) from
+    the committed counter passes of a training step, or None when they were
+    taken on another workload or another kernel source."""
+    import hashlib
+    try:
+        with open(TRAIN_TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(GEMM_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if t.get("workload") != workload or t.get("source_sha256") != sha:
+        return None
+    return int(t["bytes_per_launch"])
+
+
 TRAIN_METRIC = ("MoE-layer fwd+bwd tokens/s at DSV3 shape, 1 GPU (training step: forward keeping "
                 "pre-activations, backward to dx, dW and dlogits)")
 
@@ -312,7 +333,7 @@ def run_train(args, cfg, layer, data, stream):
                    "gating": cfg.gating, "shared_experts": int(cfg.shared), "path": args.path,
                    "train": True},
         "roofline": {"kernel": "moe_grouped_weight_grad: dW13 = dgu^T x rows (one launch)", **roof,
-                     "traffic": None, "algorithmic_bytes": wg_bytes, "algorithmic_flops": f_gu,
+                     "traffic": measured_train_traffic(cfg.name), "algorithmic_bytes": wg_bytes, "algorithmic_flops": f_gu,
                      "intensity_flop_per_byte": round(intensity, 1),
                      "ridge_flop_per_byte": round(ridge, 1),
                      "mfma_frac": round(flop_rate / peak, 4),
@@ -388,6 +409,17 @@ def main():
                      train=args.train)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        # A plain device copy of known size: its FETCH_SIZE / WRITE_SIZE counter
+        # readings calibrate the counters of the path's kernels.
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 2, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read, {n} bytes written")
+        del src, dst
+
     if args.train:
         run_train(args, cfg, layer, (x, w13, w2, logits, sh, ids_in, w_in), stream)
         return
@@ -403,17 +435,6 @@ def main():
             getattr(layer, name)()
             if evs is not None:
                 evs[i + 1].record(stream)
-
-    if args.copy_calibration:
-        # A plain device copy of known size: its FETCH_SIZE / WRITE_SIZE counter
-        # readings calibrate the counters of the path's kernels.
-        n = args.copy_calibration << 20
-        src = torch.ones(n // 2, dtype=torch.int16, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy: {n} bytes read, {n} bytes written")
-        del src, dst
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
