@@ -376,7 +376,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the path is one GPU's share of the EP layer and "
-              "this build has no cross-GPU exchange. Run with --gpus 1.", file=sys.stderr)
+              "libmoe355 has no cross-GPU exchange. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
