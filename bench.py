@@ -458,6 +458,22 @@ def main():
     def pct(q):
         return round(step_ev[min(K - 1, int(q * (K - 1) + 0.5))], 4)
 
+    # The same step from cold caches: a 1 GiB fill before each step (outside
+    # its events) evicts the L2s and the 256 MB MALL, so nothing the step
+    # reads is left over from the previous one.
+    n_cold = min(5, K)
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(n_cold)]
+    for i in range(n_cold):
+        scrub.fill_(float(i))
+        step(cold[i])
+    torch.cuda.synchronize()
+    del scrub
+    cold_step = sorted(c[0].elapsed_time(c[-1]) for c in cold)
+    cold_info = {"steps": n_cold, "step_ms_p50": round(cold_step[n_cold // 2], 4),
+                 "stages_ms": {name: round(sum(c[j].elapsed_time(c[j + 1]) for c in cold) / n_cold, 4)
+                               for j, name in enumerate(stages)}}
+
     from token_routing_expert_amd.layer import to_host
     counts = to_host(layer.counts)
     f_gate_up, f_down, f_shared = expert_flops(cfg)
@@ -536,6 +552,7 @@ def main():
         },
         "stages": stage_info,
         "step_ms_events": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
+        "cold_cache": cold_info,
         "load": load_accounting(cfg, counts,
                                 to_host(layer.send_counts) if cfg.n_ep else None),
         "device": torch.cuda.get_device_name(0),
