@@ -370,6 +370,8 @@ def main():
     ap.add_argument("--train", action="store_true",
                     help="time a training step instead: the forward keeping the pre-activations, "
                          "then the backward to dx, the weight gradients and dlogits (bf16 only)")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="after the timed steps, time this many more from cold caches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -461,8 +463,8 @@ def main():
     # The same step from cold caches: a 1 GiB fill before each step (outside
     # its events) evicts the L2s and the 256 MB MALL, so nothing the step
     # reads is left over from the previous one.
-    n_cold = min(5, K)
-    scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    n_cold = min(args.cold_steps, K)
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if n_cold else None
     cold = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(n_cold)]
     for i in range(n_cold):
         scrub.fill_(float(i))
@@ -470,9 +472,11 @@ def main():
     torch.cuda.synchronize()
     del scrub
     cold_step = sorted(c[0].elapsed_time(c[-1]) for c in cold)
-    cold_info = {"steps": n_cold, "step_ms_p50": round(cold_step[n_cold // 2], 4),
-                 "stages_ms": {name: round(sum(c[j].elapsed_time(c[j + 1]) for c in cold) / n_cold, 4)
-                               for j, name in enumerate(stages)}}
+    cold_info = None
+    if n_cold:
+        cold_info = {"steps": n_cold, "step_ms_p50": round(cold_step[n_cold // 2], 4),
+                     "stages_ms": {name: round(sum(c[j].elapsed_time(c[j + 1]) for c in cold) / n_cold, 4)
+                                   for j, name in enumerate(stages)}}
 
     from token_routing_expert_amd.layer import to_host
     counts = to_host(layer.counts)
