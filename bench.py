@@ -485,6 +485,13 @@ def main():
     gather = args.path == "gather"
     b_perm, b_comb = stage_bytes(cfg, gather)
     b_gate_up = gate_up_bytes(cfg, counts, gather)
+    # Route: logits read once, ids and gates written; the send counts read
+    # the ids again and write the n_ep x n_ep matrix.
+    b_route = None
+    if cfg.gating != "given":
+        b_route = cfg.T * (cfg.E * 4 + cfg.k * 8)
+        if cfg.n_ep:
+            b_route += cfg.T * cfg.k * 4 + cfg.n_ep * cfg.n_ep * 4
     if layer.merge_shared:
         # The shared expert runs as one more group of the routed launches.
         f_gate_up += 2 * f_shared // 3
@@ -496,7 +503,8 @@ def main():
     for name in stages:
         ms = stage_ms[name]
         info = {"ms": round(ms, 4)}
-        nbytes = {"permute": b_perm, "combine": b_comb, "gate_up": b_gate_up}.get(name)
+        nbytes = {"permute": b_perm, "combine": b_comb, "gate_up": b_gate_up,
+                  "route": b_route}.get(name)
         flops = {"gate_up": f_gate_up, "down": f_down, "experts_shared": f_shared}.get(name)
         if flops:
             rate = flops / (ms * 1e-3)
