@@ -106,18 +106,21 @@ def load_accounting(cfg, counts, send_counts):
     return out
 
 
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "dsv3_prefill_gate_up_traffic.json")
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 GEMM_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "token_routing_expert_amd",
                            "csrc", "grouped_gemm.hip")
 
 
-def measured_traffic(workload):
-    """HBM bytes per gate/up launch from the committed rocprofv3 counter passes,
-    or None when they were taken on another workload or another kernel source."""
+def measured_traffic(workload, path="gather"):
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter passes
+    of this workload (taken on the default fused-gather path), or None when
+    there are none, they were taken on another kernel source, or the run
+    uses the packed path."""
     import hashlib
+    if path != "gather":
+        return None
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(PROFILES, f"{workload}_gate_up_traffic.json")) as f:
             t = json.load(f)
         with open(GEMM_SOURCE, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
@@ -553,7 +556,7 @@ def main():
             "kernel": ("moe_grouped_gate_up_gather" if gather else "moe_grouped_gate_up")
                       + ": routed gate/up products + SwiGLU (one launch)",
             **roof,
-            "traffic": measured_traffic(cfg.name),
+            "traffic": measured_traffic(cfg.name, args.path),
             "algorithmic_bytes": b_gate_up,
             "algorithmic_flops": f_gate_up,
             "intensity_flop_per_byte": round(intensity, 1),
