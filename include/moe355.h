@@ -247,6 +247,33 @@ moe_status moe_grouped_down(const void *h, moe_dtype dt, int M, int ffn, int d,
                             hipStream_t stream);
 
 /*
+ * One expert's SwiGLU MLP on few rows: the always-active shared expert of a
+ * decode step ("05 -- Expert Parallelism (MoE)", section "Fine-grained vs
+ * coarse experts": DeepSeek-V3 has one shared expert beside its routed ones;
+ * same page, "The serving asymmetry": decode time is weight reads).
+ *   h = SiLU(x W_gate^T) * (x W_up^T),  y = h W_down^T
+ * which is moe_grouped_swiglu with G = 1, computed with each product's
+ * reduction split into K ranges over many workgroups; fp32 partial sums go
+ * to the workspace and are added in a fixed order (split 0 first), so the
+ * result does not depend on scheduling.  It may differ from
+ * moe_grouped_swiglu's in the last bits (another summation order).
+ *   x [M, d], w13 [2, ffn, d] (gate rows, then up rows), w2 [d, ffn] in;
+ *   h [M, ffn] and y [M, d] out; gu [M, 2 ffn] out (optional, NULL skips
+ *   it): the pre-activations (gate, then up) in bf16, for a backward.
+ *   workspace: device memory of at least
+ *   moe_dense_swiglu_workspace_bytes(M, d, ffn) bytes, owned by the caller
+ *   and overwritten.  Calls sharing a workspace must not overlap.
+ * bf16 only.  Errors: INVALID_ARG for M < 0, d or ffn < 1, a null pointer
+ * (other than gu), pointers not 16-byte aligned, or a workspace too small;
+ * UNSUPPORTED for fp32, M > 256, or d or ffn not a multiple of 64.  M = 0
+ * launches nothing.
+ */
+size_t moe_dense_swiglu_workspace_bytes(int M, int d, int ffn);
+moe_status moe_dense_swiglu(const void *x, moe_dtype dt, int M, int d, int ffn, const void *w13,
+                            const void *w2, void *h, void *gu, void *y, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
  * moe_grouped_gate_up with the permute's row copy folded into the product's
  * loads ("Token permutation and grouped GEMMs": X[order] is only ever read by
  * the first expert product, so the rows can be gathered where they are

@@ -231,6 +231,24 @@ def test_router_backward_validation(lib):
     assert f(a, a, 1, 512, 512, a, 256, NULL, NULL, NULL, 0, NULL) == 0      # nothing asked
 
 
+def test_dense_swiglu_validation(lib):
+    a = ctypes.c_void_p(16)
+    ws = lib.moe_dense_swiglu_workspace_bytes(128, 7168, 2048)
+    # gate/up split 8 ways: 8 x 128 x 4096 fp32 partial sums
+    assert ws == 8 * 128 * 4096 * 4
+    f = lib.moe_dense_swiglu
+    #       x  dt M    d    ffn w13 w2 h gu    y  ws bytes stream
+    assert f(a, 0, 128, 256, 128, a, a, a, NULL, a, a, ws, NULL) == UNSUPPORTED   # fp32
+    assert f(a, 1, 257, 256, 128, a, a, a, NULL, a, a, ws, NULL) == UNSUPPORTED   # M > 256
+    assert f(a, 1, 128, 200, 128, a, a, a, NULL, a, a, ws, NULL) == UNSUPPORTED   # d % 64
+    assert f(a, 1, -1, 256, 128, a, a, a, NULL, a, a, ws, NULL) == INVALID
+    small = lib.moe_dense_swiglu_workspace_bytes(128, 256, 128)
+    assert f(a, 1, 128, 256, 128, a, a, a, NULL, a, a, small - 1, NULL) == INVALID
+    assert f(a, 1, 128, 256, 128, a, NULL, a, NULL, a, a, small, NULL) == INVALID  # null w2
+    assert f(a, 1, 128, 256, 128, a, a, a, ctypes.c_void_p(8), a, a, small, NULL) == INVALID  # gu alignment
+    assert f(NULL, 1, 0, 256, 128, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == 0   # no rows
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(moe.MoeError):
         moe.load_library(str(tmp_path / "missing.so"))

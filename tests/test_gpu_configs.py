@@ -155,8 +155,10 @@ def test_row_copy_path_is_bit_identical(case):
 
 
 def test_shared_in_routed_launches_is_bit_identical(case):
-    """With the shared expert as group E of the routed launches the layer
-    output keeps its bits."""
+    """With the shared expert as group E of the routed launches the routed
+    rows keep their bits, and so does the layer output -- unless the separate
+    shared expert ran with split reductions (few tokens: moe_dense_swiglu, a
+    different summation order), where the output agrees within the bf16 bar."""
     from token_routing_expert_amd.layer import MoeLayer, to_host
     cfg, lay = case.cfg, case.layer
     if not cfg.shared:
@@ -165,10 +167,14 @@ def test_shared_in_routed_launches_is_bit_identical(case):
                      sh_w2=lay.sh_w2, fused_gather=True, merge_shared=True)
     other.forward()
     torch.cuda.synchronize()
-    y = to_host(other.y)
+    y, y_perm = to_host(other.y), to_host(other.y_perm)
     del other
     torch.cuda.empty_cache()
-    assert np.array_equal(y.view(np.uint8), case.g["y"].view(np.uint8))
+    assert np.array_equal(y_perm.view(np.uint8), to_host(lay.y_perm).view(np.uint8))
+    if lay.sh_dense:
+        _rows_close(_f64(y), _f64(case.g["y"]), 2e-2)
+    else:
+        assert np.array_equal(y.view(np.uint8), case.g["y"].view(np.uint8))
 
 
 def _host_rows(t, idx):

@@ -523,6 +523,45 @@ def test_grouped_swiglu_shared_expert_form(lib):
     rows_close(as_f64(host(y)), ref, 2e-2)
 
 
+@pytest.mark.parametrize("M,d,ffn", [(1, 256, 128), (77, 256, 384), (128, 1024, 512), (129, 512, 256),
+                                     (256, 448, 192)])
+def test_dense_swiglu_split_reductions(lib, M, d, ffn):
+    """moe_dense_swiglu (one expert, split reductions): y against the oracle's
+    dense SwiGLU MLP and the pre-activations gu against a float64 product,
+    per row within 2e-2 of the row's largest magnitude; the same call twice
+    gives the same bits (fixed summation order).  Shapes: one row, a ragged
+    row block, exactly four row blocks, the second row block of a wave in
+    use (129 and 256 rows), reductions split 1 to 16 ways."""
+    cfg = inputs.MoeConfig("t", 5, T=M, E=1, k=1, d=d, ffn=ffn, dtype="bf16", gating="softmax")
+    a = inputs.gen_x(cfg)
+    w13, w2 = inputs.gen_expert_weights(cfg)
+    ref = oracle.expert_swiglu_rows(a, np.zeros(M, np.int32), w13, w2)
+    xa, w13d, w2d = dev(a), dev(w13), dev(w2)
+    gu = torch.empty((M, 2 * ffn), dtype=torch.bfloat16, device="cuda")
+    y = lib.moe_dense_swiglu(xa, w13d, w2d, gu=gu)
+    y2 = lib.moe_dense_swiglu(xa, w13d, w2d)
+    torch.cuda.synchronize()
+    rows_close(as_f64(host(y)), ref, 2e-2)
+    assert np.array_equal(host(y).view(np.uint16), host(y2).view(np.uint16))
+    xf, wf = as_f64(a), as_f64(w13)[0]
+    pre = np.concatenate([xf @ wf[0].T, xf @ wf[1].T], axis=1)
+    rows_close(as_f64(host(gu)), pre, 2e-2)
+
+
+def test_dense_swiglu_errors(lib):
+    cfg = inputs.MoeConfig("t", 5, T=8, E=1, k=1, d=256, ffn=128, dtype="bf16", gating="softmax")
+    x = dev(inputs.gen_x(cfg))
+    w13, w2 = (dev(w) for w in inputs.gen_expert_weights(cfg))
+    big = torch.zeros((257, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(lib.MoeError, match="UNSUPPORTED|unsupported"):
+        lib.moe_dense_swiglu(big, w13, w2)
+    small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(lib.MoeError):
+        lib.moe_dense_swiglu(x, w13, w2, workspace=small_ws)
+    y = lib.moe_dense_swiglu(x[:0], w13, w2)   # no rows: nothing to do
+    assert y.shape == (0, 256)
+
+
 def test_grouped_swiglu_errors(lib):
     a = torch.zeros((4, 96), dtype=torch.bfloat16, device="cuda")
     w13 = torch.zeros((1, 2, 128, 96), dtype=torch.bfloat16, device="cuda")

@@ -26,7 +26,7 @@ EXPORTS = ("moe_status_string", "moe_route_topk", "moe_route_topk_biased", "moe_
            "moe_unpermute_combine", "moe_grouped_gate_up_save", "moe_combine_backward",
            "moe_gate_backward", "moe_grouped_down_backward", "moe_grouped_gate_up_backward",
            "moe_grouped_weight_grad", "moe_router_backward_workspace_bytes",
-           "moe_router_backward")
+           "moe_router_backward", "moe_dense_swiglu_workspace_bytes", "moe_dense_swiglu")
 
 
 class MoeError(RuntimeError):
@@ -70,12 +70,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_router_backward_workspace_bytes.argtypes = [i32, i32]
     lib.moe_router_backward_workspace_bytes.restype = sz
     lib.moe_router_backward.argtypes = [P, P, i32, i32, i32, P, i32, P, P, P, sz, P]
+    lib.moe_dense_swiglu_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.moe_dense_swiglu_workspace_bytes.restype = sz
+    lib.moe_dense_swiglu.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, sz, P]
     for name in ("moe_route_topk", "moe_route_topk_biased", "moe_router_logits",
                  "moe_router_bias_update", "moe_sigmoid_pinned", "moe_send_counts", "moe_permute",
                  "moe_grouped_swiglu", "moe_grouped_gate_up", "moe_grouped_gate_up_gather",
                  "moe_grouped_down", "moe_unpermute_combine", "moe_grouped_gate_up_save",
                  "moe_combine_backward", "moe_gate_backward", "moe_grouped_down_backward",
-                 "moe_grouped_gate_up_backward", "moe_grouped_weight_grad", "moe_router_backward"):
+                 "moe_grouped_gate_up_backward", "moe_grouped_weight_grad", "moe_router_backward",
+                 "moe_dense_swiglu"):
         getattr(lib, name).restype = i32
     if path == LIB_PATH:
         _lib = lib
@@ -265,6 +269,41 @@ def moe_grouped_swiglu(a, offsets, w13, w2, h=None, y=None, stream=None):
     _check(load_library().moe_grouped_swiglu(_ptr(a), _dtype_code(a), M, d, ffn, _ptr(offsets),
                                              G, _ptr(w13), _ptr(w2), _ptr(h), _ptr(y),
                                              _stream(stream)), "moe_grouped_swiglu")
+    return y
+
+
+def moe_dense_swiglu_workspace_bytes(M, d, ffn) -> int:
+    return int(load_library().moe_dense_swiglu_workspace_bytes(M, d, ffn))
+
+
+def moe_dense_swiglu(x, w13, w2, h=None, gu=None, y=None, workspace=None, stream=None):
+    """One expert's SwiGLU MLP on few rows (at most 256) with split reductions:
+    x [M, d], w13 [2, ffn, d] (or [1, 2, ffn, d]), w2 [d, ffn] (or [1, d, ffn]);
+    returns y [M, d].  gu, when given, receives the pre-activations [M, 2 ffn]."""
+    torch = _torch()
+    _dev(x, "x", (torch.bfloat16,))
+    w13 = w13[0] if w13.dim() == 4 else w13
+    w2 = w2[0] if w2.dim() == 3 else w2
+    _dev(w13, "w13", (x.dtype,))
+    _dev(w2, "w2", (x.dtype,))
+    M, d = x.shape
+    two, ffn, d2 = w13.shape
+    if two != 2 or d2 != d or tuple(w2.shape) != (d, ffn):
+        raise MoeError("moe_dense_swiglu: inconsistent shapes")
+    h = torch.empty((M, ffn), dtype=x.dtype, device=x.device) if h is None else h
+    y = torch.empty((M, d), dtype=x.dtype, device=x.device) if y is None else y
+    _dev(h, "h", (x.dtype,))
+    _dev(y, "y", (x.dtype,))
+    if gu is not None:
+        _dev(gu, "gu", (x.dtype,))
+    nbytes = moe_dense_swiglu_workspace_bytes(M, d, ffn)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace", (torch.uint8,))
+    _check(load_library().moe_dense_swiglu(
+        _ptr(x), _dtype_code(x), M, d, ffn, _ptr(w13), _ptr(w2), _ptr(h),
+        _ptr(gu) if gu is not None else None, _ptr(y), _ptr(workspace), workspace.numel(),
+        _stream(stream)), "moe_dense_swiglu")
     return y
 
 

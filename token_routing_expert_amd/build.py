@@ -20,6 +20,7 @@ LIB = os.path.join(PKG, "libmoe355.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["route.hip", "router.hip", "permute.hip", "grouped_gemm.hip", "grouped_gemm_bwd.hip",
+           "dense_splitk.hip",
            "combine.hip", "backward.hip"]
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,

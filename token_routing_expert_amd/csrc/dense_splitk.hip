@@ -1,0 +1,206 @@
+// One expert's SwiGLU MLP over few rows, with each reduction split over many
+// workgroups: the shared expert of a decode step.
+//
+// "05 -- Expert Parallelism (MoE)" (project-fortress), "Fine-grained vs
+// coarse experts": DeepSeek-V3 adds one always-active shared expert to its
+// 256 routed ones, a SwiGLU MLP of 3 d ffn weights ("Expert parallelism",
+// zerotofrontier.app, "A worked example at DeepSeek-V3's shape") that every
+// token goes through; and at decode a layer's time is the weights it reads
+// (the first page, "The serving asymmetry").  Tiling such a product
+// by output columns alone gives one workgroup per 64-256 weight rows, a few
+// dozen for the whole GPU, each streaming the full reduction length; the
+// split here gives every workgroup one K range of one 64-column tile, so
+// hundreds of workgroups stream the weights at once.
+//
+//   pass 1  P[s, m, n] = sum over k in K range s of A[m, k] W[n, k]   (fp32)
+//   pass 2  sum over s in order 0, 1, ... (a fixed order: the result does
+//           not depend on the schedule), then SwiGLU (gate/up) or a plain
+//           cast (down), rounded once to bf16.
+//
+// A (rows) and W (weights) are bf16, row-major and K-contiguous, so each MFMA
+// operand is one 16-byte load per lane straight from memory: lane l holds
+// row l % 32 and K positions 8 (l / 32) .. + 7 of a 16-deep K step.
+#include "common.hpp"
+#include "gemm_common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kDenseBN = 64;       // output columns (weight rows) per workgroup
+constexpr int kDenseMaxRows = 256;  // 8 row blocks of 32, two per wave
+constexpr int kDenseU = 8;          // K steps whose operands are loaded together
+
+__device__ __forceinline__ void mma_bf16(const u32x4 &a, const u32x4 &b, f32x16 &c) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                              c, 0, 0, 0);
+}
+
+// Workgroup (n tile blockIdx.x, K range blockIdx.y), 4 waves; wave w owns
+// row blocks w and w + 4 (the second only when M > 128) and both 32-column
+// blocks of the tile.  Rows past M read row M - 1 and are not stored.
+// Host guarantees: 1 <= M <= 256, N % 64 == 0, K % (16 S) == 0 with
+// kchunk = K / S, gridDim = (N / 64, S).
+__global__ __launch_bounds__(256) void k_dense_partial(const u32x4 *__restrict__ A, int M, int K,
+                                                       const u32x4 *__restrict__ W, int N, int kchunk,
+                                                       float *__restrict__ P) {
+  const int lane = lane_id();
+  const int wave = uniform(threadIdx.x >> 6);
+  const int nrb = (M + 31) / 32;
+  if (wave >= nrb) return;   // no live row block (no barrier follows)
+  const bool two = wave + 4 < nrb;
+  const int n0 = blockIdx.x * kDenseBN, s = blockIdx.y;
+  const int kvec = K / 8, lr = lane & 31, kh = lane >> 5;
+  const int c0 = s * (kchunk / 8) + kh;   // this lane's first 16-byte chunk
+  int r0 = wave * 32 + lr, r1 = (wave + 4) * 32 + lr;
+  r0 = r0 < M ? r0 : M - 1;
+  r1 = r1 < M ? r1 : M - 1;
+  const u32x4 *a0 = A + (int64_t)r0 * kvec + c0;
+  const u32x4 *a1 = A + (int64_t)r1 * kvec + c0;
+  const u32x4 *b0 = W + (int64_t)(n0 + lr) * kvec + c0;
+  const u32x4 *b1 = W + (int64_t)(n0 + 32 + lr) * kvec + c0;
+  const int steps = kchunk / 16;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  for (int k0 = 0; k0 < steps; k0 += kDenseU) {
+    u32x4 fa0[kDenseU], fa1[kDenseU], fb0[kDenseU], fb1[kDenseU];
+#pragma unroll
+    for (int u = 0; u < kDenseU; ++u)
+      if (k0 + u < steps) {
+        const int off = 2 * (k0 + u);   // one K step is two 16-byte chunks
+        fb0[u] = b0[off];
+        fb1[u] = b1[off];
+        fa0[u] = a0[off];
+        if (two) fa1[u] = a1[off];
+      }
+#pragma unroll
+    for (int u = 0; u < kDenseU; ++u)
+      if (k0 + u < steps) {
+        mma_bf16(fa0[u], fb0[u], acc[0][0]);
+        mma_bf16(fa0[u], fb1[u], acc[0][1]);
+        if (two) {
+          mma_bf16(fa1[u], fb0[u], acc[1][0]);
+          mma_bf16(fa1[u], fb1[u], acc[1][1]);
+        }
+      }
+  }
+
+  // MFMA 32x32 output layout: lane l holds column l % 32 and, in register v,
+  // row 8 (v / 4) + 4 (l / 32) + v % 4 of the block.
+  float *out = P + (int64_t)s * M * N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i == 1 && !two) break;
+    const int rb = (wave + 4 * i) * 32;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = rb + 8 * (v >> 2) + 4 * kh + (v & 3);
+        if (row < M) out[(int64_t)row * N + n0 + 32 * j + lr] = acc[i][j][v];
+      }
+  }
+}
+
+// h[m, f] = SiLU(g) u with g = sum_s P[s, m, f], u = sum_s P[s, m, ffn + f];
+// gu (optional) keeps (g, u) in bf16 as a [M, 2 ffn] row.  Four columns per
+// thread.
+__global__ __launch_bounds__(256) void k_dense_reduce_swiglu(const float *__restrict__ P, int S, int M,
+                                                             int ffn, uint16_t *__restrict__ h,
+                                                             uint16_t *__restrict__ gu) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // group of 4 columns
+  const int64_t nq = (int64_t)M * ffn / 4;
+  if (q >= nq) return;
+  const int64_t m = q / (ffn / 4);
+  const int f = (int)(q - m * (ffn / 4)) * 4;
+  const int64_t N = 2 * (int64_t)ffn;
+  float g[4] = {0, 0, 0, 0}, u[4] = {0, 0, 0, 0};
+  for (int s = 0; s < S; ++s) {
+    const float4 pg = *reinterpret_cast<const float4 *>(P + ((int64_t)s * M + m) * N + f);
+    const float4 pu = *reinterpret_cast<const float4 *>(P + ((int64_t)s * M + m) * N + ffn + f);
+    g[0] += pg.x; g[1] += pg.y; g[2] += pg.z; g[3] += pg.w;
+    u[0] += pu.x; u[1] += pu.y; u[2] += pu.z; u[3] += pu.w;
+  }
+  uint2 hv;
+  hv.x = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
+  hv.y = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
+  *reinterpret_cast<uint2 *>(h + m * ffn + f) = hv;
+  if (gu) {
+    *reinterpret_cast<uint2 *>(gu + m * N + f) = make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
+    *reinterpret_cast<uint2 *>(gu + m * N + ffn + f) =
+        make_uint2(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]));
+  }
+}
+
+// y[m, n] = sum_s P[s, m, n], four columns per thread.
+__global__ __launch_bounds__(256) void k_dense_reduce(const float *__restrict__ P, int S, int M, int N,
+                                                      uint16_t *__restrict__ y) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nq = (int64_t)M * N / 4;
+  if (q >= nq) return;
+  float a[4] = {0, 0, 0, 0};
+  for (int s = 0; s < S; ++s) {
+    const float4 p = *reinterpret_cast<const float4 *>(P + (int64_t)s * M * N + 4 * q);
+    a[0] += p.x; a[1] += p.y; a[2] += p.z; a[3] += p.w;
+  }
+  *reinterpret_cast<uint2 *>(y + 4 * q) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+}
+
+// Splits of a K-deep reduction over N / 64 column tiles: enough workgroups
+// for two per CU (512), at most 16 splits, each split a multiple of 16 deep.
+int dense_splits(int K, int N) {
+  const int tiles = N / kDenseBN;
+  int s = (512 + tiles - 1) / tiles;
+  s = s < 1 ? 1 : (s > 16 ? 16 : s);
+  while (s > 1 && K % (16 * s) != 0) --s;
+  return s;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_dense_swiglu_workspace_bytes(int M, int d, int ffn) {
+  if (M < 1 || d < 1 || ffn < 1) return 16;
+  const size_t p1 = (size_t)dense_splits(d, 2 * ffn) * (size_t)M * 2 * (size_t)ffn;
+  const size_t p2 = (size_t)dense_splits(ffn, d) * (size_t)M * (size_t)d;
+  return (p1 > p2 ? p1 : p2) * sizeof(float);
+}
+
+extern "C" moe_status moe_dense_swiglu(const void *x, moe_dtype dt, int M, int d, int ffn,
+                                       const void *w13, const void *w2, void *h, void *gu, void *y,
+                                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (M < 0 || d < 1 || ffn < 1) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_BF16 || M > kDenseMaxRows || d % 64 != 0 || ffn % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (M == 0) return MOE_OK;
+  if (!x || !w13 || !w2 || !h || !y || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || !aligned16(h) || !aligned16(y) ||
+      !aligned16(workspace) || (gu && !aligned16(gu)))
+    return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < moe_dense_swiglu_workspace_bytes(M, d, ffn)) return MOE_ERR_INVALID_ARG;
+  float *P = static_cast<float *>(workspace);
+
+  // Gate/up: N = 2 ffn weight rows (gate rows, then up rows), K = d.
+  const int s1 = dense_splits(d, 2 * ffn);
+  k_dense_partial<<<dim3(2 * ffn / kDenseBN, s1), dim3(256), 0, stream>>>(
+      static_cast<const u32x4 *>(x), M, d, static_cast<const u32x4 *>(w13), 2 * ffn, d / s1, P);
+  const int64_t q1 = (int64_t)M * ffn / 4;
+  k_dense_reduce_swiglu<<<dim3((unsigned)((q1 + 255) / 256)), dim3(256), 0, stream>>>(
+      P, s1, M, ffn, static_cast<uint16_t *>(h), static_cast<uint16_t *>(gu));
+  // Down: N = d, K = ffn.
+  const int s2 = dense_splits(ffn, d);
+  k_dense_partial<<<dim3(d / kDenseBN, s2), dim3(256), 0, stream>>>(
+      static_cast<const u32x4 *>(h), M, ffn, static_cast<const u32x4 *>(w2), d, ffn / s2, P);
+  const int64_t q2 = (int64_t)M * d / 4;
+  k_dense_reduce<<<dim3((unsigned)((q2 + 255) / 256)), dim3(256), 0, stream>>>(P, s2, M, d,
+                                                                             static_cast<uint16_t *>(y));
+  return launch_status();
+}

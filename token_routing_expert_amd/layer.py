@@ -15,7 +15,8 @@ from . import (MoeError, moe_combine_backward, moe_gate_backward, moe_grouped_do
                moe_grouped_down_backward, moe_grouped_gate_up, moe_grouped_gate_up_backward,
                moe_grouped_gate_up_gather, moe_grouped_gate_up_save, moe_grouped_swiglu,
                moe_grouped_weight_grad, moe_permute, moe_permute_workspace_bytes, moe_route_topk,
-               moe_router_bias_update, moe_router_logits, moe_send_counts, moe_unpermute_combine)
+               moe_router_bias_update, moe_router_logits, moe_send_counts, moe_unpermute_combine,
+               moe_dense_swiglu, moe_dense_swiglu_workspace_bytes)
 from .inputs import MoeConfig
 
 
@@ -160,6 +161,13 @@ class MoeLayer:
             self.sh_offsets = torch.tensor([0, T], dtype=i32, device=dev)
             self.sh_h = torch.empty((T, ffn), dtype=act, device=dev)
             self.y_sh = torch.empty((T, d), dtype=act, device=dev)
+            # A shared expert over few tokens (decode) splits its reductions
+            # over many workgroups (moe_dense_swiglu) instead of tiling by
+            # output columns alone, which leaves most CUs idle.
+            self.sh_dense = act == torch.bfloat16 and 0 < T <= 256 and d % 64 == 0 and ffn % 64 == 0
+            if self.sh_dense:
+                self.sh_ws = torch.empty(moe_dense_swiglu_workspace_bytes(T, d, ffn), dtype=torch.uint8,
+                                         device=dev)
         else:
             self.y_sh = None
         if self.train:
@@ -228,7 +236,11 @@ class MoeLayer:
         """The shared expert's own launches (with merge_shared its rows are
         part of the routed launches and this does nothing)."""
         if self.cfg.shared and not self.merge_shared:
-            if self.train:
+            if self.sh_dense:
+                moe_dense_swiglu(self.x, self.sh_w13, self.sh_w2, h=self.sh_h,
+                                 gu=self.sh_gu if self.train else None, y=self.y_sh,
+                                 workspace=self.sh_ws, stream=stream)
+            elif self.train:
                 moe_grouped_gate_up_save(self.x, self.sh_offsets, self.sh_w13, self.sh_h,
                                          self.sh_gu, stream=stream)
                 moe_grouped_down(self.sh_h, self.sh_offsets, self.sh_w2, self.y_sh, stream=stream)
