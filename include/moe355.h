@@ -263,8 +263,9 @@ moe_status moe_grouped_down(const void *h, moe_dtype dt, int M, int ffn, int d,
  *   workspace: device memory of at least
  *   moe_dense_swiglu_workspace_bytes(M, d, ffn) bytes, owned by the caller
  *   and overwritten.  Calls sharing a workspace must not overlap.
- * bf16 only.  Errors: INVALID_ARG for M < 0, d or ffn < 1, a null pointer
- * (other than gu), pointers not 16-byte aligned, or a workspace too small;
+ * bf16 only.  Errors: INVALID_ARG for M < 0, d or ffn < 1, an unknown dtype
+ * code, a null pointer (other than gu), pointers not 16-byte aligned, or a
+ * workspace too small;
  * UNSUPPORTED for fp32, M > 256, or d or ffn not a multiple of 64.  M = 0
  * launches nothing.
  */
