@@ -1,6 +1,6 @@
 /*
- * libmoe355 -- one GPU's hot path of an expert-parallel MoE layer forward,
- * hand-written HIP for gfx950 (MI355X).
+ * libmoe355 -- one GPU's hot path of an expert-parallel MoE layer, forward and
+ * backward, hand-written HIP for gfx950 (MI355X).
  *
  * The path follows the numbered forward-pass steps of the textbook section
  * "Expert parallelism" (zerotofrontier.app/moe/expert-parallel): route (step 1),
