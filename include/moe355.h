@@ -14,9 +14,10 @@
  *    stated; every call is asynchronous on `stream` (NULL = the null stream)
  *    and performs no device-to-host synchronisation.
  *  - The caller owns every buffer, including scratch.  The library never
- *    allocates device memory and keeps no state between calls; calls are
- *    reentrant and may run concurrently on different streams when their
- *    buffers do not overlap.
+ *    allocates device memory.  Between calls it keeps only per-device caches
+ *    of launch-shape queries (compute-unit count, kernel occupancy), held in
+ *    atomics, so calls are reentrant and may run concurrently on different
+ *    host threads and streams when their buffers do not overlap.
  *  - Outputs are fully overwritten.  Inputs are not modified.  Inputs and
  *    outputs must not alias.
  *  - Results are deterministic: the same inputs give the same output bits.

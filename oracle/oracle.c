@@ -52,9 +52,9 @@ static double widen(const void *base, int dtype, int64_t i)
 /* ------------------------------------------------------------------------
  * Pinned fp32 sigmoid.
  *
- * DeepSeek-V3's node-limited routing scores a group of experts by the sum of
- * the token's two highest affinities there ("What DeepSeek-V3 did about it");
- * the affinity is the sigmoid of the logit.  Which groups survive is an
+ * In DeepSeek-V3's node-limited routing ("What DeepSeek-V3 did about it") a
+ * group's score for a token adds up the token's two largest affinities among
+ * the group's experts, and an affinity is the sigmoid of a logit.  Which groups survive is an
  * integer decision taken on fp32 sums, so both sides must produce the same
  * fp32 sigmoid bits.  This is that function, written from the mathematics:
  *
@@ -100,8 +100,8 @@ void orc_sigmoid_pinned_array(const float *x, float *y, int64_t n)
 /* ------------------------------------------------------------------------
  * O1  Route: top-k per token, optionally node (group) limited, plus gates.
  *
- * Step 1 of the forward pass ("Expert parallelism": compute the router and
- * the top-k choices for the local tokens).  The key of expert e is the fp32
+ * Step 1 of the forward pass ("Expert parallelism", section "Expert
+ * parallelism"): every GPU picks k experts for each of its own tokens.  The key of expert e is the fp32
  * logit with -0 read as +0; both gating maps are increasing, so ranking by
  * the logit ranks by the gate.  Among equal keys the lower expert id wins,
  * and slot j holds the j-th pick.

@@ -350,6 +350,9 @@ LAYER_CASES = [
     ("small_bf16", 1024, 8, 2, 256, 512, "softmax", 1, (1, 1), False, False, True),
     ("grouped_shared", 512, 32, 4, 256, 256, "sigmoid", 1, (4, 2), True, False, True),
     ("merged_shared", 384, 16, 2, 256, 384, "sigmoid", 1, (1, 1), True, True, True),
+    # T <= 256: the shared expert runs on the split-reduction kernel, which
+    # also writes the pre-activations its backward reads.
+    ("dense_shared", 128, 32, 4, 256, 256, "sigmoid", 1, (4, 2), True, False, True),
     ("packed_rows", 300, 8, 2, 384, 256, "softmax", 0, (1, 1), False, False, False),
 ]
 
@@ -367,6 +370,8 @@ def test_layer_backward_matches_oracle(lib, case):
     dy = to_bf16(np.random.default_rng(3).standard_normal((T, d)))
     layer = MoeLayer(cfg, x, w13, w2, logits=logits, sh_w13=sh13, sh_w2=sh2, device="cuda",
                      fused_gather=fused, merge_shared=merge, train=True)
+    if shared and not merge:
+        assert layer.sh_dense == (T <= 256)
     layer.forward()
     g = layer.backward(dev(dy))
     torch.cuda.synchronize()

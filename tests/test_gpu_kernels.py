@@ -524,14 +524,17 @@ def test_grouped_swiglu_shared_expert_form(lib):
 
 
 @pytest.mark.parametrize("M,d,ffn", [(1, 256, 128), (77, 256, 384), (128, 1024, 512), (129, 512, 256),
-                                     (256, 448, 192)])
+                                     (256, 448, 192), (128, 7168, 2048), (32, 16384, 8192),
+                                     (8, 256, 16384)])
 def test_dense_swiglu_split_reductions(lib, M, d, ffn):
     """moe_dense_swiglu (one expert, split reductions): y against the oracle's
     dense SwiGLU MLP and the pre-activations gu against a float64 product,
     per row within 2e-2 of the row's largest magnitude; the same call twice
     gives the same bits (fixed summation order).  Shapes: one row, a ragged
     row block, exactly four row blocks, the second row block of a wave in
-    use (129 and 256 rows), reductions split 1 to 16 ways."""
+    use (129 and 256 rows), the DeepSeek-V3 decode shared expert (128 rows,
+    d 7168, ffn 2048).  The (gate/up, down) reductions are split (16, 8),
+    (16, 12), (16, 16), (16, 16), (14, 12), (8, 4), (2, 2) and (1, 16) ways."""
     cfg = inputs.MoeConfig("t", 5, T=M, E=1, k=1, d=d, ffn=ffn, dtype="bf16", gating="softmax")
     a = inputs.gen_x(cfg)
     w13, w2 = inputs.gen_expert_weights(cfg)

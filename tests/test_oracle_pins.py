@@ -403,9 +403,10 @@ def test_unpermute_of_permute_is_identity():
 @pytest.mark.parametrize("gating,n_groups,topk_groups,shared", [
     ("softmax", 1, 1, False), ("sigmoid", 4, 2, True)])
 def test_sparse_layer_equals_dense_masked(gating, n_groups, topk_groups, shared):
-    """EP, "Expert parallelism": on one device an MoE layer is a gather, some
-    matrix products and a scatter.  The sparse path (route, permute, experts on
-    packed rows, combine) equals evaluating every expert on every token and
+    """EP, "Expert parallelism": without the exchanges, the layer reduces to
+    moving rows into expert order, running each expert's products on its rows
+    and moving the results back.  That sparse path (route, permute, experts on
+    packed rows, combine) must equal evaluating every expert on every token and
     masking with the gate."""
     cfg = inputs.MoeConfig("t", 1, T=16, E=8, k=2, d=16, ffn=24, dtype="f32", gating=gating,
                            n_groups=n_groups, topk_groups=topk_groups, shared=shared, w_std=0.3)

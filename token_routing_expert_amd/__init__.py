@@ -117,6 +117,14 @@ def _dev(t, name, dtypes):
     return t
 
 
+def _shape(t, shape, name, what):
+    """Raise unless t (an output buffer the kernels write from the sizes they
+    are given) has exactly this shape."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise MoeError(f"{what}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
 def _dtype_code(t) -> int:
     torch = _torch()
     return MOE_BF16 if t.dtype == torch.bfloat16 else MOE_F32
@@ -151,6 +159,8 @@ def moe_route_topk(logits, k, gating="softmax", renormalize=True, n_groups=1, to
         topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
     _dev(topk_ids, "topk_ids", (torch.int32,))
     _dev(topk_w, "topk_w", (torch.float32,))
+    _shape(topk_ids, (T, k), "topk_ids", "moe_route_topk")
+    _shape(topk_w, (T, k), "topk_w", "moe_route_topk")
     g = MOE_SOFTMAX if gating == "softmax" else MOE_SIGMOID if gating == "sigmoid" else -1
     lib = load_library()
     if bias is None:
@@ -179,6 +189,7 @@ def moe_router_logits(x, w_router, logits=None, stream=None):
         raise MoeError("moe_router_logits: w_router must be [E, d]")
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if logits is None else logits
     _dev(logits, "logits", (torch.float32,))
+    _shape(logits, (T, E), "logits", "moe_router_logits")
     _check(load_library().moe_router_logits(_ptr(x), _dtype_code(x), T, d, _ptr(w_router), E,
                                             _ptr(logits), _stream(stream)), "moe_router_logits")
     return logits
@@ -205,6 +216,7 @@ def moe_send_counts(topk_ids, E, n_ep, send_counts=None, stream=None):
     if send_counts is None:
         send_counts = torch.empty((n_ep, n_ep), dtype=torch.int32, device=topk_ids.device)
     _dev(send_counts, "send_counts", (torch.int32,))
+    _shape(send_counts, (n_ep, n_ep), "send_counts", "moe_send_counts")
     _check(load_library().moe_send_counts(_ptr(topk_ids), T, k, E, n_ep, _ptr(send_counts),
                                           _stream(stream)), "moe_send_counts")
     return send_counts
@@ -240,10 +252,13 @@ def moe_permute(x, topk_ids, E, counts=None, offsets=None, order=None, inv=None,
     nbytes = moe_permute_workspace_bytes(T, k, E)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
-    for name, t in (("counts", counts), ("offsets", offsets), ("order", order), ("inv", inv)):
+    for name, t, n in (("counts", counts, E), ("offsets", offsets, E + 1), ("order", order, M),
+                       ("inv", inv, M)):
         _dev(t, name, (i32,))
+        _shape(t, (n,), name, "moe_permute")
     if rows:
         _dev(x_perm, "x_perm", (x.dtype,))
+        _shape(x_perm, (M, d), "x_perm", "moe_permute")
     _check(load_library().moe_permute(
         _ptr(x) if rows else None, _dtype_code(x), T, d, _ptr(topk_ids), k, E, _ptr(counts),
         _ptr(offsets), _ptr(order), _ptr(inv), _ptr(x_perm), _ptr(workspace), workspace.numel(),
@@ -266,6 +281,8 @@ def moe_grouped_swiglu(a, offsets, w13, w2, h=None, y=None, stream=None):
     y = torch.empty((M, d), dtype=a.dtype, device=a.device) if y is None else y
     _dev(h, "h", (a.dtype,))
     _dev(y, "y", (a.dtype,))
+    _shape(h, (M, ffn), "h", "moe_grouped_swiglu")
+    _shape(y, (M, d), "y", "moe_grouped_swiglu")
     _check(load_library().moe_grouped_swiglu(_ptr(a), _dtype_code(a), M, d, ffn, _ptr(offsets),
                                              G, _ptr(w13), _ptr(w2), _ptr(h), _ptr(y),
                                              _stream(stream)), "moe_grouped_swiglu")
@@ -294,8 +311,11 @@ def moe_dense_swiglu(x, w13, w2, h=None, gu=None, y=None, workspace=None, stream
     y = torch.empty((M, d), dtype=x.dtype, device=x.device) if y is None else y
     _dev(h, "h", (x.dtype,))
     _dev(y, "y", (x.dtype,))
+    _shape(h, (M, ffn), "h", "moe_dense_swiglu")
+    _shape(y, (M, d), "y", "moe_dense_swiglu")
     if gu is not None:
         _dev(gu, "gu", (x.dtype,))
+        _shape(gu, (M, 2 * ffn), "gu", "moe_dense_swiglu")
     nbytes = moe_dense_swiglu_workspace_bytes(M, d, ffn)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
@@ -331,6 +351,7 @@ def moe_grouped_gate_up(a, offsets, w13, h=None, stream=None):
         raise MoeError("moe_grouped_gate_up: inconsistent shapes")
     h = _torch().empty((M, ffn), dtype=a.dtype, device=a.device) if h is None else h
     _dev(h, "h", (a.dtype,))
+    _shape(h, (M, ffn), "h", "moe_grouped_gate_up")
     _check(load_library().moe_grouped_gate_up(_ptr(a), _dtype_code(a), M, d, ffn, _ptr(offsets),
                                               G, _ptr(w13), _ptr(h), _stream(stream)),
            "moe_grouped_gate_up")
@@ -353,6 +374,7 @@ def moe_grouped_gate_up_gather(x, order, k, offsets, w13, h=None, stream=None):
         raise MoeError("moe_grouped_gate_up_gather: inconsistent shapes")
     h = torch.empty((M, ffn), dtype=x.dtype, device=x.device) if h is None else h
     _dev(h, "h", (x.dtype,))
+    _shape(h, (M, ffn), "h", "moe_grouped_gate_up_gather")
     _check(load_library().moe_grouped_gate_up_gather(
         _ptr(x), _dtype_code(x), T, k, M, d, ffn, _ptr(order), _ptr(offsets), G, _ptr(w13),
         _ptr(h), _stream(stream)), "moe_grouped_gate_up_gather")
@@ -368,6 +390,7 @@ def moe_grouped_down(h, offsets, w2, y=None, stream=None):
         raise MoeError("moe_grouped_down: inconsistent shapes")
     y = _torch().empty((M, d), dtype=h.dtype, device=h.device) if y is None else y
     _dev(y, "y", (h.dtype,))
+    _shape(y, (M, d), "y", "moe_grouped_down")
     _check(load_library().moe_grouped_down(_ptr(h), _dtype_code(h), M, ffn, d, _ptr(offsets), G,
                                            _ptr(w2), _ptr(y), _stream(stream)), "moe_grouped_down")
     return y
@@ -389,10 +412,14 @@ def moe_unpermute_combine(y_perm, inv, topk_w, y_shared=None, y=None, stream=Non
         _dev(topk_w, "topk_w", (torch.float32,))
         T, k = topk_w.shape
     d = y_perm.shape[1]
+    if y_perm.shape[0] < T * k or inv.numel() != T * k:
+        raise MoeError("moe_unpermute_combine: inv must have T k entries and y_perm at least T k rows")
     if y_shared is not None:
         _dev(y_shared, "y_shared", (y_perm.dtype,))
+        _shape(y_shared, (T, d), "y_shared", "moe_unpermute_combine")
     y = torch.empty((T, d), dtype=y_perm.dtype, device=y_perm.device) if y is None else y
     _dev(y, "y", (y_perm.dtype,))
+    _shape(y, (T, d), "y", "moe_unpermute_combine")
     _check(load_library().moe_unpermute_combine(_ptr(y_perm), _dtype_code(y_perm), T, k, d,
                                                 _ptr(inv), _ptr(topk_w), _ptr(y_shared), _ptr(y),
                                                 _stream(stream)), "moe_unpermute_combine")
@@ -423,6 +450,8 @@ def moe_grouped_gate_up_save(x, offsets, w13, h=None, gu=None, order=None, k=1, 
     gu = torch.empty((M, 2 * ffn), dtype=x.dtype, device=x.device) if gu is None else gu
     _dev(h, "h", (x.dtype,))
     _dev(gu, "gu", (x.dtype,))
+    _shape(h, (M, ffn), "h", "moe_grouped_gate_up_save")
+    _shape(gu, (M, 2 * ffn), "gu", "moe_grouped_gate_up_save")
     _check(load_library().moe_grouped_gate_up_save(
         _ptr(x), _dtype_code(x), T, k, M, d, ffn, _ptr(order), _ptr(offsets), G, _ptr(w13),
         _ptr(h), _ptr(gu), _stream(stream)), "moe_grouped_gate_up_save")
@@ -444,14 +473,22 @@ def moe_combine_backward(dy, inv, topk_w, y_perm=None, dy_perm=None, dgate=None,
     dev = dy.device
     dy_perm = torch.empty((T * k, d), dtype=dy.dtype, device=dev) if dy_perm is None else dy_perm
     _dev(dy_perm, "dy_perm", (dy.dtype,))
+    _shape(dy, (T, d), "dy", "moe_combine_backward")
+    _shape(dy_perm, (T * k, d), "dy_perm", "moe_combine_backward")
+    if inv.numel() != T * k:
+        raise MoeError("moe_combine_backward: inv must have T k entries")
     if want_dgate and y_perm is not None:
         _dev(y_perm, "y_perm", (dy.dtype,))
+        if y_perm.shape[0] < T * k or y_perm.shape[1] != d:
+            raise MoeError("moe_combine_backward: y_perm must have at least T k rows of d")
         dgate = torch.empty((T, k), dtype=torch.float32, device=dev) if dgate is None else dgate
         _dev(dgate, "dgate", (torch.float32,))
+        _shape(dgate, (T, k), "dgate", "moe_combine_backward")
     else:
         y_perm, dgate = None, None
     if dy_shared is not None:
         _dev(dy_shared, "dy_shared", (dy.dtype,))
+        _shape(dy_shared, (T, d), "dy_shared", "moe_combine_backward")
     _check(load_library().moe_combine_backward(
         _ptr(dy), _dtype_code(dy), T, k, d, _ptr(inv), _ptr(topk_w), _ptr(y_perm), _ptr(dy_perm),
         _ptr(dgate), _ptr(dy_shared), _stream(stream)), "moe_combine_backward")
@@ -471,6 +508,10 @@ def moe_gate_backward(logits, topk_ids, topk_w, dgate, gating="softmax", renorma
     dlogits = torch.empty((T, E), dtype=torch.float32, device=logits.device) if dlogits is None \
         else dlogits
     _dev(dlogits, "dlogits", (torch.float32,))
+    _shape(dlogits, (T, E), "dlogits", "moe_gate_backward")
+    _shape(topk_ids, (T, k), "topk_ids", "moe_gate_backward")
+    _shape(topk_w, (T, k), "topk_w", "moe_gate_backward")
+    _shape(dgate, (T, k), "dgate", "moe_gate_backward")
     g = MOE_SOFTMAX if gating == "softmax" else MOE_SIGMOID if gating == "sigmoid" else -1
     _check(load_library().moe_gate_backward(_ptr(logits), _ptr(topk_ids), _ptr(topk_w),
                                             _ptr(dgate), T, E, k, g, int(bool(renormalize)),
@@ -490,6 +531,7 @@ def moe_grouped_down_backward(dy_perm, offsets, w2, gu, dgu=None, stream=None):
     dgu = _torch().empty((M, 2 * ffn), dtype=dy_perm.dtype, device=dy_perm.device) if dgu is None \
         else dgu
     _dev(dgu, "dgu", (dy_perm.dtype,))
+    _shape(dgu, (M, 2 * ffn), "dgu", "moe_grouped_down_backward")
     _check(load_library().moe_grouped_down_backward(
         _ptr(dy_perm), _dtype_code(dy_perm), M, d, ffn, _ptr(offsets), G, _ptr(w2), _ptr(gu),
         _ptr(dgu), _stream(stream)), "moe_grouped_down_backward")
@@ -506,6 +548,7 @@ def moe_grouped_gate_up_backward(dgu, offsets, w13, dx_perm=None, stream=None):
     dx_perm = _torch().empty((M, d), dtype=dgu.dtype, device=dgu.device) if dx_perm is None \
         else dx_perm
     _dev(dx_perm, "dx_perm", (dgu.dtype,))
+    _shape(dx_perm, (M, d), "dx_perm", "moe_grouped_gate_up_backward")
     _check(load_library().moe_grouped_gate_up_backward(
         _ptr(dgu), _dtype_code(dgu), M, d, ffn, _ptr(offsets), G, _ptr(w13), _ptr(dx_perm),
         _stream(stream)), "moe_grouped_gate_up_backward")
@@ -557,9 +600,11 @@ def moe_router_backward(dlogits, x, w_router, dx=None, dw_router=None, workspace
         raise MoeError("moe_router_backward: inconsistent shapes")
     if dx is not None:
         _dev(dx, "dx", (x.dtype,))
+        _shape(dx, (T, d), "dx", "moe_router_backward")
     dw_router = torch.empty((E, d), dtype=x.dtype, device=x.device) if dw_router is None \
         else dw_router
     _dev(dw_router, "dw_router", (x.dtype,))
+    _shape(dw_router, (E, d), "dw_router", "moe_router_backward")
     nbytes = moe_router_backward_workspace_bytes(T, E)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)

@@ -3,21 +3,21 @@
 // which is also the backward of the permute (the dispatch's gradient is
 // combined back into the token).
 //
-// Step 7 of the forward pass in "Expert parallelism" (zerotofrontier.app):
-// undo the sort and scatter-add each row into its token with its gate.  Here
-// the scatter-add is done in its gather form: one wave per token reads the
-// token's k packed rows through inv and writes the token once, so there are
-// no atomics and the fp32 sum order (slot 0..k-1, then the shared row) is
-// fixed.
+// "Expert parallelism" (zerotofrontier.app), section "Expert parallelism",
+// step 7 of the forward pass: every expert output row returns to the token it
+// came from, scaled by that token's gate for the expert, and the k
+// contributions add up.  The kernel computes this sum from the token's side:
+// one wave per token fetches the token's k packed rows through inv and
+// stores the token once.  No two waves write one token, so no atomics are
+// needed, and the fp32 additions run in a fixed order (slot 0..k-1, then the
+// shared row).
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-#ifndef MOE_COMBINE_NV
-#define MOE_COMBINE_NV 2   // 16-byte vectors per lane per round
-#endif
+constexpr int kCombineNV = 2;   // 16-byte vectors per lane per round
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
@@ -189,7 +189,7 @@ extern "C" moe_status moe_unpermute_combine(const void *y_perm, moe_dtype dt, in
   const uint4 *yp = static_cast<const uint4 *>(y_perm);
   const uint4 *ys = static_cast<const uint4 *>(y_shared);
   uint4 *out = static_cast<uint4 *>(y);
-  constexpr int NV = MOE_COMBINE_NV;
+  constexpr int NV = kCombineNV;
   if (dt == MOE_BF16) {
     if (k == 1)
       k_combine<true, 1, NV><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);

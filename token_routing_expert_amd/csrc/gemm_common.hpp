@@ -4,6 +4,8 @@
 // and the persistent grid.
 #pragma once
 
+#include <atomic>
+
 #include "common.hpp"
 
 namespace moe {
@@ -143,29 +145,45 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Compute units of the current device (cached per device id).
-inline int device_cus() {
-  static int cus[64];
+// Per-device caches of launch-shape queries.  Entries are atomics: calls on
+// several host threads may fill one at the same time (each stores the same
+// value), and a reader sees either 0 (not yet queried) or the value.
+constexpr int kMaxDevices = 64;
+struct DeviceCache {
+  std::atomic<int> v[kMaxDevices];
+};
+
+// The current device, or -1 when it cannot be cached.
+inline int current_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  return dev;
+}
+
+// Compute units of the current device.
+inline int device_cus() {
+  static DeviceCache cus;   // zero-initialised: static storage
+  const int dev = current_device();
+  int n = dev >= 0 ? cus.v[dev].load(std::memory_order_relaxed) : 0;
+  if (n > 0) return n;
+  if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;
+  if (dev >= 0) cus.v[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 // Persistent grid: resident workgroups (CUs x blocks per CU), no more than
-// there can be tiles, rounded to a multiple of the XCD count.  per_cu caches
-// the occupancy query of one kernel instantiation.
-inline int persistent_grid(const void *kernel, int threads, int &per_cu, int64_t max_tiles) {
+// there can be tiles, rounded to a multiple of the XCD count.  occ caches the
+// occupancy query of one kernel instantiation, per device.
+inline int persistent_grid(const void *kernel, int threads, DeviceCache &occ, int64_t max_tiles) {
+  const int dev = current_device();
+  int per_cu = dev >= 0 ? occ.v[dev].load(std::memory_order_relaxed) : 0;
   if (per_cu == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1)
-      n = 1;
-    per_cu = n;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    if (dev >= 0) occ.v[dev].store(per_cu, std::memory_order_relaxed);
   }
   int64_t g = (int64_t)device_cus() * per_cu;
   const int64_t cap = (max_tiles + kXcds - 1) / kXcds * kXcds;

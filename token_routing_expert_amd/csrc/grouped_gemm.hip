@@ -839,8 +839,8 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
     const int64_t mtiles_max = (M + Cfg::BM - 1) / Cfg::BM + G;
     auto kern = k_grouped_gemm_pp<BF16, Cfg::BM, Cfg::BR, Cfg::SA, Cfg::SB, Cfg::CPR, Cfg::DA, SWIGLU,
                                   Cfg::SPLIT, SAVE>;
-    static int per_cu = 0;
-    const int grid = persistent_grid((const void *)kern, 512, per_cu, mtiles_max * ntiles);
+    static DeviceCache occ;
+    const int grid = persistent_grid((const void *)kern, 512, occ, mtiles_max * ntiles);
     kern<<<dim3(grid), dim3(512), 0, stream>>>(static_cast<const u32x4 *>(a), M, kvec, offsets, G,
                                               static_cast<const u32x4 *>(w), b_expert, b_up,
                                               ntiles, N, out, gather, gk, a_rows, gu);
@@ -848,9 +848,9 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
     const int ntiles = N / Cfg::BN;
     const int64_t mtiles_max = (M + Cfg::BM - 1) / Cfg::BM + G;
     auto kern = k_grouped_gemm<BF16, Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, SWIGLU, Cfg::SA, Cfg::SB, SAVE>;
-    static int per_cu = 0;
+    static DeviceCache occ;
     const int threads = Cfg::WM * Cfg::WN * 64;
-    const int grid = persistent_grid((const void *)kern, threads, per_cu, mtiles_max * ntiles);
+    const int grid = persistent_grid((const void *)kern, threads, occ, mtiles_max * ntiles);
     kern<<<dim3(grid), dim3(threads), 0, stream>>>(static_cast<const u32x4 *>(a), M, kvec, offsets,
                                                   G, static_cast<const u32x4 *>(w), b_expert,
                                                   b_up, ntiles, N, out, gather, gk, a_rows, gu);
@@ -869,36 +869,15 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
 //          phase has to drain its LDS reads) and 5 weight stages (4 ahead).
 //   Large  (many rows per expert): ping-pong tiles of 256 rows, 128-byte
 //          slices, 2 row stages (1 ahead) and 3 weight stages (2 ahead).
-#ifndef MOE_G1_SMALL
-#define MOE_G1_SMALL 32, 128, 1, 4, 2, 4
-#endif
-#ifndef MOE_G2_SMALL
-#define MOE_G2_SMALL 32, 128, 1, 4, 2, 4
-#endif
-#ifndef MOE_PP1_MEDIUM
-#define MOE_PP1_MEDIUM 320, 256, 4, 5, 4, true, 2
-#endif
-#ifndef MOE_PP2_MEDIUM
-#define MOE_PP2_MEDIUM 320, 256, 4, 5, 4, true, 2
-#endif
-#ifndef MOE_PP1_LARGE
-#define MOE_PP1_LARGE 256, 256, 2, 3, 8, true, 1
-#endif
-#ifndef MOE_PP2_LARGE
-#define MOE_PP2_LARGE 256, 256, 2, 3, 8, true, 1
-#endif
+using G1Small = TileCfg<32, 128, 1, 4, 2, 4>;
+using G2Small = TileCfg<32, 128, 1, 4, 2, 4>;
+using G1Medium = PpCfg<320, 256, 4, 5, 4, true, 2>;
+using G2Medium = PpCfg<320, 256, 4, 5, 4, true, 2>;
+using G1Large = PpCfg<256, 256, 2, 3, 8, true, 1>;
+using G2Large = PpCfg<256, 256, 2, 3, 8, true, 1>;
 // Weight gradients: 256 x 256 output tiles of an expert's dW, the reduction
 // over its rows in 32-row slices, deep rings (the reductions are short).
-#ifndef MOE_PP_WGRAD
-#define MOE_PP_WGRAD 256, 256, 4, 5, 4, true, 2
-#endif
-using G1Small = TileCfg<MOE_G1_SMALL>;
-using G2Small = TileCfg<MOE_G2_SMALL>;
-using G1Medium = PpCfg<MOE_PP1_MEDIUM>;
-using G2Medium = PpCfg<MOE_PP2_MEDIUM>;
-using G1Large = PpCfg<MOE_PP1_LARGE>;
-using G2Large = PpCfg<MOE_PP2_LARGE>;
-using G2Wgrad = PpCfg<MOE_PP_WGRAD>;
+using G2Wgrad = PpCfg<256, 256, 4, 5, 4, true, 2>;
 
 // Which tile family serves a call: by the mean rows per expert.  Both halves
 // of an expert MLP use the same family.  The ping-pong tiles are up to 128
@@ -958,8 +937,8 @@ void launch_dgrad(const void *a, int M, int K, int N, const int32_t *offsets, in
   const int64_t mtiles_max = (M + Cfg::BM - 1) / Cfg::BM + G;
   auto kern = k_grouped_gemm_pp<true, Cfg::BM, Cfg::BR, Cfg::SA, Cfg::SB, Cfg::CPR, Cfg::DA, false,
                                 Cfg::SPLIT, false, VAR>;
-  static int per_cu = 0;
-  const int grid = persistent_grid((const void *)kern, 512, per_cu, mtiles_max * ntiles);
+  static DeviceCache occ;
+  const int grid = persistent_grid((const void *)kern, 512, occ, mtiles_max * ntiles);
   kern<<<dim3(grid), dim3(512), 0, stream>>>(static_cast<const u32x4 *>(a), M, kvec, offsets, G,
                                             static_cast<const u32x4 *>(w), b_expert, 0, ntiles, N,
                                             out, nullptr, 1, 0, const_cast<void *>(gu));
@@ -983,9 +962,9 @@ moe_status check_shape(moe_dtype dt, int M, int d, int ffn, int G) {
 
 }  // namespace
 
-#ifndef MOE_DGRAD_LONGK
-#define MOE_DGRAD_LONGK 4096   // reduction length from which var 1 uses medium tiles
-#endif
+// Reduction length from which the first product's input gradient (var 1)
+// uses the medium tiles.
+constexpr int kDgradLongK = 4096;
 
 bool launch_wgrad_pp(const void *a, const void *b, int M, int m_dim, int n_dim,
                      const int32_t *offsets, int G, void *out, hipStream_t stream) {
@@ -995,8 +974,8 @@ bool launch_wgrad_pp(const void *a, const void *b, int M, int m_dim, int n_dim,
   const int64_t tiles = (int64_t)G * (m_dim / Cfg::BM) * ntiles;
   auto kern = k_grouped_gemm_pp<true, Cfg::BM, Cfg::BR, Cfg::SA, Cfg::SB, Cfg::CPR, Cfg::DA, false,
                                 Cfg::SPLIT, false, 3>;
-  static int per_cu = 0;
-  const int grid = persistent_grid((const void *)kern, 512, per_cu, tiles);
+  static DeviceCache occ;
+  const int grid = persistent_grid((const void *)kern, 512, occ, tiles);
   kern<<<dim3(grid), dim3(512), 0, stream>>>(static_cast<const u32x4 *>(a), M, 0, offsets, G,
                                             static_cast<const u32x4 *>(b), 0, 0, ntiles, n_dim, out,
                                             nullptr, 1, m_dim, nullptr);
@@ -1012,7 +991,7 @@ bool launch_dgrad_pp(int var, const void *a, int M, int K, int N, const int32_t 
   // rings of narrower slices once K is long; the down product's (var 2, with
   // the SwiGLU epilogue) stays on the large tiles (measured at Mixtral and
   // EP64-share shapes).
-  if (f == Family::Medium || (var == 1 && K >= MOE_DGRAD_LONGK)) {
+  if (f == Family::Medium || (var == 1 && K >= kDgradLongK)) {
     if (var == 2) launch_dgrad<2, G2Medium>(a, M, K, N, offsets, G, w, out, gu, stream);
     else if (var == 4) launch_dgrad<4, G2Medium>(a, M, K, N, offsets, G, w, out, gu, stream);
     else launch_dgrad<1, G2Medium>(a, M, K, N, offsets, G, w, out, gu, stream);

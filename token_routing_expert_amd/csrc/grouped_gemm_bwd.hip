@@ -394,25 +394,18 @@ __global__ __launch_bounds__(WM * 128) void k_grouped_gemm_bwd(const BwdParams p
   }
 }
 
-#ifndef MOE_BWD_WM
-#define MOE_BWD_WM 2        // waves along M: 2 -> 128-row tiles, 4 -> 256-row tiles
-#endif
-#ifndef MOE_BWD_STAGES
-#define MOE_BWD_STAGES 2
-#endif
-#ifndef MOE_BWD_KS
-#define MOE_BWD_KS 64       // K per ring stage: 64 or 32
-#endif
-constexpr int kKS = MOE_BWD_KS;
+constexpr int kBwdWM = 2;       // waves along M: 2 -> 128-row tiles
+constexpr int kBwdStages = 2;
+constexpr int kKS = 64;         // K per ring stage
 
-constexpr int kTileM = 64 * MOE_BWD_WM;
+constexpr int kTileM = 64 * kBwdWM;
 
 template <int MODE, bool GATHER, bool BF16>
 void launch_t(const BwdParams &prm, hipStream_t stream, int64_t tiles) {
-  constexpr int WM = MOE_BWD_WM, S = MOE_BWD_STAGES;
+  constexpr int WM = kBwdWM, S = kBwdStages;
   auto kern = k_grouped_gemm_bwd<MODE, WM, S, kKS, GATHER, BF16>;
-  static int per_cu = 0;
-  const int grid = persistent_grid((const void *)kern, WM * 128, per_cu, tiles);
+  static DeviceCache occ;
+  const int grid = persistent_grid((const void *)kern, WM * 128, occ, tiles);
   kern<<<dim3(grid), dim3(WM * 128), 0, stream>>>(prm);
 }
 

@@ -11,9 +11,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-#ifndef MOE_SCATTER_NV
-#define MOE_SCATTER_NV 8   // 16-byte vectors per lane per round of the row scatter
-#endif                // 4 waves per block
+constexpr int kScatterNV = 8;   // 16-byte vectors per lane per round of the row scatter
 constexpr int kMaxChunks = 1024;
 
 // Assignments per chunk: at least 2048, and few enough chunks that the scan's
@@ -266,7 +264,7 @@ extern "C" moe_status moe_permute(const void *x, moe_dtype dt, int T, int d,
   const int nvec = (int)((int64_t)d * elem / 16);
   const dim3 grid((T + 3) / 4);
   if (k <= 16)
-    k_row_scatter<MOE_SCATTER_NV><<<grid, dim3(kThreads), 0, stream>>>(
+    k_row_scatter<kScatterNV><<<grid, dim3(kThreads), 0, stream>>>(
         static_cast<const uint4 *>(x), T, k, nvec, inv, M, static_cast<uint4 *>(x_perm));
   else
     k_row_scatter_anyk<<<grid, dim3(kThreads), 0, stream>>>(static_cast<const uint4 *>(x), T, k,
