@@ -56,6 +56,10 @@ def _load():
     lib.orc_permute_index.argtypes = [P, i64, i32, P, P, P, P]
     lib.orc_permute_index.restype = i32
     lib.orc_gather_rows.argtypes = [P, i64, P, i64, i32, P]
+    lib.orc_expert_capacity.argtypes = [i64, i32, f64]
+    lib.orc_expert_capacity.restype = i64
+    lib.orc_permute_capacity.argtypes = [P, i64, i32, i64, P, P, P]
+    lib.orc_permute_capacity.restype = i32
     lib.orc_expert_swiglu_rows.argtypes = [P, i32, i64, i32, i32, P, P, P, P]
     lib.orc_combine.argtypes = [P, i32, i64, i32, i32, P, P, P, i32, P]
     lib.orc_alltoall_bytes.argtypes = [i64, i32, i64, i32, f64, f64, i32]
@@ -179,6 +183,39 @@ def permute_index(ids: np.ndarray, E: int):
     return counts, offsets, order, inv
 
 
+def expert_capacity(M: int, E: int, cf: float) -> int:
+    """N2: cap = ceil(CF M / E), the rows of every expert's block in the
+    padded batched form (oracle.c, orc_expert_capacity)."""
+    cap = _load().orc_expert_capacity(M, E, float(cf))
+    if cap < 0:
+        raise ValueError("orc_expert_capacity: arguments outside the contract")
+    return int(cap)
+
+
+def permute_capacity(ids: np.ndarray, E: int, cap: int):
+    """N2: counts [E] (before the cap), slot_of [M] (slot e cap + r, or -1 when
+    dropped), assign_of [E cap] (assignment, or -1 for a padding slot)
+    (oracle.c, orc_permute_capacity)."""
+    flat = _c(ids, np.int32).reshape(-1)
+    M = flat.size
+    counts = np.empty(E, np.int32)
+    slot_of = np.empty(M, np.int32)
+    assign_of = np.empty(E * cap, np.int32)
+    if _load().orc_permute_capacity(_ptr(flat), M, E, cap, _ptr(counts), _ptr(slot_of),
+                                    _ptr(assign_of)) != 0:
+        raise ValueError("orc_permute_capacity: expert id out of range or cap < 0")
+    return counts, slot_of, assign_of
+
+
+def gather_rows_padded(x: np.ndarray, assign_of: np.ndarray, k: int) -> np.ndarray:
+    """The padded batch: slot s holds token assign_of[s] // k bit for bit, a
+    padding slot (assign_of = -1) holds zeros."""
+    out = np.zeros((assign_of.size,) + x.shape[1:], x.dtype)
+    live = assign_of >= 0
+    out[live] = gather_rows(x, assign_of[live], k)
+    return out
+
+
 def gather_rows(x: np.ndarray, order: np.ndarray, k: int) -> np.ndarray:
     """X[order] with packed row p = token order[p] // k, bit for bit (oracle.c, orc_gather_rows)."""
     x = _c(x)
@@ -259,6 +296,25 @@ def layer_tokens(x, ids, w, w13, w2, tokens, sh_w13=None, sh_w2=None):
 # gives its shape (the combine's gradient is dispatched, the dispatch's
 # gradient combined).
 # --------------------------------------------------------------------------
+
+def layer_tokens_capacity(x, ids, w, slot_of, w13, w2, tokens, sh_w13=None, sh_w2=None):
+    """The padded batched form's output for selected tokens: the plain
+    definition with every dropped assignment (slot_of = -1) left out,
+    y[t] = sum over kept j of w[t,j] f_{ids[t,j]}(x[t]) (+ f_shared(x[t])),
+    evaluated with O4 and O5 in fp64.  Returns [len(tokens), d]."""
+    tokens = np.asarray(tokens, np.int64)
+    k = ids.shape[1]
+    kept = (np.asarray(slot_of).reshape(-1, k)[tokens] >= 0).reshape(-1)
+    xs = _c(x[tokens])
+    rows = np.repeat(xs, k, axis=0)[kept]
+    y_rows = expert_swiglu_rows(rows, ids[tokens].reshape(-1)[kept], w13, w2)
+    y_sh = None
+    if sh_w13 is not None:
+        y_sh = expert_swiglu_rows(xs, np.zeros(len(tokens), np.int32), sh_w13, sh_w2)
+    inv = np.full(len(tokens) * k, -1, np.int32)
+    inv[kept] = np.arange(int(kept.sum()), dtype=np.int32)
+    return combine(y_rows, inv, w[tokens], y_sh)
+
 
 def combine_backward(dy: np.ndarray, inv: np.ndarray, w: np.ndarray, y_perm: np.ndarray):
     """B5: dy_perm [T k, d] (row inv[t k + j] = w[t,j] dy[t]) and dw [T,k]

@@ -250,6 +250,49 @@ int orc_permute_index(const int32_t *ids, int64_t M, int E, int32_t *counts,
     return 0;
 }
 
+/* ------------------------------------------------------------------------
+ * N2  Pad to capacity and batch ("Expert parallelism", "Token permutation
+ * and grouped GEMMs", the second of its three ways to run the E expert
+ * products).  Every expert's block holds exactly cap rows, so one batched
+ * product of E blocks covers all of them; assignments beyond an expert's cap
+ * are dropped and blocks with fewer rows are padded.  cap is CF times an
+ * expert's fair share T k / E ("Load imbalance becomes idle time"), rounded
+ * up to a whole row, evaluated in double precision.
+ * ---------------------------------------------------------------------- */
+int64_t orc_expert_capacity(int64_t M, int E, double cf)
+{
+    if (E < 1 || M < 0 || !(cf > 0.0)) return -1;
+    return (int64_t)ceil(cf * (double)M / (double)E);
+}
+
+/* Which assignments an expert keeps: its assignments a = t k + j in
+ * increasing a (the order a stable sort leaves them in), the first cap of
+ * them.  Kept assignment number r of expert e goes to slot e cap + r.
+ *   counts[e]     all assignments to e, before the cap;
+ *   slot_of[a]    its slot, or -1 when the assignment is dropped;
+ *   assign_of[s]  the assignment in slot s, or -1 when the slot is padding.
+ * Written as a direct walk over the assignments with a fill count per
+ * expert. */
+int orc_permute_capacity(const int32_t *ids, int64_t M, int E, int64_t cap, int32_t *counts,
+                         int32_t *slot_of, int32_t *assign_of)
+{
+    if (cap < 0) return -1;
+    for (int64_t s = 0; s < (int64_t)E * cap; ++s) assign_of[s] = -1;
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t a = 0; a < M; ++a) {
+        int e = ids[a];
+        if (e < 0 || e >= E) return -1;
+        int64_t r = counts[e]++;
+        if (r < cap) {
+            slot_of[a] = (int32_t)(e * cap + r);
+            assign_of[e * cap + r] = (int32_t)a;
+        } else {
+            slot_of[a] = -1;
+        }
+    }
+    return 0;
+}
+
 /* X[order]: packed row p is a copy of token order[p] / k, bit for bit. */
 void orc_gather_rows(const void *x, int64_t row_bytes, const int32_t *order, int64_t M,
                      int k, void *x_perm)
@@ -310,6 +353,9 @@ void orc_expert_swiglu_rows(const void *xrows, int dtype, int64_t R, int d, int 
  * expert outputs are added with their gates, slot order j = 0..k-1, then the
  * shared expert's output (weight 1) if given:
  *   y[t] = sum_j w[t,j] y_perm[inv[t k + j]]  (+ y_shared[t]).
+ * An assignment that a capacity limit dropped (inv = -1; "Token permutation
+ * and grouped GEMMs": overflowing rows are dropped) has no expert output and
+ * adds nothing.
  * ---------------------------------------------------------------------- */
 void orc_combine(const void *y_perm, int dtype, int64_t T, int k, int d, const int32_t *inv,
                  const float *w, const void *y_shared, int sh_dtype, double *y)
@@ -320,6 +366,7 @@ void orc_combine(const void *y_perm, int dtype, int64_t T, int k, int d, const i
             double acc = 0.0;
             for (int j = 0; j < k; ++j) {
                 int64_t p = inv[t * k + j];
+                if (p < 0) continue;
                 acc += (double)w[t * k + j] * widen(y_perm, dtype, p * d + m);
             }
             if (y_shared) acc += widen(y_shared, sh_dtype, t * d + m);
