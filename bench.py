@@ -106,6 +106,71 @@ def load_accounting(cfg, counts, send_counts):
     return out
 
 
+def time_steps(layer, stages, stream, reps, warmup=2):
+    """Median step time (HIP events around each step on the launch stream)
+    and mean per-stage times of `reps` steps of layer, after `warmup`."""
+    import torch
+    for _ in range(warmup):
+        for name in stages:
+            getattr(layer, name)()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(reps)]
+    for i in range(reps):
+        evs[i][0].record(stream)
+        for j, name in enumerate(stages):
+            getattr(layer, name)()
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    steps = sorted(e[0].elapsed_time(e[-1]) for e in evs)
+    stage_ms = {name: round(sum(e[j].elapsed_time(e[j + 1]) for e in evs) / reps, 4)
+                for j, name in enumerate(stages)}
+    return steps[len(steps) // 2], stage_ms
+
+
+def alternatives(cfg, layer, stages, stream, grouped_ms, grouped_load, reps=10, loop_reps=3):
+    """The two other ways to run the expert products ("Expert parallelism",
+    "Token permutation and grouped GEMMs"), timed on the same batch and
+    weights as the grouped step: padded to capacity and batched at CF = 1 and
+    1.25 (dropped and padding rows from the batch's counts), and a loop of one
+    product pair per expert (its step includes the copy of the segment sizes
+    to the host that the loop needs)."""
+    import numpy as np
+    import torch
+
+    from token_routing_expert_amd.layer import MoeLayer, to_host
+    given = cfg.gating == "given"
+    common = dict(logits=layer.logits, sh_w13=getattr(layer, "sh_w13", None),
+                  sh_w2=getattr(layer, "sh_w2", None),
+                  topk_ids=layer.topk_ids if given else None, topk_w=layer.topk_w if given else None)
+    M = cfg.T * cfg.k
+    out = {"grouped": {"ms_per_step": round(grouped_ms, 4), "dropped_frac": 0.0,
+                       "tile_padding_frac": grouped_load["tile_padding_frac"],
+                       "mfma_padding_frac": grouped_load["mfma_padding_frac"]}}
+    for cf in (1.0, 1.25):
+        alt = MoeLayer(cfg, layer.x, layer.w13, layer.w2, fused_gather=True, capacity_factor=cf,
+                       **common)
+        ms, st = time_steps(alt, stages, stream, reps)
+        counts = to_host(alt.counts).astype(np.int64)
+        cap = alt.cap
+        kept = np.minimum(counts, cap)
+        out[f"capacity_cf{cf:g}"] = {
+            "cap": cap, "ms_per_step": round(ms, 4), "tokens_per_s": cfg.T / (ms * 1e-3),
+            "dropped_frac": round(float((counts - kept).sum()) / M, 4),
+            "padding_slots_frac": round(float(cfg.E * cap - kept.sum()) / (cfg.E * cap), 4),
+            "computed_rows_over_needed": round(cfg.E * cap / M, 4),
+            "gate_up_ms": st["gate_up"], "down_ms": st["down"]}
+        del alt
+        torch.cuda.empty_cache()
+    alt = MoeLayer(cfg, layer.x, layer.w13, layer.w2, fused_gather=False, expert_loop=True, **common)
+    ms, st = time_steps(alt, stages, stream, loop_reps, warmup=1)
+    out["expert_loop"] = {"ms_per_step": round(ms, 4), "tokens_per_s": cfg.T / (ms * 1e-3),
+                          "experts_ms": round(st["gate_up"] + st["down"], 4),
+                          "launches": 2 * int((to_host(alt.counts) > 0).sum())}
+    del alt
+    torch.cuda.empty_cache()
+    return out
+
+
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 GEMM_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "token_routing_expert_amd",
                            "csrc", "grouped_gemm.hip")
@@ -375,6 +440,8 @@ def main():
                          "then the backward to dx, the weight gradients and dlogits (bf16 only)")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="after the timed steps, time this many more from cold caches")
+    ap.add_argument("--no-alternatives", action="store_true",
+                    help="skip timing the capacity-padded (CF 1, 1.25) and per-expert-loop forms")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -577,6 +644,10 @@ def main():
         # stable scatter into the packed buffer X[order]) is measured here
         # on the same batch, outside the timed step, for its HBM figure.
         result["permute_packed"] = packed_permute_rate(layer, cfg, stage_bytes(cfg)[0])
+    if not args.no_alternatives and not router:
+        log("alternatives: capacity CF 1 and 1.25, one product pair per expert")
+        result["alternatives"] = alternatives(cfg, layer, stages, stream, step_ev[K // 2],
+                                              result["load"])
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(cfg, (x, w13, w2, logits, sh, ids_in, w_in))

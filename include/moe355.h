@@ -319,6 +319,87 @@ moe_status moe_unpermute_combine(const void *y_perm, moe_dtype dt, int T, int k,
                                  const int32_t *inv, const float *topk_w, const void *y_shared,
                                  void *y, hipStream_t stream);
 
+/*
+ * moe_unpermute_combine over expert outputs of any row count: y_perm has
+ * `rows` rows (for the capacity form below, E cap), and inv entries outside
+ * [0, rows) -- a dropped assignment's -1 -- contribute nothing.
+ * moe_unpermute_combine is this call with rows = T k.  Same layouts,
+ * precision and errors, plus INVALID_ARG for rows < 0; y_perm may be NULL
+ * only when rows = 0.
+ */
+moe_status moe_unpermute_combine_rows(const void *y_perm, int64_t rows, moe_dtype dt, int T,
+                                      int k, int d, const int32_t *inv, const float *topk_w,
+                                      const void *y_shared, void *y, hipStream_t stream);
+
+/* ========================================================================
+ * The two other ways to run the E expert products ("Expert parallelism",
+ * section "Token permutation and grouped GEMMs", which weighs three: a loop
+ * of products, padding every expert to a fixed capacity and batching, and
+ * the grouped product above).  Both are here for comparison with the grouped
+ * path, which is dropless and pads only inside a tile.
+ * ======================================================================== */
+
+/*
+ * The capacity: cap = ceil(cf M / E), cf times an expert's fair share of the
+ * M = T k assignments ("Load imbalance becomes idle time": a capacity factor
+ * caps every expert at CF times its fair share), evaluated in double
+ * precision.  Host function.  Returns -1 for E < 1, M < 0 or cf <= 0.
+ */
+int64_t moe_expert_capacity(int64_t M, int E, double cf);
+
+/* Bytes of device scratch moe_permute_capacity needs.  Host function. */
+size_t moe_permute_capacity_workspace_bytes(int T, int k, int E);
+
+/*
+ * Pad to capacity ("Token permutation and grouped GEMMs": every expert's
+ * block is exactly cap rows, so one batched product of E blocks runs all
+ * experts; overflowing rows are dropped).  Expert e keeps its first cap
+ * assignments in increasing a = t k + j -- the order moe_permute's stable
+ * sort gives -- at slots e cap + 0, 1, ...; its later assignments are
+ * dropped.  Blocks with fewer assignments are padded.
+ *
+ *   x, dt, T, d, topk_ids, k, E   as moe_permute.
+ *   cap        rows per expert block, >= 0 (moe_expert_capacity).
+ *   counts     [E] int32 out: assignments per expert BEFORE the cap (so the
+ *              dropped count is sum max(0, counts[e] - cap)).
+ *   offsets    [E+1] int32 out: offsets[e] = e cap, the segment list that
+ *              makes moe_grouped_swiglu (or its halves) one batched product.
+ *   order      [E cap] int32 out: the assignment in each slot, -1 for a
+ *              padding slot.  moe_grouped_gate_up_gather accepts it as is
+ *              (a padding slot then computes a row of x[T-1], never read).
+ *   inv        [T k] int32 out: each assignment's slot, -1 when dropped;
+ *              moe_unpermute_combine_rows(rows = E cap) skips those.
+ *   x_cap      [E cap, d] out, dtype dt: slot s holds token order[s] / k bit
+ *              for bit, a padding slot zeros.  x and x_cap both NULL:
+ *              index-only mode.
+ *   workspace  moe_permute_capacity_workspace_bytes(T, k, E) bytes of device
+ *              scratch owned by the caller.
+ * Errors: INVALID_ARG for null required pointers, T < 0, k < 1, E < 1,
+ * cap < 0, a small workspace, misaligned x / x_cap; UNSUPPORTED for E > 1024,
+ * d % 8 != 0, T k >= 2^31 or E cap >= 2^31.
+ */
+moe_status moe_permute_capacity(const void *x, moe_dtype dt, int T, int d, const int32_t *topk_ids,
+                                int k, int E, int cap, int32_t *counts, int32_t *offsets,
+                                int32_t *order, int32_t *inv, void *x_cap, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * A loop of products ("Token permutation and grouped GEMMs": one kernel
+ * launch per expert): moe_grouped_swiglu's result, computed as two launches
+ * per expert with rows, each sized and tiled for that expert's rows alone.
+ * The launch count and grid sizes come from offsets_host, a HOST copy of the
+ * device array offsets (the loop form needs the segment sizes on the host;
+ * getting them costs the caller a device-to-host copy).  Same layouts,
+ * precision and errors as moe_grouped_swiglu, plus INVALID_ARG when
+ * offsets_host is NULL or not non-decreasing within [0, M].  The results
+ * equal moe_grouped_swiglu's bit for bit when each expert's row count picks
+ * the same tile family as the grouped call's mean rows per expert.
+ */
+moe_status moe_expert_loop_swiglu(const void *a, moe_dtype dt, int M, int d, int ffn,
+                                  const int32_t *offsets, const int32_t *offsets_host, int G,
+                                  const void *w13, const void *w2, void *h, void *y,
+                                  hipStream_t stream);
+
 /* ========================================================================
  * Training: the forward product that keeps what the backward needs, and the
  * backward pass.  The backward runs the forward's steps in reverse: the

@@ -252,3 +252,54 @@ def test_dense_swiglu_validation(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(moe.MoeError):
         moe.load_library(str(tmp_path / "missing.so"))
+
+
+def test_capacity_host_function(lib):
+    """moe_expert_capacity against the oracle's independent ceil(cf M / E)."""
+    import oracle
+    lib.moe_expert_capacity.restype = ctypes.c_int64
+    lib.moe_expert_capacity.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_double]
+    for M in (0, 1, 12, 2048, 32768, 65536, 999_999):
+        for E in (1, 3, 4, 8, 256, 1024):
+            for cf in (0.01, 0.5, 1.0, 1.1, 1.25, 2.0, 7.3):
+                assert lib.moe_expert_capacity(M, E, cf) == oracle.expert_capacity(M, E, cf)
+    assert lib.moe_expert_capacity(10, 0, 1.0) == -1
+    assert lib.moe_expert_capacity(10, 4, 0.0) == -1
+    assert lib.moe_expert_capacity(-1, 4, 1.0) == -1
+
+
+def test_permute_capacity_validation(lib):
+    f = lib.moe_permute_capacity
+    P = ctypes.c_void_p
+    fake = P(4096)   # never dereferenced: every call below fails its host checks
+    ws = lib.moe_permute_capacity_workspace_bytes(64, 2, 8)
+    assert ws == lib.moe_permute_workspace_bytes(64, 2, 8) + 9 * 4
+    args = lambda T=64, k=2, E=8, cap=16, wsb=ws: (fake, 1, T, 64, fake, k, E, cap, fake, fake, fake,
+                                                   fake, fake, fake, wsb, NULL)
+    assert f(*args(T=-1)) == INVALID
+    assert f(*args(k=0)) == INVALID
+    assert f(*args(cap=-1)) == INVALID
+    assert f(*args(E=2048)) == UNSUPPORTED
+    assert f(*args(E=1024, cap=1 << 21)) == UNSUPPORTED     # E cap >= 2^31
+    assert f(*args(wsb=ws - 4)) == INVALID                  # workspace too small
+    assert f(fake, 1, 64, 64, fake, 2, 8, 16, NULL, fake, fake, fake, fake, fake, ws, NULL) == INVALID
+    # exactly one of x, x_cap given
+    assert f(fake, 1, 64, 64, fake, 2, 8, 16, fake, fake, fake, fake, NULL, fake, ws, NULL) == INVALID
+
+
+def test_combine_rows_and_loop_validation(lib):
+    P = ctypes.c_void_p
+    fake = P(4096)
+    lib.moe_unpermute_combine_rows.argtypes = [P, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, P, P, P, P, P]
+    g = lib.moe_unpermute_combine_rows
+    assert g(fake, -1, 1, 4, 2, 64, fake, fake, NULL, fake, NULL) == INVALID   # rows < 0
+    assert g(NULL, 8, 1, 4, 2, 64, fake, fake, NULL, fake, NULL) == INVALID    # rows > 0, no y_perm
+    assert g(fake, 8, 1, 0, 2, 64, fake, fake, NULL, fake, NULL) == 0          # T = 0: no-op
+    h = lib.moe_expert_loop_swiglu
+    bad = (ctypes.c_int32 * 3)(0, 6, 4)
+    out_of_range = (ctypes.c_int32 * 3)(0, 4, 9)
+    assert h(fake, 1, 8, 128, 128, fake, NULL, 2, fake, fake, fake, fake, NULL) == INVALID
+    assert h(fake, 1, 8, 128, 128, fake, bad, 2, fake, fake, fake, fake, NULL) == INVALID
+    assert h(fake, 1, 8, 128, 128, fake, out_of_range, 2, fake, fake, fake, fake, NULL) == INVALID
+    assert h(fake, 1, 8, 96, 128, fake, bad, 2, fake, fake, fake, fake, NULL) == UNSUPPORTED  # d % 128

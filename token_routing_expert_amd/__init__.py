@@ -26,7 +26,9 @@ EXPORTS = ("moe_status_string", "moe_route_topk", "moe_route_topk_biased", "moe_
            "moe_unpermute_combine", "moe_grouped_gate_up_save", "moe_combine_backward",
            "moe_gate_backward", "moe_grouped_down_backward", "moe_grouped_gate_up_backward",
            "moe_grouped_weight_grad", "moe_router_backward_workspace_bytes",
-           "moe_router_backward", "moe_dense_swiglu_workspace_bytes", "moe_dense_swiglu")
+           "moe_router_backward", "moe_dense_swiglu_workspace_bytes", "moe_dense_swiglu",
+           "moe_unpermute_combine_rows", "moe_expert_capacity",
+           "moe_permute_capacity_workspace_bytes", "moe_permute_capacity", "moe_expert_loop_swiglu")
 
 
 class MoeError(RuntimeError):
@@ -73,13 +75,21 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_dense_swiglu_workspace_bytes.argtypes = [i32, i32, i32]
     lib.moe_dense_swiglu_workspace_bytes.restype = sz
     lib.moe_dense_swiglu.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, P, sz, P]
+    lib.moe_unpermute_combine_rows.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P]
+    lib.moe_expert_capacity.argtypes = [i64, i32, ctypes.c_double]
+    lib.moe_expert_capacity.restype = i64
+    lib.moe_permute_capacity_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.moe_permute_capacity_workspace_bytes.restype = sz
+    lib.moe_permute_capacity.argtypes = [P, i32, i32, i32, P, i32, i32, i32, P, P, P, P, P, P, sz, P]
+    lib.moe_expert_loop_swiglu.argtypes = [P, i32, i32, i32, i32, P, P, i32, P, P, P, P, P]
     for name in ("moe_route_topk", "moe_route_topk_biased", "moe_router_logits",
                  "moe_router_bias_update", "moe_sigmoid_pinned", "moe_send_counts", "moe_permute",
                  "moe_grouped_swiglu", "moe_grouped_gate_up", "moe_grouped_gate_up_gather",
                  "moe_grouped_down", "moe_unpermute_combine", "moe_grouped_gate_up_save",
                  "moe_combine_backward", "moe_gate_backward", "moe_grouped_down_backward",
                  "moe_grouped_gate_up_backward", "moe_grouped_weight_grad", "moe_router_backward",
-                 "moe_dense_swiglu"):
+                 "moe_dense_swiglu", "moe_unpermute_combine_rows", "moe_permute_capacity",
+                 "moe_expert_loop_swiglu"):
         getattr(lib, name).restype = i32
     if path == LIB_PATH:
         _lib = lib
@@ -396,11 +406,14 @@ def moe_grouped_down(h, offsets, w2, y=None, stream=None):
     return y
 
 
-def moe_unpermute_combine(y_perm, inv, topk_w, y_shared=None, y=None, stream=None, k=None):
+def moe_unpermute_combine(y_perm, inv, topk_w, y_shared=None, y=None, stream=None, k=None,
+                          rows=None):
     """y [T, d] = sum_j topk_w[t,j] y_perm[inv[t k + j]] (+ y_shared[t]).
 
     topk_w None (then k is required): every gate is 1, the sum of a token's
-    k rows -- the permute's backward."""
+    k rows -- the permute's backward.  rows (optional): y_perm holds this
+    many rows (moe_unpermute_combine_rows; inv entries outside [0, rows),
+    such as a dropped assignment's -1, add nothing)."""
     torch = _torch()
     _dev(y_perm, "y_perm", _act_dtypes())
     _dev(inv, "inv", (torch.int32,))
@@ -412,7 +425,10 @@ def moe_unpermute_combine(y_perm, inv, topk_w, y_shared=None, y=None, stream=Non
         _dev(topk_w, "topk_w", (torch.float32,))
         T, k = topk_w.shape
     d = y_perm.shape[1]
-    if y_perm.shape[0] < T * k or inv.numel() != T * k:
+    if rows is not None:
+        if rows < 0 or y_perm.shape[0] < rows or inv.numel() != T * k:
+            raise MoeError("moe_unpermute_combine: inv must have T k entries and y_perm `rows` rows")
+    elif y_perm.shape[0] < T * k or inv.numel() != T * k:
         raise MoeError("moe_unpermute_combine: inv must have T k entries and y_perm at least T k rows")
     if y_shared is not None:
         _dev(y_shared, "y_shared", (y_perm.dtype,))
@@ -420,9 +436,99 @@ def moe_unpermute_combine(y_perm, inv, topk_w, y_shared=None, y=None, stream=Non
     y = torch.empty((T, d), dtype=y_perm.dtype, device=y_perm.device) if y is None else y
     _dev(y, "y", (y_perm.dtype,))
     _shape(y, (T, d), "y", "moe_unpermute_combine")
-    _check(load_library().moe_unpermute_combine(_ptr(y_perm), _dtype_code(y_perm), T, k, d,
-                                                _ptr(inv), _ptr(topk_w), _ptr(y_shared), _ptr(y),
-                                                _stream(stream)), "moe_unpermute_combine")
+    lib = load_library()
+    if rows is None:
+        _check(lib.moe_unpermute_combine(_ptr(y_perm), _dtype_code(y_perm), T, k, d, _ptr(inv),
+                                         _ptr(topk_w), _ptr(y_shared), _ptr(y), _stream(stream)),
+               "moe_unpermute_combine")
+    else:
+        _check(lib.moe_unpermute_combine_rows(_ptr(y_perm), int(rows), _dtype_code(y_perm), T, k, d,
+                                              _ptr(inv), _ptr(topk_w), _ptr(y_shared), _ptr(y),
+                                              _stream(stream)), "moe_unpermute_combine_rows")
+    return y
+
+
+# --------------------------------------------------------------------------
+# The two other ways to run the expert products: padded to a capacity and
+# batched, or one product per expert in a loop.
+# --------------------------------------------------------------------------
+
+def moe_expert_capacity(M, E, cf) -> int:
+    """cap = ceil(cf M / E) rows per expert block (host function)."""
+    cap = int(load_library().moe_expert_capacity(int(M), int(E), float(cf)))
+    if cap < 0:
+        raise MoeError("moe_expert_capacity: E < 1, M < 0 or cf <= 0")
+    return cap
+
+
+def moe_permute_capacity_workspace_bytes(T, k, E) -> int:
+    return int(load_library().moe_permute_capacity_workspace_bytes(T, k, E))
+
+
+def moe_permute_capacity(x, topk_ids, E, cap, counts=None, offsets=None, order=None, inv=None,
+                         x_cap=None, workspace=None, stream=None, rows=True):
+    """Pad to capacity: returns (counts [E] before the cap, offsets [E+1] = e cap,
+    order [E cap] (-1: padding slot), inv [T k] (-1: dropped), x_cap [E cap, d]
+    or None in index-only mode (rows=False))."""
+    torch = _torch()
+    _dev(x, "x", _act_dtypes())
+    _dev(topk_ids, "topk_ids", (torch.int32,))
+    T, d = x.shape
+    k = topk_ids.shape[1]
+    if topk_ids.shape[0] != T:
+        raise MoeError("moe_permute_capacity: topk_ids must have one row per token of x")
+    dev, i32 = x.device, torch.int32
+    S = E * cap
+    counts = torch.empty(E, dtype=i32, device=dev) if counts is None else counts
+    offsets = torch.empty(E + 1, dtype=i32, device=dev) if offsets is None else offsets
+    order = torch.empty(S, dtype=i32, device=dev) if order is None else order
+    inv = torch.empty(T * k, dtype=i32, device=dev) if inv is None else inv
+    for name, t, n in (("counts", counts, E), ("offsets", offsets, E + 1), ("order", order, S),
+                       ("inv", inv, T * k)):
+        _dev(t, name, (i32,))
+        _shape(t, (n,), name, "moe_permute_capacity")
+    if rows:
+        x_cap = torch.empty((S, d), dtype=x.dtype, device=dev) if x_cap is None else x_cap
+        _dev(x_cap, "x_cap", (x.dtype,))
+        _shape(x_cap, (S, d), "x_cap", "moe_permute_capacity")
+    elif x_cap is not None:
+        raise MoeError("moe_permute_capacity: x_cap given in index-only mode")
+    nbytes = moe_permute_capacity_workspace_bytes(T, k, E)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    _check(load_library().moe_permute_capacity(
+        _ptr(x) if rows else None, _dtype_code(x), T, d, _ptr(topk_ids), k, E, int(cap),
+        _ptr(counts), _ptr(offsets), _ptr(order), _ptr(inv), _ptr(x_cap), _ptr(workspace),
+        workspace.numel(), _stream(stream)), "moe_permute_capacity")
+    return counts, offsets, order, inv, x_cap
+
+
+def moe_expert_loop_swiglu(a, offsets, w13, w2, h=None, y=None, offsets_host=None, stream=None):
+    """moe_grouped_swiglu as a loop of one product pair per expert.  The loop
+    needs the segment sizes on the host: offsets_host (an int32 array of
+    G + 1 entries) or, when None, a copy of offsets made here (a device-to-host
+    synchronisation)."""
+    import numpy as np
+    torch = _torch()
+    G = _expert_shapes("moe_expert_loop_swiglu", a, offsets, w13=w13, w2=w2)
+    M, d = a.shape
+    ffn = w13.shape[2]
+    if w13.shape[3] != d or tuple(w2.shape) != (G, d, ffn):
+        raise MoeError("moe_expert_loop_swiglu: inconsistent shapes")
+    if offsets_host is None:
+        offsets_host = offsets.cpu().numpy()
+    oh = np.ascontiguousarray(np.asarray(offsets_host, dtype=np.int32))
+    if oh.shape != (G + 1,):
+        raise MoeError("moe_expert_loop_swiglu: offsets_host must have G + 1 entries")
+    h = torch.empty((M, ffn), dtype=a.dtype, device=a.device) if h is None else h
+    y = torch.empty((M, d), dtype=a.dtype, device=a.device) if y is None else y
+    _dev(h, "h", (a.dtype,))
+    _dev(y, "y", (a.dtype,))
+    _shape(h, (M, ffn), "h", "moe_expert_loop_swiglu")
+    _shape(y, (M, d), "y", "moe_expert_loop_swiglu")
+    _check(load_library().moe_expert_loop_swiglu(
+        _ptr(a), _dtype_code(a), M, d, ffn, _ptr(offsets), oh.ctypes.data_as(ctypes.c_void_p), G,
+        _ptr(w13), _ptr(w2), _ptr(h), _ptr(y), _stream(stream)), "moe_expert_loop_swiglu")
     return y
 
 

@@ -172,19 +172,20 @@ __global__ __launch_bounds__(kThreads) void k_combine_anyk(const uint4 *__restri
 
 using namespace moe;
 
-extern "C" moe_status moe_unpermute_combine(const void *y_perm, moe_dtype dt, int T, int k, int d,
-                                            const int32_t *inv, const float *topk_w,
-                                            const void *y_shared, void *y, hipStream_t stream) {
-  if (T < 0 || k < 1 || d < 1) return MOE_ERR_INVALID_ARG;
+extern "C" moe_status moe_unpermute_combine_rows(const void *y_perm, int64_t rows, moe_dtype dt,
+                                                 int T, int k, int d, const int32_t *inv,
+                                                 const float *topk_w, const void *y_shared, void *y,
+                                                 hipStream_t stream) {
+  if (T < 0 || k < 1 || d < 1 || rows < 0) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (d % 8 != 0 || k > 64 || (int64_t)T * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  if (!y_perm || !inv || !y) return MOE_ERR_INVALID_ARG;   // topk_w NULL: every gate is 1
-  if (!aligned16(y_perm) || !aligned16(y) || (y_shared && !aligned16(y_shared)))
+  if ((rows > 0 && !y_perm) || !inv || !y) return MOE_ERR_INVALID_ARG;   // topk_w NULL: every gate is 1
+  if ((y_perm && !aligned16(y_perm)) || !aligned16(y) || (y_shared && !aligned16(y_shared)))
     return MOE_ERR_INVALID_ARG;
   const int elem = dt == MOE_F32 ? 4 : 2;
   const int nvec = (int)((int64_t)d * elem / 16);
-  const int64_t M = (int64_t)T * k;
+  const int64_t M = rows;   // inv entries outside [0, rows) add nothing
   const dim3 grid((T + 3) / 4), block(kThreads);
   const uint4 *yp = static_cast<const uint4 *>(y_perm);
   const uint4 *ys = static_cast<const uint4 *>(y_shared);
@@ -214,4 +215,13 @@ extern "C" moe_status moe_unpermute_combine(const void *y_perm, moe_dtype dt, in
       k_combine_anyk<false><<<grid, block, 0, stream>>>(yp, T, k, nvec, inv, topk_w, ys, M, out);
   }
   return launch_status();
+}
+
+extern "C" moe_status moe_unpermute_combine(const void *y_perm, moe_dtype dt, int T, int k, int d,
+                                            const int32_t *inv, const float *topk_w,
+                                            const void *y_shared, void *y, hipStream_t stream) {
+  if (T < 0 || k < 1) return MOE_ERR_INVALID_ARG;
+  if (!y_perm && T > 0) return MOE_ERR_INVALID_ARG;
+  return moe_unpermute_combine_rows(y_perm, (int64_t)T * k, dt, T, k, d, inv, topk_w, y_shared, y,
+                                    stream);
 }

@@ -824,10 +824,13 @@ struct PpCfg {
 // gather (optional): packed row p of the product is row gather[p] / gk of a,
 // which then has a_rows rows.
 // gu (SAVE only): also store the gate and up pre-activations, [M, 2 N].
+// grid_rows (optional): the rows the grid is sized for, when the segments
+// cover fewer than M rows (one expert of a loop of products).
 template <bool BF16, bool SWIGLU, typename Cfg, bool SAVE = false>
 void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int G, const void *w,
                 void *out, hipStream_t stream, const int32_t *gather = nullptr, int gk = 1,
-                int a_rows = 0, void *gu = nullptr) {
+                int a_rows = 0, void *gu = nullptr, int grid_rows = -1) {
+  const int gm = grid_rows >= 0 ? grid_rows : M;
   const int elem = BF16 ? 2 : 4;
   const int kvec = K * elem / 16;
   // w13 is [G, 2, N, K] (gate rows, then up rows); w2 is [G, N, K].
@@ -836,7 +839,7 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
   if constexpr (Cfg::PP) {
     constexpr int BN = SWIGLU ? Cfg::BR / 2 : Cfg::BR;
     const int ntiles = N / BN;
-    const int64_t mtiles_max = (M + Cfg::BM - 1) / Cfg::BM + G;
+    const int64_t mtiles_max = (gm + Cfg::BM - 1) / Cfg::BM + G;
     auto kern = k_grouped_gemm_pp<BF16, Cfg::BM, Cfg::BR, Cfg::SA, Cfg::SB, Cfg::CPR, Cfg::DA, SWIGLU,
                                   Cfg::SPLIT, SAVE>;
     static DeviceCache occ;
@@ -846,7 +849,7 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
                                               ntiles, N, out, gather, gk, a_rows, gu);
   } else {
     const int ntiles = N / Cfg::BN;
-    const int64_t mtiles_max = (M + Cfg::BM - 1) / Cfg::BM + G;
+    const int64_t mtiles_max = (gm + Cfg::BM - 1) / Cfg::BM + G;
     auto kern = k_grouped_gemm<BF16, Cfg::BM, Cfg::BN, Cfg::WM, Cfg::WN, SWIGLU, Cfg::SA, Cfg::SB, SAVE>;
     static DeviceCache occ;
     const int threads = Cfg::WM * Cfg::WN * 64;
@@ -895,7 +898,7 @@ inline Family family_of(int M, int G, int d) {
 template <bool BF16>
 void launch_gate_up(Family f, const void *a, int M, int d, int ffn, const int32_t *offsets, int G,
                     const void *w13, void *h, hipStream_t stream, const int32_t *gather = nullptr,
-                    int gk = 1, int a_rows = 0, void *gu = nullptr) {
+                    int gk = 1, int a_rows = 0, void *gu = nullptr, int grid_rows = -1) {
   if (gu) {
     if (f == Family::Small)
       launch_one<BF16, true, G1Small, true>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows, gu);
@@ -906,25 +909,31 @@ void launch_gate_up(Family f, const void *a, int M, int d, int ffn, const int32_
     return;
   }
   if (f == Family::Small)
-    launch_one<BF16, true, G1Small>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows);
+    launch_one<BF16, true, G1Small>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows,
+                                    nullptr, grid_rows);
   else if (f == Family::Medium)
-    launch_one<BF16, true, G1Medium>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows);
+    launch_one<BF16, true, G1Medium>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows,
+                                     nullptr, grid_rows);
   else
-    launch_one<BF16, true, G1Large>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows);
+    launch_one<BF16, true, G1Large>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows,
+                                    nullptr, grid_rows);
 }
 
 // GEMM2: down, K = ffn, N = d.
 template <bool BF16>
 void launch_down(Family f, const void *h, int M, int ffn, int d, const int32_t *offsets, int G,
-                 const void *w2, void *y, hipStream_t stream) {
+                 const void *w2, void *y, hipStream_t stream, int grid_rows = -1) {
   if (f == Family::Small)
-    launch_one<BF16, false, G2Small>(h, M, ffn, d, offsets, G, w2, y, stream);
+    launch_one<BF16, false, G2Small>(h, M, ffn, d, offsets, G, w2, y, stream, nullptr, 1, 0, nullptr,
+                                     grid_rows);
   else if (f == Family::Medium || ffn >= kLongK)
     // A long K (wide experts) is better served by the medium tiles' deeper
     // rings of 64-byte slices, also when there are many rows per expert.
-    launch_one<BF16, false, G2Medium>(h, M, ffn, d, offsets, G, w2, y, stream);
+    launch_one<BF16, false, G2Medium>(h, M, ffn, d, offsets, G, w2, y, stream, nullptr, 1, 0, nullptr,
+                                      grid_rows);
   else
-    launch_one<BF16, false, G2Large>(h, M, ffn, d, offsets, G, w2, y, stream);
+    launch_one<BF16, false, G2Large>(h, M, ffn, d, offsets, G, w2, y, stream, nullptr, 1, 0, nullptr,
+                                     grid_rows);
 }
 
 // Backward input-gradient products on the ping-pong tiles (bf16).
@@ -1091,6 +1100,41 @@ extern "C" moe_status moe_grouped_swiglu(const void *a, moe_dtype dt, int M, int
   } else {
     launch_gate_up<false>(f, a, M, d, ffn, offsets, G, w13, h, stream);
     launch_down<false>(f, h, M, ffn, d, offsets, G, w2, y, stream);
+  }
+  return launch_status();
+}
+
+extern "C" moe_status moe_expert_loop_swiglu(const void *a, moe_dtype dt, int M, int d, int ffn,
+                                             const int32_t *offsets, const int32_t *offsets_host,
+                                             int G, const void *w13, const void *w2, void *h,
+                                             void *y, hipStream_t stream) {
+  const moe_status st = check_shape(dt, M, d, ffn, G);
+  if (st != MOE_OK) return st;
+  if (!offsets_host) return MOE_ERR_INVALID_ARG;
+  if (offsets_host[0] < 0 || offsets_host[G] > M) return MOE_ERR_INVALID_ARG;
+  for (int e = 0; e < G; ++e)
+    if (offsets_host[e + 1] < offsets_host[e]) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  if (!a || !offsets || !w13 || !w2 || !h || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(w13) || !aligned16(w2) || !aligned16(h) || !aligned16(y))
+    return MOE_ERR_INVALID_ARG;
+  const int64_t elem = dt == MOE_F32 ? 4 : 2;
+  const int64_t w13_bytes = 2 * (int64_t)ffn * d * elem, w2_bytes = (int64_t)d * ffn * elem;
+  // One product per expert: the kernels read the segment bounds from
+  // offsets + e (a one-expert list) and the grid is sized for its rows.
+  for (int e = 0; e < G; ++e) {
+    const int n = offsets_host[e + 1] - offsets_host[e];
+    if (n == 0) continue;
+    const Family f = family_of(n, 1, d);
+    const void *we13 = static_cast<const char *>(w13) + e * w13_bytes;
+    const void *we2 = static_cast<const char *>(w2) + e * w2_bytes;
+    if (dt == MOE_BF16) {
+      launch_gate_up<true>(f, a, M, d, ffn, offsets + e, 1, we13, h, stream, nullptr, 1, 0, nullptr, n);
+      launch_down<true>(f, h, M, ffn, d, offsets + e, 1, we2, y, stream, n);
+    } else {
+      launch_gate_up<false>(f, a, M, d, ffn, offsets + e, 1, we13, h, stream, nullptr, 1, 0, nullptr, n);
+      launch_down<false>(f, h, M, ffn, d, offsets + e, 1, we2, y, stream, n);
+    }
   }
   return launch_status();
 }

@@ -5,6 +5,8 @@
 // "Token permutation and grouped GEMMs" (zerotofrontier.app, "Expert
 // parallelism"): order is the stable argsort of the expert ids, X[order] puts
 // rows in expert order, and inv (inv[order] = arange) undoes it.
+#include <math.h>
+
 #include "common.hpp"
 
 namespace moe {
@@ -103,11 +105,17 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t *__restrict__ hist, int n
 // with equal expert ids find each other with one ballot per id bit, and the
 // rank of a lane is the number of equal lanes below it.  Ranks therefore
 // follow assignment order, which makes the sort stable.
+//
+// Capacity form (cap >= 0): an assignment's rank inside its expert is its
+// packed position minus seg_start[e]; rank r < cap goes to slot e cap + r,
+// a higher rank is dropped (inv = -1, no order entry).
 __global__ __launch_bounds__(kThreads) void k_multisplit(const int32_t *__restrict__ ids, int64_t M,
                                                          int E, int nbits, int64_t chunk,
                                                          const int32_t *__restrict__ base,
                                                          int32_t *__restrict__ order,
-                                                         int32_t *__restrict__ inv) {
+                                                         int32_t *__restrict__ inv,
+                                                         const int32_t *__restrict__ seg_start = nullptr,
+                                                         int cap = -1) {
   extern __shared__ int cnt[];  // [4][E]
   const int wv = uniform(threadIdx.x >> 6), lane = lane_id();
   for (int i = threadIdx.x; i < 4 * E; i += kThreads) cnt[i] = 0;
@@ -145,8 +153,15 @@ __global__ __launch_bounds__(kThreads) void k_multisplit(const int32_t *__restri
     int pos = 0;
     if (valid) {
       pos = mine[e] + __popcll(peers & below);
-      order[pos] = (int32_t)a;
-      inv[a] = pos;
+      if (cap < 0) {
+        order[pos] = (int32_t)a;
+        inv[a] = pos;
+      } else {
+        const int r = pos - seg_start[e];
+        const int slot = r < cap ? e * cap + r : -1;
+        if (slot >= 0) order[slot] = (int32_t)a;
+        inv[a] = slot;
+      }
     }
     // All lanes have read mine[] above; now the lowest lane of each group of
     // equal ids advances that expert's cursor.
@@ -154,6 +169,18 @@ __global__ __launch_bounds__(kThreads) void k_multisplit(const int32_t *__restri
     if (valid && (peers & below) == 0) mine[e] += __popcll(peers);
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// Capacity form: the slots no assignment reached (rank past the expert's
+// count) hold -1, and the block offsets are e cap.
+__global__ __launch_bounds__(kThreads) void k_capacity_fill(const int32_t *__restrict__ counts, int E,
+                                                            int cap, int32_t *__restrict__ order,
+                                                            int32_t *__restrict__ offsets) {
+  const int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (s <= E) offsets[s] = (int32_t)(s * cap);
+  if (s >= (int64_t)E * cap) return;
+  const int e = (int)(s / cap), r = (int)(s - (int64_t)e * cap);
+  if (r >= counts[e]) order[s] = -1;
 }
 
 // A store of data that is not read again soon (nontemporal: it does not
@@ -196,6 +223,36 @@ __global__ __launch_bounds__(kThreads) void k_row_scatter(const uint4 *__restric
         const int v = v0 + u * kWave + lane;
         if (v < nvec) store_stream(out + v, r[u]);
       }
+    }
+  }
+}
+
+// Capacity form: one wave per slot of the padded batch copies the row of the
+// slot's token, or writes zeros into a padding slot.
+__global__ __launch_bounds__(kThreads) void k_capacity_rows(const uint4 *__restrict__ x, int T, int k,
+                                                            int nvec, const int32_t *__restrict__ order,
+                                                            int64_t slots, uint4 *__restrict__ x_cap) {
+  const int64_t s = (int64_t)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+  if (s >= slots) return;
+  const int a = uniform(order[s]);
+  const int64_t t = a >= 0 ? a / k : -1;
+  uint4 *out = x_cap + s * nvec;
+  if (t < 0 || t >= T) {
+    for (int v = lane_id(); v < nvec; v += kWave) store_stream(out + v, make_uint4(0, 0, 0, 0));
+    return;
+  }
+  const uint4 *src = x + t * nvec;
+  for (int v0 = 0; v0 < nvec; v0 += kScatterNV * kWave) {
+    uint4 r[kScatterNV];
+#pragma unroll
+    for (int u = 0; u < kScatterNV; ++u) {
+      const int v = v0 + u * kWave + lane_id();
+      if (v < nvec) r[u] = src[v];
+    }
+#pragma unroll
+    for (int u = 0; u < kScatterNV; ++u) {
+      const int v = v0 + u * kWave + lane_id();
+      if (v < nvec) store_stream(out + v, r[u]);
     }
   }
 }
@@ -270,5 +327,56 @@ extern "C" moe_status moe_permute(const void *x, moe_dtype dt, int T, int d,
     k_row_scatter_anyk<<<grid, dim3(kThreads), 0, stream>>>(static_cast<const uint4 *>(x), T, k,
                                                              nvec, inv, M,
                                                              static_cast<uint4 *>(x_perm));
+  return launch_status();
+}
+
+extern "C" int64_t moe_expert_capacity(int64_t M, int E, double cf) {
+  if (E < 1 || M < 0 || !(cf > 0.0)) return -1;
+  return (int64_t)ceil(cf * (double)M / (double)E);
+}
+
+extern "C" size_t moe_permute_capacity_workspace_bytes(int T, int k, int E) {
+  if (E <= 0) return 16;
+  return moe_permute_workspace_bytes(T, k, E) + (size_t)(E + 1) * sizeof(int32_t);
+}
+
+extern "C" moe_status moe_permute_capacity(const void *x, moe_dtype dt, int T, int d,
+                                           const int32_t *topk_ids, int k, int E, int cap,
+                                           int32_t *counts, int32_t *offsets, int32_t *order,
+                                           int32_t *inv, void *x_cap, void *workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+  if (T < 0 || k < 1 || E < 1 || d < 1 || cap < 0) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (E > 1024 || d % 8 != 0 || (int64_t)T * k >= (1ll << 31) || (int64_t)E * cap >= (1ll << 31))
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t M = (int64_t)T * k, slots = (int64_t)E * cap;
+  if (!counts || !offsets || !workspace) return MOE_ERR_INVALID_ARG;
+  if ((M > 0 && (!topk_ids || !inv)) || (slots > 0 && !order)) return MOE_ERR_INVALID_ARG;
+  const bool rows = x || x_cap;   // both NULL: index-only mode
+  if (rows && slots > 0 && (!x || !x_cap || !aligned16(x) || !aligned16(x_cap)))
+    return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < moe_permute_capacity_workspace_bytes(T, k, E)) return MOE_ERR_INVALID_ARG;
+
+  const int64_t chunk = chunk_size(M > 0 ? M : 1);
+  const int nchunks = (int)((M + chunk - 1) / chunk);
+  int32_t *hist = static_cast<int32_t *>(workspace);
+  int32_t *seg_start = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) +
+                                                   moe_permute_workspace_bytes(T, k, E));
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  if (nchunks > 0)
+    k_hist<<<dim3(nchunks), dim3(kThreads), sizeof(int) * E, stream>>>(topk_ids, M, E, chunk, hist);
+  k_scan<<<dim3(1), dim3(1024), 0, stream>>>(hist, nchunks, E, counts, seg_start);
+  if (M > 0)
+    k_multisplit<<<dim3(nchunks), dim3(kThreads), sizeof(int) * 4 * E, stream>>>(
+        topk_ids, M, E, nbits, chunk, hist, order, inv, seg_start, cap);
+  const int64_t fill = (slots > E + 1 ? slots : E + 1);
+  k_capacity_fill<<<dim3((unsigned)((fill + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(
+      counts, E, cap, order, offsets);
+  if (!rows || slots == 0) return launch_status();
+  const int elem = dt == MOE_F32 ? 4 : 2;
+  const int nvec = (int)((int64_t)d * elem / 16);
+  k_capacity_rows<<<dim3((unsigned)((slots + 3) / 4)), dim3(kThreads), 0, stream>>>(
+      static_cast<const uint4 *>(x), T, k, nvec, order, slots, static_cast<uint4 *>(x_cap));
   return launch_status();
 }

@@ -11,6 +11,8 @@ from __future__ import annotations
 import numpy as np
 
 from . import (MoeError, moe_combine_backward, moe_gate_backward, moe_grouped_down,
+               moe_expert_capacity, moe_expert_loop_swiglu, moe_permute_capacity,
+               moe_permute_capacity_workspace_bytes,
                moe_router_backward,
                moe_grouped_down_backward, moe_grouped_gate_up, moe_grouped_gate_up_backward,
                moe_grouped_gate_up_gather, moe_grouped_gate_up_save, moe_grouped_swiglu,
@@ -71,6 +73,18 @@ class MoeLayer:
     bias_lr != 0 every forward ends with the bias update from that batch's
     per-expert counts, so the next forward routes with the new bias.
 
+    capacity_factor (a number) runs the experts the second of the three ways
+    "Expert parallelism", section "Token permutation and grouped GEMMs", sets
+    out: every expert's block padded (or cut) to cap = ceil(CF T k / E) rows
+    and one batched product over the E blocks; an expert's assignments past
+    its cap are dropped and add nothing to the combine.  The permute then
+    writes block-padded order and inv (moe_permute_capacity), the products run
+    over E cap rows, and the combine skips dropped slots.
+
+    expert_loop=True runs them the first way: one product pair per expert
+    (moe_expert_loop_swiglu), on the packed rows X[order], with the segment
+    sizes copied to the host in every step.
+
     train=True keeps what the backward needs: the first product also stores
     the pre-activations gu, and ``backward(dy)`` then returns the gradients
     of the layer (bf16 or fp32; with a router product bf16).  The packed
@@ -85,11 +99,20 @@ class MoeLayer:
 
     def __init__(self, cfg: MoeConfig, x, w13, w2, logits=None, sh_w13=None, sh_w2=None,
                  topk_ids=None, topk_w=None, device="cuda", fused_gather=False, w_router=None,
-                 bias=None, bias_lr=0.0, merge_shared=False, train=False):
+                 bias=None, bias_lr=0.0, merge_shared=False, train=False, capacity_factor=None,
+                 expert_loop=False):
         import torch
         self.cfg = cfg
         self.train = bool(train)
         self.fused_gather = fused_gather
+        self.capacity_factor = capacity_factor
+        self.expert_loop = bool(expert_loop)
+        if (capacity_factor is not None or expert_loop) and (train or merge_shared):
+            raise ValueError("capacity_factor / expert_loop: forward only, shared expert not merged")
+        if capacity_factor is not None and expert_loop:
+            raise ValueError("capacity_factor and expert_loop are two different forms")
+        if expert_loop and fused_gather:
+            raise ValueError("expert_loop runs on the packed rows (fused_gather=False)")
         if merge_shared and not (fused_gather and cfg.shared):
             raise ValueError("merge_shared needs the fused-gather path and a shared expert")
         self.merge_shared = bool(merge_shared)
@@ -131,10 +154,15 @@ class MoeLayer:
         self.send_counts = torch.empty((cfg.n_ep, cfg.n_ep), dtype=i32, device=dev) if cfg.n_ep else None
         self.counts = torch.empty(E, dtype=i32, device=dev)
         self.inv = torch.empty(M, dtype=i32, device=dev)
+        # Rows of the expert products: M packed rows, or E cap block rows.
+        self.cap = None if capacity_factor is None else moe_expert_capacity(M, E, capacity_factor)
+        R = M if self.cap is None else E * self.cap
+        self.rows = R
         keep_rows = not fused_gather or (self.train and not merge_shared)
-        self.x_perm = torch.empty((M, d), dtype=act, device=dev) if keep_rows else None
-        self.workspace = torch.empty(max(16, moe_permute_workspace_bytes(T, k, E)), dtype=torch.uint8,
-                                     device=dev)
+        self.x_perm = torch.empty((R, d), dtype=act, device=dev) if keep_rows else None
+        ws = moe_permute_workspace_bytes(T, k, E) if self.cap is None else \
+            moe_permute_capacity_workspace_bytes(T, k, E)
+        self.workspace = torch.empty(max(16, ws), dtype=torch.uint8, device=dev)
         self.y = torch.empty((T, d), dtype=act, device=dev)
         if self.merge_shared:
             # The permute writes the first M (E + 1) entries; the shared group's
@@ -150,9 +178,9 @@ class MoeLayer:
             self.y_perm, self.y_sh = self.y_perm_all[:M], self.y_perm_all[M:]
         else:
             self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
-            self.order = torch.empty(M, dtype=i32, device=dev)
-            self.h = torch.empty((M, ffn), dtype=act, device=dev)
-            self.y_perm = torch.empty((M, d), dtype=act, device=dev)
+            self.order = torch.empty(R, dtype=i32, device=dev)
+            self.h = torch.empty((R, ffn), dtype=act, device=dev)
+            self.y_perm = torch.empty((R, d), dtype=act, device=dev)
         if self.merge_shared:
             self.sh_w13, self.sh_w2 = self.w13_all[E:], self.w2_all[E:]
         elif cfg.shared:
@@ -192,11 +220,20 @@ class MoeLayer:
             moe_send_counts(self.topk_ids, c.E, c.n_ep, self.send_counts, stream=stream)
 
     def permute(self, stream=None):
+        if self.cap is not None:
+            moe_permute_capacity(self.x, self.topk_ids, self.cfg.E, self.cap, self.counts,
+                                 self.offsets, self.order, self.inv, self.x_perm, self.workspace,
+                                 stream=stream, rows=self.x_perm is not None)
+            return
         moe_permute(self.x, self.topk_ids, self.cfg.E, self.counts, self.offsets, self.order,
                     self.inv, self.x_perm, self.workspace, stream=stream,
                     rows=self.x_perm is not None)
 
     def experts_routed(self, stream=None):
+        if self.expert_loop:
+            moe_expert_loop_swiglu(self.x_perm, self.offsets, self.w13, self.w2, self.h, self.y_perm,
+                                   stream=stream)
+            return
         if self.fused_gather or self.train:
             self.gate_up(stream)
             self.down(stream)
@@ -206,6 +243,11 @@ class MoeLayer:
 
     def gate_up(self, stream=None):
         """The routed experts' first product alone (the same launch experts_routed makes)."""
+        if self.expert_loop:
+            # The loop form's launches come in pairs per expert: both products
+            # run here, down() has nothing left to do.
+            self.experts_routed(stream)
+            return
         if self.train:
             if self.merge_shared:
                 moe_grouped_gate_up_save(self.x, self.offsets_all, self.w13_all, self.h, self.gu,
@@ -227,6 +269,8 @@ class MoeLayer:
 
     def down(self, stream=None):
         """The routed experts' second product alone."""
+        if self.expert_loop:
+            return
         if self.merge_shared:
             moe_grouped_down(self.h, self.offsets_all, self.w2_all, self.y_perm_all, stream=stream)
         else:
@@ -253,7 +297,8 @@ class MoeLayer:
         self.experts_shared(stream)
 
     def combine(self, stream=None):
-        moe_unpermute_combine(self.y_perm, self.inv, self.topk_w, self.y_sh, self.y, stream=stream)
+        moe_unpermute_combine(self.y_perm, self.inv, self.topk_w, self.y_sh, self.y, stream=stream,
+                              rows=self.rows if self.cap is not None else None)
 
     def bias_update(self, stream=None):
         """bias += bias_lr (mean load - load) from this batch's counts (a no-op
