@@ -196,6 +196,23 @@ moe_status moe_permute(const void *x, moe_dtype dt, int T, int d, const int32_t 
                        hipStream_t stream);
 
 /*
+ * moe_permute for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call without the workspace argument.  Its per-chunk histograms go to a
+ * library-owned device array of 1 MiB (moe_permute_workspace_bytes(T, k, E)
+ * must not exceed 1048576: every call with E <= 256 fits, E = 1024 up to
+ * T k = 2^19), one copy per GPU, held until the process ends.  The
+ * call allocates nothing; its first call on a device looks up that device's
+ * copy.  Same arguments, outputs, layouts and errors as moe_permute, plus
+ * UNSUPPORTED when the workspace would exceed the array and MOE_ERR_HIP when
+ * the array cannot be looked up.  Calls that overlap on one GPU (several
+ * streams or host threads at once) share the array and race; serialise them.
+ */
+moe_status moe_permute_noalloc(const void *x, moe_dtype dt, int T, int d, const int32_t *topk_ids,
+                               int k, int E, int32_t *counts, int32_t *offsets, int32_t *order,
+                               int32_t *inv, void *x_perm, hipStream_t stream);
+
+/*
  * Grouped SwiGLU expert MLP (step 5; "Token permutation and grouped GEMMs":
  * one launch computes the products of all experts' row segments, scheduling
  * output tiles from all of them, with no padding beyond the tile and nothing

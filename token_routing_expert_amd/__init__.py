@@ -28,7 +28,8 @@ EXPORTS = ("moe_status_string", "moe_route_topk", "moe_route_topk_biased", "moe_
            "moe_grouped_weight_grad", "moe_router_backward_workspace_bytes",
            "moe_router_backward", "moe_dense_swiglu_workspace_bytes", "moe_dense_swiglu",
            "moe_unpermute_combine_rows", "moe_expert_capacity",
-           "moe_permute_capacity_workspace_bytes", "moe_permute_capacity", "moe_expert_loop_swiglu")
+           "moe_permute_capacity_workspace_bytes", "moe_permute_capacity", "moe_expert_loop_swiglu",
+           "moe_permute_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -82,6 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_permute_capacity_workspace_bytes.restype = sz
     lib.moe_permute_capacity.argtypes = [P, i32, i32, i32, P, i32, i32, i32, P, P, P, P, P, P, sz, P]
     lib.moe_expert_loop_swiglu.argtypes = [P, i32, i32, i32, i32, P, P, i32, P, P, P, P, P]
+    lib.moe_permute_noalloc.argtypes = [P, i32, i32, i32, P, i32, i32, P, P, P, P, P, P]
     for name in ("moe_route_topk", "moe_route_topk_biased", "moe_router_logits",
                  "moe_router_bias_update", "moe_sigmoid_pinned", "moe_send_counts", "moe_permute",
                  "moe_grouped_swiglu", "moe_grouped_gate_up", "moe_grouped_gate_up_gather",
@@ -89,7 +91,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                  "moe_combine_backward", "moe_gate_backward", "moe_grouped_down_backward",
                  "moe_grouped_gate_up_backward", "moe_grouped_weight_grad", "moe_router_backward",
                  "moe_dense_swiglu", "moe_unpermute_combine_rows", "moe_permute_capacity",
-                 "moe_expert_loop_swiglu"):
+                 "moe_expert_loop_swiglu", "moe_permute_noalloc"):
         getattr(lib, name).restype = i32
     if path == LIB_PATH:
         _lib = lib
@@ -273,6 +275,30 @@ def moe_permute(x, topk_ids, E, counts=None, offsets=None, order=None, inv=None,
         _ptr(x) if rows else None, _dtype_code(x), T, d, _ptr(topk_ids), k, E, _ptr(counts),
         _ptr(offsets), _ptr(order), _ptr(inv), _ptr(x_perm), _ptr(workspace), workspace.numel(),
         _stream(stream)), "moe_permute")
+    return counts, offsets, order, inv, x_perm
+
+
+def moe_permute_noalloc(x, topk_ids, E, counts, offsets, order, inv, x_perm=None, stream=None):
+    """moe_permute without a workspace: the library's own device scratch holds
+    the histograms, so the call allocates nothing (every output must be
+    given; x_perm None is the index-only mode).  Returns the outputs."""
+    torch = _torch()
+    _dev(x, "x", _act_dtypes())
+    _dev(topk_ids, "topk_ids", (torch.int32,))
+    T, d = x.shape
+    k = topk_ids.shape[1]
+    M = T * k
+    for name, t, n in (("counts", counts, E), ("offsets", offsets, E + 1), ("order", order, M),
+                       ("inv", inv, M)):
+        _dev(t, name, (torch.int32,))
+        _shape(t, (n,), name, "moe_permute_noalloc")
+    if x_perm is not None:
+        _dev(x_perm, "x_perm", (x.dtype,))
+        _shape(x_perm, (M, d), "x_perm", "moe_permute_noalloc")
+    rows = x_perm is not None
+    _check(load_library().moe_permute_noalloc(
+        _ptr(x) if rows else None, _dtype_code(x), T, d, _ptr(topk_ids), k, E, _ptr(counts),
+        _ptr(offsets), _ptr(order), _ptr(inv), _ptr(x_perm), _stream(stream)), "moe_permute_noalloc")
     return counts, offsets, order, inv, x_perm
 
 

@@ -7,6 +7,9 @@
 // rows in expert order, and inv (inv[order] = arange) undoes it.
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 
 namespace moe {
@@ -328,6 +331,53 @@ extern "C" moe_status moe_permute(const void *x, moe_dtype dt, int T, int d,
                                                              nvec, inv, M,
                                                              static_cast<uint4 *>(x_perm));
   return launch_status();
+}
+
+// ---- the permute without a caller workspace --------------------------------
+// The per-chunk histograms live in this file-scope device array instead.  In
+// host code `scratch` names a host-side stand-in: the device address of each
+// GPU's copy comes from hipGetSymbolAddress, once per device, and only that
+// address is ever passed to a kernel.
+constexpr size_t kNoAllocScratchBytes = 1u << 20;
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / sizeof(int32_t)];
+
+namespace moe {
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxScratchDevices];   // zero-initialised: static storage
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch`, looked up on the first call on
+// that device; NULL if the lookup fails.
+void *device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+    (void)hipGetLastError();   // clear the error so it does not surface at a later call
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_permute_noalloc(const void *x, moe_dtype dt, int T, int d,
+                                          const int32_t *topk_ids, int k, int E, int32_t *counts,
+                                          int32_t *offsets, int32_t *order, int32_t *inv,
+                                          void *x_perm, hipStream_t stream) {
+  if (T < 0 || k < 1 || E < 1 || d < 1) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_permute_workspace_bytes(T, k, E);
+  if (need > kNoAllocScratchBytes) return MOE_ERR_UNSUPPORTED;
+  void *ws = device_scratch();
+  if (!ws) return MOE_ERR_HIP;
+  return moe_permute(x, dt, T, d, topk_ids, k, E, counts, offsets, order, inv, x_perm, ws,
+                     kNoAllocScratchBytes, stream);
 }
 
 extern "C" int64_t moe_expert_capacity(int64_t M, int E, double cf) {
