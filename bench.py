@@ -17,6 +17,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 METRIC = "MoE-layer fwd tokens/s at DSV3 shape, 1 GPU; % MFMA peak; permute % HBM BW"
 PEAK_MFMA = {"bf16": 2.5e15, "f32": 157.3e12}     # dense, MI355X published
 PEAK_HBM = 8.0e12
@@ -196,6 +198,61 @@ def measured_traffic(workload, path="gather"):
     return int(t["bytes_per_launch"])
 
 
+def host_info():
+    """The host the oracle runs on: CPU model, sockets, physical cores and
+    hardware threads (from /proc/cpuinfo), and the threads this process may use."""
+    model, sockets, cores = None, set(), set()
+    try:
+        phys = core = None
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "model name" and model is None:
+                    model = val
+                elif key == "physical id":
+                    phys = val
+                    sockets.add(val)
+                elif key == "core id":
+                    core = val
+                    cores.add((phys, core))
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "sockets": len(sockets) or None, "physical_cores": len(cores) or None,
+            "hardware_threads": os.cpu_count(), "threads_usable_here": usable}
+
+
+def oracle_small_layer_single_thread():
+    """The oracle's whole forward (route, send counts, permute with the row
+    copy, experts, combine) on the small fp32 layer (1,024 tokens, 8 experts,
+    top-2, d 256, ffn 512), on one thread: seconds and tokens/s."""
+    import oracle
+    from token_routing_expert_amd import inputs
+    cfg = inputs.CONFIGS["small_fp32"]
+    logits, x = inputs.gen_logits(cfg), inputs.gen_x(cfg)
+    w13, w2 = inputs.gen_expert_weights(cfg)
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        ids, w = oracle.route(logits, cfg.k, cfg.gating, cfg.renormalize)
+        oracle.send_counts(ids, cfg.E, cfg.n_ep)
+        _, offsets, order, inv = oracle.permute_index(ids, cfg.E)
+        rows = oracle.gather_rows(x, order, cfg.k)
+        e_of = np.repeat(np.arange(cfg.E, dtype=np.int32), np.diff(offsets))
+        y_perm = oracle.expert_swiglu_rows(rows, e_of, w13, w2)
+        oracle.combine(y_perm, inv, w)
+        sec = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(threads)
+    return {"workload": "small_fp32", "threads": 1, "seconds": round(sec, 4),
+            "tokens_per_s": round(cfg.T / sec, 1)}
+
+
 def cpu_baseline(cfg, data, budget_s=15.0, max_tokens=2048):
     """The oracle, untuned, on the host cores: route, send counts and permute on
     every token, then experts and combine on seeded tokens until about budget_s
@@ -230,6 +287,8 @@ def cpu_baseline(cfg, data, budget_s=15.0, max_tokens=2048):
         "value": 1.0 / per_token,
         "unit": "tokens/s",
         "cores": oracle.num_threads(),
+        "host": host_info(),
+        "small_layer_single_thread": oracle_small_layer_single_thread(),
         "kind": "oracle",
         "sample": (f"route, send counts, permute and row gather on all {cfg.T} tokens "
                    f"({t_index:.2f} s) + experts and combine on {done} seeded tokens "
@@ -438,7 +497,7 @@ def main():
     ap.add_argument("--train", action="store_true",
                     help="time a training step instead: the forward keeping the pre-activations, "
                          "then the backward to dx, the weight gradients and dlogits (bf16 only)")
-    ap.add_argument("--cold-steps", type=int, default=5,
+    ap.add_argument("--cold-steps", type=int, default=10,
                     help="after the timed steps, time this many more from cold caches")
     ap.add_argument("--no-alternatives", action="store_true",
                     help="skip timing the capacity-padded (CF 1, 1.25) and per-expert-loop forms")
@@ -545,6 +604,9 @@ def main():
     cold_info = None
     if n_cold:
         cold_info = {"steps": n_cold, "step_ms_p50": round(cold_step[n_cold // 2], 4),
+                     "tokens_per_s_p50": round(cfg.T / (cold_step[n_cold // 2] * 1e-3), 1),
+                     "step_ms_p10": round(cold_step[int(0.1 * (n_cold - 1) + 0.5)], 4),
+                     "step_ms_p90": round(cold_step[int(0.9 * (n_cold - 1) + 0.5)], 4),
                      "stages_ms": {name: round(sum(c[j].elapsed_time(c[j + 1]) for c in cold) / n_cold, 4)
                                    for j, name in enumerate(stages)}}
 
@@ -634,6 +696,10 @@ def main():
         },
         "stages": stage_info,
         "step_ms_events": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
+        "headline": ("value: the K timed steps back to back (wall clock around them; a step may "
+                     "find the previous step's data in the L2s and the 256 MB MALL); "
+                     "cold_cache.tokens_per_s_p50: the median of steps each run after a 1 GiB fill "
+                     "that evicts both (HIP events, the fill outside them)"),
         "cold_cache": cold_info,
         "load": load_accounting(cfg, counts,
                                 to_host(layer.send_counts) if cfg.n_ep else None),

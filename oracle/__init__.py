@@ -19,6 +19,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle355.so")
+# Another build of oracle.c to load instead (the tests' sanitizer run sets it).
+_LIB_OVERRIDE = os.environ.get("MOE_ORACLE_LIB")
 
 F32, BF16, F64 = 0, 1, 2
 SOFTMAX, SIGMOID = 0, 1
@@ -41,9 +43,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
     i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
     lib.orc_sigmoid_pinned.argtypes = [ctypes.c_float]
@@ -77,6 +82,7 @@ def _load():
     lib.orc_gate_backward.restype = i32
     lib.orc_router_backward.argtypes = [P, i32, i64, i32, P, i32, P, P, P]
     lib.orc_num_threads.restype = i32
+    lib.orc_set_num_threads.argtypes = [i32]
     _lib = lib
     return lib
 
@@ -97,6 +103,11 @@ def _dtype_code(a: np.ndarray) -> int:
     if a.dtype == np.float64:
         return F64
     raise TypeError(f"unsupported oracle dtype {a.dtype}")
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's OpenMP loops use from now on (timing only)."""
+    _load().orc_set_num_threads(int(n))
 
 
 def num_threads() -> int:

@@ -744,6 +744,8 @@ void orc_router_backward(const void *x, int dtype, int64_t T, int d, const void 
 #ifdef _OPENMP
 #include <omp.h>
 int orc_num_threads(void) { return omp_get_max_threads(); }
+void orc_set_num_threads(int n) { if (n > 0) omp_set_num_threads(n); }
 #else
 int orc_num_threads(void) { return 1; }
+void orc_set_num_threads(int n) { (void)n; }
 #endif
