@@ -86,6 +86,19 @@ def packed_permute_rate(layer, cfg, nbytes, reps=10):
             "hbm_frac": round(nbytes / (ms * 1e-3) / PEAK_HBM, 4)}
 
 
+def forward_tile_rows(cfg, M, cus=256):
+    """Rows per tile of the forward products (the library's tile choice): 32
+    for few rows per expert or a problem that the larger tiles would spread
+    over fewer tiles than compute units, else 320 up to 320 rows per expert
+    and 256 beyond."""
+    per_expert = -(-M // cfg.E) if cfg.E else 0
+    if per_expert < 96 or cfg.d % 256:
+        return 32
+    bm = 320 if per_expert <= 320 else 256
+    tiles = cfg.E * -(-per_expert // bm) * (cfg.d // 256)
+    return 32 if tiles < cus else bm
+
+
 def load_accounting(cfg, counts, send_counts):
     """Load and padding statistics of the batch: rows per expert, the rows the
     GEMM tiles compute beyond the real ones (tile padding), and the imbalance
@@ -94,8 +107,7 @@ def load_accounting(cfg, counts, send_counts):
     import numpy as np
     counts = np.asarray(counts, np.int64)
     M = int(counts.sum())
-    per_expert = -(-M // cfg.E) if cfg.E else 0
-    bm = 32 if per_expert < 96 or cfg.d % 256 else (320 if per_expert <= 288 else 256)
+    bm = forward_tile_rows(cfg, M)
     tiled = int((-(-counts // bm) * bm).sum())
     blocks = int((-(-counts // 32) * 32).sum())   # MFMAs run on 32-row blocks with a live row
     out = {"rows": M, "rows_per_expert_min": int(counts.min()), "rows_per_expert_max": int(counts.max()),

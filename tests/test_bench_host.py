@@ -62,14 +62,28 @@ def test_load_accounting_by_hand():
     cfg = dataclasses.replace(inputs.CONFIGS["dsv3_prefill"], E=4)
     counts = np.array([300, 0, 10, 290])
     acc = bench.load_accounting(cfg, counts, np.array([[1, 2], [3, 4]]))
-    # 600 rows, 150 per expert on average: 320-row tiles; 32-row MFMA blocks
-    assert acc["rows"] == 600 and acc["tile_rows"] == 320
+    # 600 rows, 150 per expert on average: the 320-row tiles would give only
+    # 4 x 28 down tiles for 256 compute units, so the forward uses 32-row
+    # tiles, which are also the MFMA blocks
+    assert acc["rows"] == 600 and acc["tile_rows"] == 32
     assert acc["rows_per_expert_min"] == 0 and acc["rows_per_expert_max"] == 300
     assert acc["empty_experts"] == 1 and acc["dropped_rows"] == 0
-    assert acc["tile_padding_frac"] == pytest.approx((3 * 320 - 600) / 600)
+    assert acc["tile_padding_frac"] == pytest.approx((320 + 32 + 320 - 600) / 600)
     assert acc["mfma_padding_frac"] == pytest.approx((320 + 32 + 320 - 600) / 600)
     # receiving ranks get column sums 4 and 6: 6 / mean 5
     assert acc["ep_recv_imbalance"] == pytest.approx(1.2)
+
+
+def test_forward_tile_rows_at_the_workloads():
+    """The tile rows the library picks at the five workloads: the prefill
+    layer's ~256 rows per expert fit one 320-row tile; Mixtral and the EP64
+    share have 256-row tiles; decode's few rows per expert and the small fp32
+    layer (8 down tiles with 320 rows) take 32-row tiles."""
+    want = {"small_fp32": 32, "mixtral_bf16": 256, "dsv3_decode": 32, "dsv3_prefill": 320,
+            "ep64_share": 256}
+    for name, bm in want.items():
+        cfg = inputs.CONFIGS[name]
+        assert bench.forward_tile_rows(cfg, cfg.T * cfg.k) == bm, name
 
 
 def test_measured_traffic_is_per_workload_and_path():

@@ -298,6 +298,11 @@ PERMUTE_CASES = [
     (2049, 1, 1024, 8, "bf16", "random"),
     (300, 20, 40, 32, "f32", "random"),
     (1, 1, 1, 8, "f32", "one"),
+    # One chunk of assignments (M <= 2048): the single-launch permute up to
+    # E = 960, the three-launch one above it.
+    (1024, 2, 960, 16, "bf16", "random"),
+    (2048, 1, 1024, 8, "f32", "random"),
+    (128, 8, 256, 7168, "bf16", "random"),
 ]
 
 

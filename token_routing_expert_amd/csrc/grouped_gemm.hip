@@ -873,6 +873,10 @@ void launch_one(const void *a, int M, int K, int N, const int32_t *offsets, int 
 //   Large  (many rows per expert): ping-pong tiles of 256 rows, 128-byte
 //          slices, 2 row stages (1 ahead) and 3 weight stages (2 ahead).
 using G1Small = TileCfg<32, 128, 1, 4, 2, 4>;
+// fp32 rows are twice as long per K element: with two weight stages a
+// workgroup takes 73 KB of LDS instead of 139, so two fit per CU (small
+// problems then run their tiles in one round).
+using G1SmallF32 = TileCfg<32, 128, 1, 4, 2, 2>;
 using G2Small = TileCfg<32, 128, 1, 4, 2, 4>;
 using G1Medium = PpCfg<320, 256, 4, 5, 4, true, 2>;
 using G2Medium = PpCfg<320, 256, 4, 5, 4, true, 2>;
@@ -890,7 +894,21 @@ constexpr int kLongK = 8192;   // reduction length from which the down product u
 inline Family family_of(int M, int G, int d) {
   const int64_t per_expert = ((int64_t)M + G - 1) / G;
   if (per_expert < 96 || d % 256 != 0) return Family::Small;
-  return per_expert <= 288 ? Family::Medium : Family::Large;
+  return per_expert <= 320 ? Family::Medium : Family::Large;
+}
+
+// The forward products: family_of, except that a problem too small to give
+// the ping-pong tiles one tile per compute unit -- counted for the down
+// product, which has the fewest (d / 256 column tiles per row tile) -- runs
+// on the 32-row tiles, which spread it over several times as many
+// workgroups (the small fp32 layer: 8 down tiles become 128).
+inline Family forward_family(int M, int G, int d) {
+  const Family f = family_of(M, G, d);
+  if (f == Family::Small) return f;
+  const int64_t per_expert = ((int64_t)M + G - 1) / G;
+  const int bm = f == Family::Medium ? 320 : 256;
+  const int64_t tiles = (int64_t)G * ((per_expert + bm - 1) / bm) * (d / 256);
+  return tiles < device_cus() ? Family::Small : f;
 }
 
 // GEMM1: gate/up + SwiGLU, K = d, N = ffn.  With gu, the pre-activations
@@ -901,7 +919,8 @@ void launch_gate_up(Family f, const void *a, int M, int d, int ffn, const int32_
                     int gk = 1, int a_rows = 0, void *gu = nullptr, int grid_rows = -1) {
   if (gu) {
     if (f == Family::Small)
-      launch_one<BF16, true, G1Small, true>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows, gu);
+      launch_one<BF16, true, std::conditional_t<BF16, G1Small, G1SmallF32>, true>(
+          a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows, gu);
     else if (f == Family::Medium)
       launch_one<BF16, true, G1Medium, true>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows, gu);
     else
@@ -909,8 +928,8 @@ void launch_gate_up(Family f, const void *a, int M, int d, int ffn, const int32_
     return;
   }
   if (f == Family::Small)
-    launch_one<BF16, true, G1Small>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows,
-                                    nullptr, grid_rows);
+    launch_one<BF16, true, std::conditional_t<BF16, G1Small, G1SmallF32>>(
+        a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows, nullptr, grid_rows);
   else if (f == Family::Medium)
     launch_one<BF16, true, G1Medium>(a, M, d, ffn, offsets, G, w13, h, stream, gather, gk, a_rows,
                                      nullptr, grid_rows);
@@ -1023,7 +1042,7 @@ extern "C" moe_status moe_grouped_gate_up(const void *a, moe_dtype dt, int M, in
   if (st != MOE_OK || M == 0) return st;
   if (!a || !offsets || !w13 || !h) return MOE_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(w13) || !aligned16(h)) return MOE_ERR_INVALID_ARG;
-  const Family f = family_of(M, G, d);
+  const Family f = forward_family(M, G, d);
   if (dt == MOE_BF16)
     launch_gate_up<true>(f, a, M, d, ffn, offsets, G, w13, h, stream);
   else
@@ -1043,7 +1062,7 @@ extern "C" moe_status moe_grouped_gate_up_gather(const void *x, moe_dtype dt, in
   if ((int64_t)T * d * elem >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
   if (!x || !order || !offsets || !w13 || !h) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w13) || !aligned16(h)) return MOE_ERR_INVALID_ARG;
-  const Family f = family_of(M, G, d);
+  const Family f = forward_family(M, G, d);
   if (dt == MOE_BF16)
     launch_gate_up<true>(f, x, M, d, ffn, offsets, G, w13, h, stream, order, k, T);
   else
@@ -1062,7 +1081,7 @@ extern "C" moe_status moe_grouped_gate_up_save(const void *x, moe_dtype dt, int 
   if (order && (int64_t)T * d * elem >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
   if (!x || !offsets || !w13 || !h || !gu) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w13) || !aligned16(h) || !aligned16(gu)) return MOE_ERR_INVALID_ARG;
-  const Family f = family_of(M, G, d);
+  const Family f = forward_family(M, G, d);
   if (dt == MOE_BF16)
     launch_gate_up<true>(f, x, M, d, ffn, offsets, G, w13, h, stream, order, order ? k : 1, order ? T : M, gu);
   else
@@ -1077,7 +1096,7 @@ extern "C" moe_status moe_grouped_down(const void *h, moe_dtype dt, int M, int f
   if (st != MOE_OK || M == 0) return st;
   if (!h || !offsets || !w2 || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned16(h) || !aligned16(w2) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
-  const Family f = family_of(M, G, d);
+  const Family f = forward_family(M, G, d);
   if (dt == MOE_BF16)
     launch_down<true>(f, h, M, ffn, d, offsets, G, w2, y, stream);
   else
@@ -1093,7 +1112,7 @@ extern "C" moe_status moe_grouped_swiglu(const void *a, moe_dtype dt, int M, int
   if (!a || !offsets || !w13 || !w2 || !h || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(w13) || !aligned16(w2) || !aligned16(h) || !aligned16(y))
     return MOE_ERR_INVALID_ARG;
-  const Family f = family_of(M, G, d);
+  const Family f = forward_family(M, G, d);
   if (dt == MOE_BF16) {
     launch_gate_up<true>(f, a, M, d, ffn, offsets, G, w13, h, stream);
     launch_down<true>(f, h, M, ffn, d, offsets, G, w2, y, stream);

@@ -103,39 +103,37 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t *__restrict__ hist, int n
   }
 }
 
-// Stable ranks within a chunk.  The chunk is cut into 4 contiguous quarters,
-// one per wave.  Each wave walks its quarter 64 assignments at a time; lanes
-// with equal expert ids find each other with one ballot per id bit, and the
-// rank of a lane is the number of equal lanes below it.  Ranks therefore
-// follow assignment order, which makes the sort stable.
+// Stable ranks within a chunk, for a workgroup of NW waves.  The chunk
+// [c0, c0 + chunk) is cut into NW contiguous parts, one per wave.  Each wave
+// walks its part 64 assignments at a time; lanes with equal expert ids find
+// each other with one ballot per id bit, and the rank of a lane is the
+// number of equal lanes below it.  Ranks therefore follow assignment order,
+// which makes the sort stable.  base(e) is the first packed position of the
+// chunk's expert-e assignments; cnt is NW E ints of LDS.
 //
 // Capacity form (cap >= 0): an assignment's rank inside its expert is its
 // packed position minus seg_start[e]; rank r < cap goes to slot e cap + r,
 // a higher rank is dropped (inv = -1, no order entry).
-__global__ __launch_bounds__(kThreads) void k_multisplit(const int32_t *__restrict__ ids, int64_t M,
-                                                         int E, int nbits, int64_t chunk,
-                                                         const int32_t *__restrict__ base,
-                                                         int32_t *__restrict__ order,
-                                                         int32_t *__restrict__ inv,
-                                                         const int32_t *__restrict__ seg_start = nullptr,
-                                                         int cap = -1) {
-  extern __shared__ int cnt[];  // [4][E]
+template <int NW, typename Base>
+__device__ __forceinline__ void stable_ranks(const int32_t *__restrict__ ids, int64_t M, int E, int nbits,
+                                             int64_t c0, int64_t chunk, Base base, int *cnt,
+                                             int32_t *__restrict__ order, int32_t *__restrict__ inv,
+                                             const int32_t *__restrict__ seg_start, int cap) {
   const int wv = uniform(threadIdx.x >> 6), lane = lane_id();
-  for (int i = threadIdx.x; i < 4 * E; i += kThreads) cnt[i] = 0;
+  for (int i = threadIdx.x; i < NW * E; i += NW * kWave) cnt[i] = 0;
   __syncthreads();
-  const int64_t quarter = chunk / 4;
-  const int64_t c0 = blockIdx.x * chunk;
-  const int64_t q0 = min(c0 + wv * quarter, M), q1 = min(q0 + quarter, M);
+  const int64_t part = (chunk + NW - 1) / NW;
+  const int64_t q0 = min(c0 + wv * part, min(c0 + chunk, M)), q1 = min(q0 + part, min(c0 + chunk, M));
   int *mine = cnt + wv * E;
   for (int64_t a = q0 + lane; a < q1; a += kWave) {
     const int e = ids[a];
     if (e >= 0 && e < E) atomicAdd(&mine[e], 1);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    int run = base[(int64_t)blockIdx.x * E + e];
+  for (int e = threadIdx.x; e < E; e += NW * kWave) {
+    int run = base(e);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const int v = cnt[w * E + e];
       cnt[w * E + e] = run;
       run += v;
@@ -172,6 +170,74 @@ __global__ __launch_bounds__(kThreads) void k_multisplit(const int32_t *__restri
     if (valid && (peers & below) == 0) mine[e] += __popcll(peers);
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// Chunk blockIdx.x of the multi-chunk permute (4 waves); its bases are the
+// scanned histogram row.
+__global__ __launch_bounds__(kThreads) void k_multisplit(const int32_t *__restrict__ ids, int64_t M,
+                                                         int E, int nbits, int64_t chunk,
+                                                         const int32_t *__restrict__ base,
+                                                         int32_t *__restrict__ order,
+                                                         int32_t *__restrict__ inv,
+                                                         const int32_t *__restrict__ seg_start = nullptr,
+                                                         int cap = -1) {
+  extern __shared__ int cnt[];  // [4][E]
+  const int32_t *row = base + (int64_t)blockIdx.x * E;
+  stable_ranks<kThreads / kWave>(ids, M, E, nbits, (int64_t)blockIdx.x * chunk, chunk,
+                                 [row](int e) { return row[e]; }, cnt, order, inv, seg_start, cap);
+}
+
+// All assignments in one chunk (M <= 2048): the histogram, the scan and the
+// stable ranks in one workgroup of 16 waves -- one launch instead of three.
+// Writes counts and offsets (dropless) or counts and seg_start (capacity).
+constexpr int kOneThreads = 1024;
+constexpr int kOneMaxE = 960;   // 17 E ints of LDS stay within 64 KB
+__global__ __launch_bounds__(kOneThreads) void k_permute_one(const int32_t *__restrict__ ids, int64_t M,
+                                                            int E, int nbits, int32_t *__restrict__ counts,
+                                                            int32_t *__restrict__ offsets,
+                                                            int32_t *__restrict__ order,
+                                                            int32_t *__restrict__ inv, int cap) {
+  extern __shared__ int lds[];  // base [E], then cnt [16][E]
+  __shared__ int wave_tot[16];
+  int *base = lds, *cnt = lds + E;
+  const int e = threadIdx.x, lane = lane_id(), wv = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < E; i += kOneThreads) base[i] = 0;
+  __syncthreads();
+  for (int64_t a = threadIdx.x; a < M; a += kOneThreads) {
+    const int x = ids[a];
+    if (x >= 0 && x < E) atomicAdd(&base[x], 1);
+  }
+  __syncthreads();
+  // Exclusive scan of the counts over the experts (E <= 1024, thread e owns e).
+  const int total = e < E ? base[e] : 0;
+  int incl = total;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) wave_tot[wv] = incl;
+  __syncthreads();
+  if (wv == 0) {
+    int t = lane < 16 ? wave_tot[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int o = __shfl_up(t, off);
+      if (lane >= off) t += o;
+    }
+    if (lane < 16) wave_tot[lane] = t;
+  }
+  __syncthreads();
+  const int excl = incl - total + (wv > 0 ? wave_tot[wv - 1] : 0);
+  if (e < E) {
+    counts[e] = total;
+    offsets[e] = excl;
+    if (e == E - 1) offsets[E] = excl + total;
+    base[e] = excl;
+  }
+  __syncthreads();
+  stable_ranks<kOneThreads / kWave>(ids, M, E, nbits, 0, M, [base](int x) { return base[x]; }, cnt, order,
+                                    inv, base, cap);
 }
 
 // Capacity form: the slots no assignment reached (rank past the expert's
@@ -312,13 +378,18 @@ extern "C" moe_status moe_permute(const void *x, moe_dtype dt, int T, int d,
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
 
-  if (nchunks > 0)
-    k_hist<<<dim3(nchunks), dim3(kThreads), sizeof(int) * E, stream>>>(topk_ids, M, E, chunk, hist);
-  // The scan also runs for M == 0 so that counts and offsets are written.
-  k_scan<<<dim3(1), dim3(1024), 0, stream>>>(hist, nchunks, E, counts, offsets);
-  if (M == 0) return launch_status();
-  k_multisplit<<<dim3(nchunks), dim3(kThreads), sizeof(int) * 4 * E, stream>>>(
-      topk_ids, M, E, nbits, chunk, hist, order, inv);
+  if (nchunks == 1 && E <= kOneMaxE) {
+    k_permute_one<<<dim3(1), dim3(kOneThreads), sizeof(int) * 17 * E, stream>>>(
+        topk_ids, M, E, nbits, counts, offsets, order, inv, -1);
+  } else {
+    if (nchunks > 0)
+      k_hist<<<dim3(nchunks), dim3(kThreads), sizeof(int) * E, stream>>>(topk_ids, M, E, chunk, hist);
+    // The scan also runs for M == 0 so that counts and offsets are written.
+    k_scan<<<dim3(1), dim3(1024), 0, stream>>>(hist, nchunks, E, counts, offsets);
+    if (M == 0) return launch_status();
+    k_multisplit<<<dim3(nchunks), dim3(kThreads), sizeof(int) * 4 * E, stream>>>(
+        topk_ids, M, E, nbits, chunk, hist, order, inv);
+  }
   if (!rows) return launch_status();
   const int elem = dt == MOE_F32 ? 4 : 2;
   const int nvec = (int)((int64_t)d * elem / 16);
@@ -414,12 +485,17 @@ extern "C" moe_status moe_permute_capacity(const void *x, moe_dtype dt, int T, i
                                                    moe_permute_workspace_bytes(T, k, E));
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  if (nchunks > 0)
-    k_hist<<<dim3(nchunks), dim3(kThreads), sizeof(int) * E, stream>>>(topk_ids, M, E, chunk, hist);
-  k_scan<<<dim3(1), dim3(1024), 0, stream>>>(hist, nchunks, E, counts, seg_start);
-  if (M > 0)
-    k_multisplit<<<dim3(nchunks), dim3(kThreads), sizeof(int) * 4 * E, stream>>>(
-        topk_ids, M, E, nbits, chunk, hist, order, inv, seg_start, cap);
+  if (nchunks == 1 && E <= kOneMaxE) {
+    k_permute_one<<<dim3(1), dim3(kOneThreads), sizeof(int) * 17 * E, stream>>>(
+        topk_ids, M, E, nbits, counts, seg_start, order, inv, cap);
+  } else {
+    if (nchunks > 0)
+      k_hist<<<dim3(nchunks), dim3(kThreads), sizeof(int) * E, stream>>>(topk_ids, M, E, chunk, hist);
+    k_scan<<<dim3(1), dim3(1024), 0, stream>>>(hist, nchunks, E, counts, seg_start);
+    if (M > 0)
+      k_multisplit<<<dim3(nchunks), dim3(kThreads), sizeof(int) * 4 * E, stream>>>(
+          topk_ids, M, E, nbits, chunk, hist, order, inv, seg_start, cap);
+  }
   const int64_t fill = (slots > E + 1 ? slots : E + 1);
   k_capacity_fill<<<dim3((unsigned)((fill + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream>>>(
       counts, E, cap, order, offsets);
