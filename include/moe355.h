@@ -426,6 +426,17 @@ moe_status moe_expert_loop_swiglu(const void *a, moe_dtype dt, int M, int d, int
  * forward's, 12 d ffn FLOPs per assignment (section "A worked example at
  * DeepSeek-V3's shape").  All values are the chain rule applied to the
  * forward's definitions.
+ *
+ * Precision (bf16).  The backward reads what the forward kept in bf16: the
+ * pre-activations gu, h, and the dispatched gradient dy_perm (rounded once
+ * each, to nearest even), and accumulates in fp32.  The SwiGLU backward's
+ * dgate = dh u SiLU'(g) then carries an error that scales with |dh u|, not
+ * with dgate itself, and a weight-gradient row sums only the rows of its
+ * expert: for an expert with one or two rows, a single row of dW13 can be
+ * off by as much as its own magnitude.  Over a whole matrix the error stays
+ * within about 1e-2 of the matrix's largest magnitude (the GPU tests' bar is
+ * 2e-2 per matrix).  fp32 layers keep fp32 pre-activations and agree with
+ * the exact gradients to about 1e-6 per row.
  * ====================================================================== */
 
 /*

@@ -301,13 +301,6 @@ def layer_tokens(x, ids, w, w13, w2, tokens, sh_w13=None, sh_w2=None):
     return combine(y_rows, inv, w[tokens], y_sh)
 
 
-# --------------------------------------------------------------------------
-# Backward pass (oracle.c, functions B0..B5): the chain rule applied to the
-# forward definition; "Expert parallelism", section "How many bytes move",
-# gives its shape (the combine's gradient is dispatched, the dispatch's
-# gradient combined).
-# --------------------------------------------------------------------------
-
 def layer_tokens_capacity(x, ids, w, slot_of, w13, w2, tokens, sh_w13=None, sh_w2=None):
     """The padded batched form's output for selected tokens: the plain
     definition with every dropped assignment (slot_of = -1) left out,
@@ -326,6 +319,13 @@ def layer_tokens_capacity(x, ids, w, slot_of, w13, w2, tokens, sh_w13=None, sh_w
     inv[kept] = np.arange(int(kept.sum()), dtype=np.int32)
     return combine(y_rows, inv, w[tokens], y_sh)
 
+
+# --------------------------------------------------------------------------
+# Backward pass (oracle.c, functions B0..B5): the chain rule applied to the
+# forward definition; "Expert parallelism", section "How many bytes move",
+# gives its shape (the combine's gradient is dispatched, the dispatch's
+# gradient combined).
+# --------------------------------------------------------------------------
 
 def combine_backward(dy: np.ndarray, inv: np.ndarray, w: np.ndarray, y_perm: np.ndarray):
     """B5: dy_perm [T k, d] (row inv[t k + j] = w[t,j] dy[t]) and dw [T,k]
@@ -375,6 +375,30 @@ def expert_swiglu_backward_rows(xrows: np.ndarray, expert_of_row: np.ndarray, w1
         opt(dgu), opt(dw13), opt(dw2))
     if want_act:
         return dx, dw13, dw2, gu, dgu
+    return dx, dw13, dw2
+
+
+def expert_backward_dense(xrows, w13e, w2e, dyrows):
+    """One expert's backward by the chain rule, with fp64 matrix products as
+    its steps (for whole weight-gradient matrices at full size, where the
+    plain loops of orc_expert_swiglu_backward_rows would take hours):
+        g = X Wg^T, u = X Wu^T, h = SiLU(g) u           (forward, kept)
+        dh = dY Wd,  dWd = dY^T h
+        dg = dh u SiLU'(g), du = dh SiLU(g),  SiLU'(g) = s (1 + g (1 - s)), s = 1 / (1 + e^-g)
+        dW13 = (dg^T X, du^T X),  dX = dg Wg + du Wu.
+    xrows [R, d], w13e [2, ffn, d], w2e [d, ffn], dyrows [R, d] (bf16 bits or
+    floats).  Returns (dx [R, d], dw13 [2, ffn, d], dw2 [d, ffn]) in fp64."""
+    X, W13, W2, dY = _f64(xrows), _f64(w13e), _f64(w2e), _f64(dyrows)
+    g, u = X @ W13[0].T, X @ W13[1].T
+    s = 1.0 / (1.0 + np.exp(-g))
+    silu = g * s
+    h = silu * u
+    dh = dY @ W2
+    dw2 = dY.T @ h
+    dg = dh * u * (s * (1.0 + g * (1.0 - s)))
+    du = dh * silu
+    dw13 = np.stack([dg.T @ X, du.T @ X])
+    dx = dg @ W13[0] + du @ W13[1]
     return dx, dw13, dw2
 
 
