@@ -99,6 +99,32 @@ def forward_tile_rows(cfg, M, cus=256):
     return 32 if tiles < cus else bm
 
 
+def combine_rate(layer, cfg, nbytes, reps=10):
+    """Mean duration of the combine launch alone (HIP events around each call
+    on the launch stream, after the step's buffers exist) and its algorithmic
+    HBM rate.  The in-step stage time also holds the gap between launches."""
+    import torch
+    from token_routing_expert_amd import moe_unpermute_combine
+    y = torch.empty_like(layer.y)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        moe_unpermute_combine(layer.y_perm, layer.inv, layer.topk_w, layer.y_sh, y,
+                              rows=layer.rows if layer.cap is not None else None)
+
+    for _ in range(3):
+        run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+    for i in range(reps):
+        ev[2 * i].record(stream)
+        run()
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)) / reps
+    return {"ms": round(ms, 4), "bytes": nbytes, "GBps": round(nbytes / ms / 1e6, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / PEAK_HBM, 4)}
+
+
 def load_accounting(cfg, counts, send_counts):
     """Load and padding statistics of the batch: rows per expert, the rows the
     GEMM tiles compute beyond the real ones (tile padding), and the imbalance
@@ -190,6 +216,124 @@ GEMM_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "token_ro
                            "csrc", "grouped_gemm.hip")
 
 
+GATE_UP_KERNEL_PREFIX = "k_grouped_gemm_pp<true, 320, 256, 4, 5, 4, 2, true, true, false, 0>"
+
+
+def _source_sha():
+    import hashlib
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _rocprof_rows(directory, suffix):
+    """Rows (dicts) of every rocprofv3 CSV file under directory whose name
+    ends with suffix."""
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def summarize_profile(workload, trace_dir, fetch_dir, write_dir, bench_line, warmup, commands, out_dir):
+    """Summarise rocprofv3 runs of bench.py for one workload into
+    out_dir/<workload>_kernels.md and out_dir/<workload>_gate_up_traffic.json.
+
+    Durations per kernel come from the kernel trace (end - start of each
+    dispatch), both over all dispatches and over the timed ones (each
+    kernel's first `warmup` dispatches dropped); HBM bytes from one-counter
+    passes FETCH_SIZE and WRITE_SIZE, scaled by what the counters read for
+    the plain 1 GiB device copy of the same runs (--copy-calibration)."""
+    from collections import defaultdict
+    trace = _rocprof_rows(trace_dir, "kernel_trace.csv")
+    if not trace:
+        raise SystemExit(f"no kernel trace under {trace_dir}")
+    durs = defaultdict(list)
+    for r in sorted(trace, key=lambda r: int(r["Start_Timestamp"])):
+        key = (r["Kernel_Name"], int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0))
+        durs[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def counters(directory, counter):
+        vals = defaultdict(list)
+        for r in _rocprof_rows(directory, "counter_collection.csv") if directory else []:
+            if r.get("Counter_Name") != counter:
+                continue
+            vals[(r["Kernel_Name"], int(r.get("Grid_Size") or 0))].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in vals.items()}
+
+    fetch, write = counters(fetch_dir, "FETCH_SIZE"), counters(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if k[0].startswith("__amd_rocclr_copyBuffer") and fetch[k] > 1e5]
+    fs = ws = None
+    if copy and write.get(copy[0]):
+        fs, ws = 1024 * 1024 / fetch[copy[0]], 1024 * 1024 / write[copy[0]]   # 1 GiB in KiB
+    lines = [f"# rocprofv3 summary: {workload}", "",
+             "Commands (the profiled bench runs, then this summary):", "", "```", *commands, "```", ""]
+    if fs:
+        lines += [f"Calibration: the plain 1 GiB device copy reads FETCH_SIZE = {1024 * 1024 / fs:.0f} KiB "
+                  f"and WRITE_SIZE = {1024 * 1024 / ws:.0f} KiB, so HBM bytes = FETCH_SIZE x {fs:.3f} KiB "
+                  f"+ WRITE_SIZE x {ws:.3f} KiB.", ""]
+    lines += [f"Durations from the kernel trace; 'timed' drops each kernel's first {warmup} dispatches "
+              "(the bench's warm-up steps), so it covers the launches the bench line times.", "",
+              "| kernel | grid (threads) | dispatches | avg us (all) | avg us (timed) | FETCH KiB | WRITE KiB "
+              "| HBM GB (scaled) | GB/s (timed) |", "|---|---|---|---|---|---|---|---|---|"]
+    gate_up = None
+    for key in sorted(durs, key=lambda k: -sum(durs[k])):
+        d = durs[key]
+        timed = d[warmup:] if len(d) > warmup else d
+        avg_all, avg_t = sum(d) / len(d), sum(timed) / len(timed)
+        fk, wk = fetch.get(key), write.get(key)
+        gb = ((fk or 0) * fs + (wk or 0) * ws) * 1024 / 1e9 if fs and (fk or wk) else None
+        lines.append(f"| {key[0][:90]} | {key[1]} | {len(d)} | {avg_all:.1f} | {avg_t:.1f} | "
+                     f"{'' if fk is None else f'{fk:.0f}'} | {'' if wk is None else f'{wk:.0f}'} | "
+                     f"{'' if gb is None else f'{gb:.3f}'} | {'' if gb is None else f'{gb / avg_t * 1e6 / 1e9:.0f}'} |")
+        if key[0].startswith(GATE_UP_KERNEL_PREFIX) and gate_up is None:
+            gate_up = (key, avg_t, len(timed), gb)
+    lines.append("")
+    rec = None
+    if gate_up:
+        key, avg_t, n, gb = gate_up
+        lines += [f"Routed gate/up launch (`{key[0][:90]}`): {avg_t:.1f} us mean over its {n} timed "
+                  f"dispatches" + (f"; {gb:.3f} GB of HBM traffic per launch." if gb else "."), ""]
+        rec = {"workload": workload, "kernel": key[0], "grid_threads": key[1],
+               "avg_us_timed": round(avg_t, 1), "timed_dispatches": n,
+               "fetch_kib": fetch.get(key), "write_kib": write.get(key), "fetch_scale": fs,
+               "write_scale": ws, "bytes_per_launch": int(gb * 1e9) if gb else None,
+               "source": os.path.relpath(GEMM_SOURCE, os.path.dirname(PROFILES)),
+               "source_sha256": _source_sha()}
+    if bench_line and os.path.exists(bench_line):
+        with open(bench_line) as f:
+            found = [l for l in f if l.startswith("{")]
+        if found:
+            r = json.loads(found[-1])
+            lines += ["bench.py line of the traced run (stage times from HIP events on the launch stream):",
+                      "", "```", json.dumps(r.get("stages")), json.dumps(r.get("roofline")), "```", ""]
+            if rec:
+                rec["bench_launch_ms_events"] = r["roofline"].get("launch_ms")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"{workload}_kernels.md"), "w") as f:
+        f.write("\n".join(lines))
+    if rec:
+        with open(os.path.join(out_dir, f"{workload}_gate_up_traffic.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+    print("\n".join(lines))
+
+
+def measured_trace(workload):
+    """The routed gate/up launch's mean duration (us) over the timed
+    dispatches of the committed kernel trace of this workload, or None when
+    there is none or it was taken on another kernel source."""
+    try:
+        with open(os.path.join(PROFILES, f"{workload}_gate_up_traffic.json")) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    if t.get("workload") != workload or t.get("source_sha256") != _source_sha():
+        return None
+    return t.get("avg_us_timed")
+
+
 def measured_traffic(workload, path="gather"):
     """HBM bytes per gate/up launch from the committed rocprofv3 counter passes
     of this workload (taken on the default fused-gather path), or None when
@@ -205,7 +349,7 @@ def measured_traffic(workload, path="gather"):
             sha = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
-    if t.get("workload") != workload or t.get("source_sha256") != sha:
+    if t.get("workload") != workload or t.get("source_sha256") != sha or not t.get("bytes_per_launch"):
         return None
     return int(t["bytes_per_launch"])
 
@@ -513,9 +657,23 @@ def main():
                     help="after the timed steps, time this many more from cold caches")
     ap.add_argument("--no-alternatives", action="store_true",
                     help="skip timing the capacity-padded (CF 1, 1.25) and per-expert-loop forms")
+    ap.add_argument("--summarize-profile", metavar="WORKLOAD",
+                    help="write profiles/WORKLOAD_kernels.md and WORKLOAD_gate_up_traffic.json from "
+                         "rocprofv3 output (--trace-dir, --fetch-dir, --write-dir, --bench-line); "
+                         "runs no GPU work")
+    ap.add_argument("--trace-dir")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--bench-line")
+    ap.add_argument("--command", action="append", default=[],
+                    help="a command line that produced the profile (repeatable; recorded verbatim)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.trace_dir, args.fetch_dir, args.write_dir,
+                          args.bench_line, args.warmup, args.command, PROFILES)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the path is one GPU's share of the EP layer and "
@@ -705,6 +863,8 @@ def main():
             "mfma_frac": round(flop_rate / peak, 4),
             "hbm_frac": round(byte_rate / PEAK_HBM, 4),
             "launch_ms": round(gu_ms, 4),
+            "trace_launch_ms": (lambda us: None if us is None else round(us / 1e3, 4))(
+                measured_trace(cfg.name) if gather else None),
         },
         "stages": stage_info,
         "step_ms_events": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
@@ -717,11 +877,18 @@ def main():
                                 to_host(layer.send_counts) if cfg.n_ep else None),
         "device": torch.cuda.get_device_name(0),
     }
+    tl = result["roofline"]["trace_launch_ms"]
+    if tl:
+        # The same fraction from the committed kernel trace's mean duration of
+        # the timed launches (a profile taken on the same kernel source).
+        result["roofline"]["trace_frac"] = round(
+            (b_gate_up if hbm_bound else f_gate_up) / (tl * 1e-3) / (PEAK_HBM if hbm_bound else peak), 4)
     if gather:
         # The timed path never copies rows; the row-copying permute (the
         # stable scatter into the packed buffer X[order]) is measured here
         # on the same batch, outside the timed step, for its HBM figure.
         result["permute_packed"] = packed_permute_rate(layer, cfg, stage_bytes(cfg)[0])
+    result["combine_alone"] = combine_rate(layer, cfg, b_comb)
     if not args.no_alternatives and not router:
         log("alternatives: capacity CF 1 and 1.25, one product pair per expert")
         result["alternatives"] = alternatives(cfg, layer, stages, stream, step_ev[K // 2],
