@@ -216,7 +216,12 @@ GEMM_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "token_ro
                            "csrc", "grouped_gemm.hip")
 
 
-GATE_UP_KERNEL_PREFIX = "k_grouped_gemm_pp<true, 320, 256, 4, 5, 4, 2, true, true, false, 0>"
+# The routed gate/up launch at the DeepSeek-V3 prefill shape (320-row tiles,
+# SwiGLU epilogue); other workloads' gate/up launches are found by family.
+GATE_UP_KERNELS = ("k_grouped_gemm_pp<true, 320, 256, 4, 5, 4, 2, true, true, false, 0>",
+                   "k_grouped_gemm_pp<true, 256, 256, 2, 3, 8, 1, true, true, false, 0>",
+                   "k_grouped_gemm<true, 32, 128, 1, 4, true, 2, 4, false>",
+                   "k_grouped_gemm<false, 32, 128, 1, 4, true, 2, 2, false>")
 
 
 def _source_sha():
@@ -252,7 +257,10 @@ def summarize_profile(workload, trace_dir, fetch_dir, write_dir, bench_line, war
         raise SystemExit(f"no kernel trace under {trace_dir}")
     durs = defaultdict(list)
     for r in sorted(trace, key=lambda r: int(r["Start_Timestamp"])):
-        key = (r["Kernel_Name"], int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0))
+        gx = r.get("Grid_Size_X")
+        gsize = (int(gx) * int(r.get("Grid_Size_Y") or 1) * int(r.get("Grid_Size_Z") or 1)) if gx \
+            else int(r.get("Grid_Size") or 0)
+        key = (r["Kernel_Name"], gsize)
         durs[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
 
     def counters(directory, counter):
@@ -285,16 +293,18 @@ def summarize_profile(workload, trace_dir, fetch_dir, write_dir, bench_line, war
         avg_all, avg_t = sum(d) / len(d), sum(timed) / len(timed)
         fk, wk = fetch.get(key), write.get(key)
         gb = ((fk or 0) * fs + (wk or 0) * ws) * 1024 / 1e9 if fs and (fk or wk) else None
-        lines.append(f"| {key[0][:90]} | {key[1]} | {len(d)} | {avg_all:.1f} | {avg_t:.1f} | "
+        name = key[0].replace("void ", "").replace("moe::(anonymous namespace)::", "").split("(")[0]
+        lines.append(f"| {name} | {key[1]} | {len(d)} | {avg_all:.1f} | {avg_t:.1f} | "
                      f"{'' if fk is None else f'{fk:.0f}'} | {'' if wk is None else f'{wk:.0f}'} | "
-                     f"{'' if gb is None else f'{gb:.3f}'} | {'' if gb is None else f'{gb / avg_t * 1e6 / 1e9:.0f}'} |")
-        if key[0].startswith(GATE_UP_KERNEL_PREFIX) and gate_up is None:
-            gate_up = (key, avg_t, len(timed), gb)
+                     f"{'' if gb is None else f'{gb:.3f}'} | {'' if gb is None else f'{gb / avg_t * 1e6:.0f}'} |")
+        if any(k in key[0] for k in GATE_UP_KERNELS) and (gate_up is None or avg_t * len(d) > gate_up[4]):
+            gate_up = (key, avg_t, len(timed), gb, avg_t * len(d))
     lines.append("")
     rec = None
     if gate_up:
-        key, avg_t, n, gb = gate_up
-        lines += [f"Routed gate/up launch (`{key[0][:90]}`): {avg_t:.1f} us mean over its {n} timed "
+        key, avg_t, n, gb, _ = gate_up
+        short = key[0].replace("void ", "").replace("moe::(anonymous namespace)::", "").split("(")[0]
+        lines += [f"Routed gate/up launch (`{short}`): {avg_t:.1f} us mean over its {n} timed "
                   f"dispatches" + (f"; {gb:.3f} GB of HBM traffic per launch." if gb else "."), ""]
         rec = {"workload": workload, "kernel": key[0], "grid_threads": key[1],
                "avg_us_timed": round(avg_t, 1), "timed_dispatches": n,
