@@ -249,7 +249,7 @@ extern "C" moe_status moe_router_backward(const float *dlogits, const void *x, m
   if (dx && !launch_dgrad_pp(4, dl, T, E, d, offsets, 1, w_router, dx, nullptr, stream))
     return MOE_ERR_UNSUPPORTED;
   // dw_router = dlogits^T x: one segment of T rows, [E, d].
-  if (dw_router && !launch_wgrad_pp(dl, x, T, E, d, offsets, 1, dw_router, stream))
+  if (dw_router && !launch_weight_grad(dl, x, T, E, d, offsets, 1, dw_router, stream))
     return MOE_ERR_UNSUPPORTED;
   return launch_status();
 }

@@ -263,4 +263,9 @@ bool launch_dgrad_pp(int var, const void *a, int M, int K, int N, const int32_t 
 // multiple of 256.
 bool launch_wgrad_pp(const void *a, const void *b, int M, int m_dim, int n_dim,
                      const int32_t *offsets, int G, void *out, hipStream_t stream);
+// The same weight gradients on tiles whose stores overlap the next tile's
+// loads and MFMAs (grouped_wgrad.hip); false (nothing launched) under the
+// same condition.
+bool launch_weight_grad(const void *a, const void *b, int M, int m_dim, int n_dim,
+                        const int32_t *offsets, int G, void *out, hipStream_t stream);
 }  // namespace moe
