@@ -65,21 +65,35 @@ struct WgTile {
   int kt;          // K slices
 };
 
-// Tiles are (expert, n tile, m tile) with m fastest (MF) or (expert, m tile,
-// n tile) with n fastest.
-template <bool MF>
-__device__ __forceinline__ WgTile wg_tile(int L, int mt, int nt, const int32_t *__restrict__ offsets,
-                                          int M) {
+// Tile order within an expert: BM = 0 walks m tiles, n fastest; BM > 0 walks
+// bands of BM m tiles, n tile by n tile, m fastest inside the band (a band
+// of all m tiles is m fastest).
+template <int BM>
+__device__ __forceinline__ WgTile wg_tile_of(int L, int mt, int nt, int lo_raw, int hi_raw, int M) {
   WgTile t;
   t.e = L / (mt * nt);
   const int rem = L - t.e * (mt * nt);
-  t.m0 = (MF ? rem % mt : rem / nt) * kWgTile;
-  t.n0 = (MF ? rem / mt : rem % nt) * kWgTile;
-  t.lo = clamp_row(offsets[t.e], M);
-  const int hi = clamp_row(offsets[t.e + 1], M);
+  if constexpr (BM == 0) {
+    t.m0 = (rem / nt) * kWgTile;
+    t.n0 = (rem % nt) * kWgTile;
+  } else {
+    const int bm = BM < mt ? BM : mt;            // m tiles per full band
+    const int band = rem / (bm * nt), r2 = rem - band * (bm * nt);
+    const int bmc = mt - band * bm < bm ? mt - band * bm : bm;   // m tiles of this band
+    t.m0 = (band * bm + r2 % bmc) * kWgTile;
+    t.n0 = (r2 / bmc) * kWgTile;
+  }
+  t.lo = clamp_row(lo_raw, M);
+  const int hi = clamp_row(hi_raw, M);
   t.hi = hi > t.lo ? hi : t.lo;
   t.kt = (t.hi - t.lo + kWgSlice - 1) / kWgSlice;
   return t;
+}
+template <int BM>
+__device__ __forceinline__ WgTile wg_tile(int L, int mt, int nt, const int32_t *__restrict__ offsets,
+                                          int M) {
+  const int e = L / (mt * nt);
+  return wg_tile_of<BM>(L, mt, nt, offsets[e], offsets[e + 1], M);
 }
 
 // s_waitcnt vmcnt(a kWgLoads + b) for a in [0, A) and b in {0, kWgStores}:
@@ -110,8 +124,8 @@ __device__ __forceinline__ void wait_vmcnt_of(int a, int b) {
 // SA / SB: stages of the A and B rings; DA / DB: slices of A / B in flight
 // ahead of the one being read.  A ring keeps one stage beyond those free at
 // every tile end for the epilogue's staging.  NT: nontemporal output stores;
-// MF: tile order.
-template <int GRP, int SA, int SB, int DA, int DB, bool NT, bool MF>
+// BM: tile order (wg_tile).
+template <int GRP, int SA, int SB, int DA, int DB, bool NT, int BM>
 __device__ __forceinline__ void wg_run(const u32x4 *__restrict__ A, const u32x4 *__restrict__ B, int M,
                                        int Mdim, int N, const int32_t *__restrict__ offsets,
                                        uint16_t *__restrict__ C, u32x4 *smem, int L0, int band_end,
@@ -148,20 +162,25 @@ __device__ __forceinline__ void wg_run(const u32x4 *__restrict__ A, const u32x4 
       off[r] = ((uint32_t)krow * (uint32_t)ld + (uint32_t)(c0 + col)) * 2u;
     }
   };
-  // Skip to the next tile with slices (tiles of empty experts have none).
+  // Move the cursor past a finished tile, and past tiles of empty experts,
+  // which have no slices.  In the loop this runs right after a compute
+  // phase's MFMAs are issued: every LDS read of the phase has landed, so the
+  // wait for the segment bounds' scalar loads waits for nothing else, and it
+  // overlaps the MFMAs still executing.
   auto advance = [&]() {
-    while (kti == KTi) {
+    while (!idone && kti == KTi) {
       Li += Lstep;
       if (Li >= band_end) {
         idone = true;
-        return;
+        break;
       }
-      const WgTile t = wg_tile<MF>(Li, mt, nt, offsets, M);
+      const WgTile t = wg_tile<BM>(Li, mt, nt, offsets, M);
       setup(t);
       kti = 0;
       KTi = t.kt;
     }
   };
+  // Issue the cursor's slice; advance() has run since the previous issue.
   auto issue_next = [&]() {
     if (idone) return;
     u32x4 *stage = ring + (ji % S) * kWgStage;
@@ -177,7 +196,6 @@ __device__ __forceinline__ void wg_run(const u32x4 *__restrict__ A, const u32x4 
       buffer_load_lds16(ub, ubytes, stage + (wq + 4 * r) * 64, off[r] + (uint32_t)kti * kstep, 0);
     ++ji;
     ++kti;
-    advance();
   };
   // Wait until stream slice j (already issued) has landed.  In flight after
   // it may stay: the slices issued after it and, if the last epilogue's
@@ -193,13 +211,16 @@ __device__ __forceinline__ void wg_run(const u32x4 *__restrict__ A, const u32x4 
   // blocks 2 wq, 2 wq + 1 of the tile.
 
   {
-    const WgTile t0 = wg_tile<MF>(L0, mt, nt, offsets, M);
+    const WgTile t0 = wg_tile<BM>(L0, mt, nt, offsets, M);
     setup(t0);
     KTi = t0.kt;
     advance();
   }
 #pragma unroll
-  for (int s = 0; s < AHEAD; ++s) issue_next();
+  for (int s = 0; s < AHEAD; ++s) {
+    issue_next();
+    advance();
+  }
   asm volatile("" ::: "memory");
   if (ji > 0) wait_for(0);
   asm volatile("" ::: "memory");
@@ -208,7 +229,7 @@ __device__ __forceinline__ void wg_run(const u32x4 *__restrict__ A, const u32x4 
 
   int jc = 0;   // stream position of the next slice read
   for (int L = L0;;) {
-    const WgTile t = wg_tile<MF>(L, mt, nt, offsets, M);
+    const WgTile t = wg_tile<BM>(L, mt, nt, offsets, M);
     if (GRP == 1) phase_barrier();   // group 1 runs one phase behind group 0
     asm volatile("" ::: "memory");
     f32x16 acc[kWgRowBlocks][kWgColBlocks];
@@ -250,6 +271,8 @@ __device__ __forceinline__ void wg_run(const u32x4 *__restrict__ A, const u32x4 
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fb[q][j]),
                                                                 __builtin_bit_cast(bf16x8, fa[q][i]),
                                                                 acc[i][j], 0, 0, 0);
+      asm volatile("" ::: "memory");
+      advance();
       asm volatile("" ::: "memory");
       if (GRP == 0 && jc + 1 < ji) wait_for(jc + 1);
       asm volatile("" ::: "memory");
@@ -315,7 +338,7 @@ __device__ __forceinline__ void wg_run(const u32x4 *__restrict__ A, const u32x4 
   }
 }
 
-template <int SA, int SB, int DA, int DB, bool NT, bool MF>
+template <int SA, int SB, int DA, int DB, bool NT, int BM>
 __global__ __launch_bounds__(512) void k_weight_grad(const u32x4 *__restrict__ A, const u32x4 *__restrict__ B,
                                                      int M, int Mdim, int N,
                                                      const int32_t *__restrict__ offsets, int G,
@@ -350,9 +373,9 @@ __global__ __launch_bounds__(512) void k_weight_grad(const u32x4 *__restrict__ A
   const int Lstep = rr ? (int)gridDim.x : nj;
   if (L0 >= band_end) return;
   if (wave < 4)
-    wg_run<0, SA, SB, DA, DB, NT, MF>(A, B, M, Mdim, N, offsets, C, smem, L0, band_end, Lstep, wave, lane);
+    wg_run<0, SA, SB, DA, DB, NT, BM>(A, B, M, Mdim, N, offsets, C, smem, L0, band_end, Lstep, wave, lane);
   else
-    wg_run<1, SA, SB, DA, DB, NT, MF>(A, B, M, Mdim, N, offsets, C, smem, L0, band_end, Lstep, wave - 4, lane);
+    wg_run<1, SA, SB, DA, DB, NT, BM>(A, B, M, Mdim, N, offsets, C, smem, L0, band_end, Lstep, wave - 4, lane);
 }
 
 }  // namespace
@@ -367,7 +390,7 @@ bool launch_weight_grad(const void *a, const void *b, int M, int m_dim, int n_di
   const int64_t widest = m_dim > n_dim ? m_dim : n_dim;
   if ((int64_t)(M + kWgSlice) * widest * 2 >= ((int64_t)1 << 32)) return false;
   const int64_t tiles = (int64_t)G * (m_dim / kWgTile) * (n_dim / kWgTile);
-  auto kern = k_weight_grad<5, 5, 3, 3, true, false>;
+  auto kern = k_weight_grad<5, 5, 3, 3, true, 4>;
   static DeviceCache occ;
   const int grid = persistent_grid((const void *)kern, 512, occ, tiles);
   kern<<<dim3(grid), dim3(512), 0, stream>>>(static_cast<const u32x4 *>(a), static_cast<const u32x4 *>(b),
