@@ -344,10 +344,9 @@ __device__ __forceinline__ int swz_c(int r, int cc) {
 // [K, N] per expert (N-contiguous) and are staged as column-contiguous tiles
 // read back transposed -- 1 stores the product, 2 is the down product's
 // backward, whose epilogue applies the SwiGLU backward with the forward's
-// pre-activations GU ([M, 2 N]) and writes dgu ([M, 2 N]) to C.  3 is a
-// weight gradient, C[e] = A[seg e]^T B[seg e] ([G, Mdim, N], Mdim passed as
-// a_rows): both operands are the segment's rows, staged column-contiguous,
-// and the reduction runs over the segment.  4 is 1 adding the product to C.
+// pre-activations GU ([M, 2 N]) and writes dgu ([M, 2 N]) to C.  4 is 1
+// adding the product to C.  (The weight gradients run on their own kernel,
+// grouped_wgrad.hip.)
 template <bool BF16, int BM, int BR, int SA, int SB, int CPR, int DA, bool SWIGLU, bool SPLIT,
           bool SAVE = false, int VAR = 0>
 __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
@@ -380,7 +379,6 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
   constexpr bool kDrainLast = DA == SA - 1;
   static_assert(FM <= 5, "row blocks per wave");
   static_assert(VAR == 0 || (BF16 && !SWIGLU && !SAVE), "backward products: bf16, plain tiles");
-  static_assert(VAR != 3 || BM == 256, "weight gradient: 256-column row-operand stages");
   constexpr bool BT = VAR != 0;                  // B [K, N]: column-contiguous stages
 
   __shared__ u32x4 smem[SA * ASTAGE + SB * BSTAGE];
@@ -398,55 +396,19 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
   const int KT_all = kvec / CPR;   // slices per tile (forward and input-gradient products)
 
   const int xcd = blockIdx.x % kXcds, nj = gridDim.x / kXcds;
-  // Weight gradient (VAR 3): a_rows is the output rows Mdim of each expert,
-  // tiles are (expert, m tile, n tile) with n fastest.
-  const int mtn = VAR == 3 ? a_rows / BM : 1;
-  const int total = VAR == 3 ? G * mtn * ntiles : count_tiles<BM>(offsets, G, M, ntiles);
-  // Weight gradients (VAR 3) of few experts, or of one expert with far more
-  // rows than the mean, walk the tiles round-robin over the XCDs instead: an
-  // expert's tiles (whose reduction length is its row count) then spread
-  // over every XCD, which keeps the XCDs evenly loaded; consecutive tiles of
-  // an XCD still belong to one expert, since such experts have many tiles.
-  // With many balanced experts the bands keep each expert's rows in one L2.
-  bool rr = false;
-  if constexpr (VAR == 3) {
-    int mx = 0;
-    for (int e = lane_id(); e < G; e += kWave) {
-      const int n = clamp_row(offsets[e + 1], M) - clamp_row(offsets[e], M);
-      mx = n > mx ? n : mx;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const int o = __shfl_xor(mx, off);
-      mx = o > mx ? o : mx;
-    }
-    rr = G <= 16 || (int64_t)uniform(mx) * G > 2 * (int64_t)M;
-  }
-  const int band_end = rr ? total : (int)((int64_t)total * (xcd + 1) / kXcds);
-  const int L0 = rr ? (int)blockIdx.x : (int)((int64_t)total * xcd / kXcds) + (int)(blockIdx.x / kXcds);
-  const int Lstep = rr ? (int)gridDim.x : nj;
+  const int total = count_tiles<BM>(offsets, G, M, ntiles);
+  const int band_end = (int)((int64_t)total * (xcd + 1) / kXcds);
+  const int L0 = (int)((int64_t)total * xcd / kXcds) + (int)(blockIdx.x / kXcds);
+  const int Lstep = nj;
 
   int cur_e = 0, cur_base = 0;   // search cursor of find_tile
   for (int L = L0; L < band_end;
        L += Lstep) {
     Tile tile;
-    int seg_lo = 0, seg_hi = 0;   // VAR 3: the expert's rows, the reduction of its tile
-    if constexpr (VAR == 3) {
-      tile.expert = L / (mtn * ntiles);
-      const int rem = L - tile.expert * (mtn * ntiles);
-      tile.m0 = (rem / ntiles) * BM;
-      tile.n_tile = rem % ntiles;
-      tile.lo = tile.m0;
-      tile.hi = tile.m0 + BM;
-      seg_lo = clamp_row(offsets[tile.expert], M);
-      seg_hi = clamp_row(offsets[tile.expert + 1], M);
-      seg_hi = seg_hi > seg_lo ? seg_hi : seg_lo;
-    } else {
-      find_tile<BM>(offsets, G, M, ntiles, L, tile, cur_e, cur_base);
-    }
+    find_tile<BM>(offsets, G, M, ntiles, L, tile, cur_e, cur_base);
     const int m0 = tile.m0, hi = tile.hi, n0 = tile.n_tile * BN;
     const int rows = hi - m0 < BM ? hi - m0 : BM;
-    const int KT = VAR == 3 ? (seg_hi - seg_lo + CPR * 8 - 1) / (CPR * 8) : KT_all;
+    const int KT = KT_all;
     const int nblk = (rows + 31) / 32;
     // Row blocks g + 2 (wm + WMG i) below nblk.
     int live = (nblk - grp - 2 * wm + 2 * WMG - 1) / (2 * WMG);
@@ -467,27 +429,14 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     constexpr int NLA = (A_TOT + 3) / 4;           // row loads per group-0 wave per slice, at most
     // Without gather the resource starts at the tile's first row; with
     // gather (packed row p is row gather[p] / gk of A) it spans A's a_rows rows.
-    // VAR 3: both operands are the segment's rows (A [M, Mdim], B [M, N]);
-    // the buffers end at the segment end, so the K-rows of a last partial
-    // slice past it read as 0 (the whole offset goes per lane: the bounds
-    // check leaves out the scalar offset).
-    const u32x4 *a_base = VAR == 3 ? A + (int64_t)seg_lo * (a_rows / 8)
-                                   : gather ? A : A + (int64_t)m0 * kvec;
-    const uint32_t a_bytes = VAR == 3 ? (uint32_t)((int64_t)(seg_hi - seg_lo) * a_rows * 2)
-                                      : (uint32_t)((int64_t)(gather ? a_rows : rows) * kvec * 16);
-    const u32x4 *b_base = VAR == 3 ? B + (int64_t)seg_lo * (N / 8) : B + (int64_t)tile.expert * b_expert_vec;
-    const uint32_t b_bytes = VAR == 3 ? (uint32_t)((int64_t)(seg_hi - seg_lo) * N * 2)
-                                      : (uint32_t)(b_expert_vec * 16);
+    const u32x4 *a_base = gather ? A : A + (int64_t)m0 * kvec;
+    const uint32_t a_bytes = (uint32_t)((int64_t)(gather ? a_rows : rows) * kvec * 16);
+    const u32x4 *b_base = B + (int64_t)tile.expert * b_expert_vec;
+    const uint32_t b_bytes = (uint32_t)(b_expert_vec * 16);
     auto a_offsets = [&](uint32_t (&off)[NLA]) {
 #pragma unroll
       for (int r = 0; r < NLA; ++r) {
         const int g = wq + 4 * r;
-        if constexpr (VAR == 3) {
-          int krow, col;
-          cc_lane<BM>(g, lane, krow, col);
-          off[r] = ((uint32_t)krow * (uint32_t)a_rows + (uint32_t)(m0 + col)) * 2u;
-          continue;
-        }
         int row = g * RPI + ld_row;
         row = row < rows ? row : rows - 1;
         const uint32_t src = gather ? gather_row(gather, m0 + row, gk, a_rows) : (uint32_t)row;
@@ -518,22 +467,13 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
       u32x4 *stage = a_ring + (kt % SA) * ASTAGE;
 #pragma unroll
       for (int r = 0; r < NLA; ++r)
-        if (r < na) {
-          if constexpr (VAR == 3)
-            buffer_load_lds16(a_base, a_bytes, stage + (wq + 4 * r) * 64,
-                              off[r] + (uint32_t)kt * (CPR * 8) * (uint32_t)a_rows * 2u, 0);
-          else
-            buffer_load_lds16(a_base, a_bytes, stage + (wq + 4 * r) * 64, off[r], kt * CPR * 16);
-        }
+        if (r < na) buffer_load_lds16(a_base, a_bytes, stage + (wq + 4 * r) * 64, off[r], kt * CPR * 16);
     };
     auto issue_b = [&](int kt, const uint32_t (&off)[NLB]) {
       u32x4 *stage = b_ring + (kt % SB) * BSTAGE;
 #pragma unroll
       for (int r = 0; r < NLB; ++r)
-        if constexpr (VAR == 3)
-          buffer_load_lds16(b_base, b_bytes, stage + (wq + 4 * r) * 64, off[r] + (uint32_t)kt * b_step, 0);
-        else
-          buffer_load_lds16(b_base, b_bytes, stage + (wq + 4 * r) * 64, off[r], (uint32_t)kt * b_step);
+        buffer_load_lds16(b_base, b_bytes, stage + (wq + 4 * r) * 64, off[r], (uint32_t)kt * b_step);
     };
     // Waits for slice k of this wave's operand: the slices after it that are
     // already issued (up to k + SB - 2, or k + DA - 1 for the row tile) may
@@ -622,13 +562,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
 #pragma unroll
           for (int i = 0; i < NL; ++i)
             if (!DYN || i < live)
-            {
-              if constexpr (VAR == 3)
-                fa[q][i] = frag_tr<BM>(reinterpret_cast<const char *>(As), GRP + 2 * (wm + WMG * i),
-                                       2 * h + q, lane);
-              else
-                fa[q][i] = As[swz_c<CPR>((GRP + 2 * (wm + WMG * i)) * 32 + (lane & 31), cc)];
-            }
+              fa[q][i] = As[swz_c<CPR>((GRP + 2 * (wm + WMG * i)) * 32 + (lane & 31), cc)];
         }
         if (h == 0) {
           if constexpr (GRP == 0) {
@@ -740,10 +674,6 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
               *reinterpret_cast<uint32_t *>(out + base + N) = pack_bf16x2(du[0], du[1]);
             }
           }
-          continue;
-        }
-        if constexpr (VAR == 3) {
-          put(static_cast<uint16_t *>(C) + (int64_t)tile.expert * a_rows * N, N, rblk, col, val);
           continue;
         }
         if constexpr (VAR == 4) {
@@ -882,9 +812,6 @@ using G1Medium = PpCfg<320, 256, 4, 5, 4, true, 2>;
 using G2Medium = PpCfg<320, 256, 4, 5, 4, true, 2>;
 using G1Large = PpCfg<256, 256, 2, 3, 8, true, 1>;
 using G2Large = PpCfg<256, 256, 2, 3, 8, true, 1>;
-// Weight gradients: 256 x 256 output tiles of an expert's dW, the reduction
-// over its rows in 32-row slices, deep rings (the reductions are short).
-using G2Wgrad = PpCfg<256, 256, 4, 5, 4, true, 2>;
 
 // Which tile family serves a call: by the mean rows per expert.  Both halves
 // of an expert MLP use the same family.  The ping-pong tiles are up to 128
@@ -993,22 +920,6 @@ moe_status check_shape(moe_dtype dt, int M, int d, int ffn, int G) {
 // Reduction length from which the first product's input gradient (var 1)
 // uses the medium tiles.
 constexpr int kDgradLongK = 4096;
-
-bool launch_wgrad_pp(const void *a, const void *b, int M, int m_dim, int n_dim,
-                     const int32_t *offsets, int G, void *out, hipStream_t stream) {
-  using Cfg = G2Wgrad;
-  if (m_dim % Cfg::BM != 0 || n_dim % Cfg::BR != 0) return false;
-  const int ntiles = n_dim / Cfg::BR;
-  const int64_t tiles = (int64_t)G * (m_dim / Cfg::BM) * ntiles;
-  auto kern = k_grouped_gemm_pp<true, Cfg::BM, Cfg::BR, Cfg::SA, Cfg::SB, Cfg::CPR, Cfg::DA, false,
-                                Cfg::SPLIT, false, 3>;
-  static DeviceCache occ;
-  const int grid = persistent_grid((const void *)kern, 512, occ, tiles);
-  kern<<<dim3(grid), dim3(512), 0, stream>>>(static_cast<const u32x4 *>(a), M, 0, offsets, G,
-                                            static_cast<const u32x4 *>(b), 0, 0, ntiles, n_dim, out,
-                                            nullptr, 1, m_dim, nullptr);
-  return true;
-}
 
 bool launch_dgrad_pp(int var, const void *a, int M, int K, int N, const int32_t *offsets, int G,
                      const void *w, void *out, const void *gu, hipStream_t stream) {
