@@ -214,6 +214,8 @@ def alternatives(cfg, layer, stages, stream, grouped_ms, grouped_load, reps=10, 
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 GEMM_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "token_routing_expert_amd",
                            "csrc", "grouped_gemm.hip")
+WGRAD_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "token_routing_expert_amd",
+                            "csrc", "grouped_wgrad.hip")
 
 
 # The routed gate/up launch at the DeepSeek-V3 prefill shape (320-row tiles,
@@ -224,9 +226,9 @@ GATE_UP_KERNELS = ("k_grouped_gemm_pp<true, 320, 256, 4, 5, 4, 2, true, true, fa
                    "k_grouped_gemm<false, 32, 128, 1, 4, true, 2, 2, false>")
 
 
-def _source_sha():
+def _source_sha(path=GEMM_SOURCE):
     import hashlib
-    with open(GEMM_SOURCE, "rb") as f:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
@@ -327,6 +329,158 @@ def summarize_profile(workload, trace_dir, fetch_dir, write_dir, bench_line, war
     if rec:
         with open(os.path.join(out_dir, f"{workload}_gate_up_traffic.json"), "w") as f:
             json.dump(rec, f, indent=1)
+    print("\n".join(lines))
+
+
+# The weight-gradient launches of one training step, in the order the
+# backward runs them (MoeLayer.BACKWARD_STAGES): the routed down and gate/up
+# products', then the shared expert's, then the router product's.
+TRAIN_WGRAD_LAUNCHES = ("routed dW_down", "routed dW13", "shared dW_down", "shared dW13", "router dW_r")
+
+
+def summarize_train_profile(workload, trace_dir, fetch_dir, write_dir, bench_line, warmup, commands,
+                            out_dir):
+    """Summarise rocprofv3 runs of `bench.py --train` into
+    out_dir/<workload>_train_kernels.md and <workload>_train_wgrad_traffic.json.
+    Kernels are listed as summarize_profile lists them.  The weight-gradient
+    kernel runs several times per step on one grid size, so its dispatches
+    are told apart by their position within the step (TRAIN_WGRAD_LAUNCHES),
+    in the trace and in the counter passes alike; the record is the routed
+    dW13 launch's."""
+    from collections import defaultdict
+    trace = sorted(_rocprof_rows(trace_dir, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    if not trace:
+        raise SystemExit(f"no kernel trace under {trace_dir}")
+    steps = None
+    if bench_line and os.path.exists(bench_line):
+        with open(bench_line) as f:
+            found = [json.loads(l) for l in f if l.startswith("{")]
+        line = found[-1] if found else None
+        steps = line["steps"] if line else None
+    else:
+        line = None
+    durs = defaultdict(list)
+    for r in trace:
+        durs[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def by_position(values, runs):
+        """Split one kernel's per-dispatch values into per-launch-position lists."""
+        per = len(values) // runs if runs else 0
+        if not per or per * runs != len(values):
+            raise SystemExit(f"{len(values)} weight-gradient dispatches do not split into {runs} steps")
+        out = defaultdict(list)
+        for i, v in enumerate(values):
+            out[i % per].append(v)
+        return out, per
+
+    wg_name = next((k for k in durs if "k_weight_grad" in k), None)
+    if wg_name is None or steps is None:
+        raise SystemExit("no weight-gradient kernel in the trace, or no bench line")
+    pos_durs, per = by_position(durs[wg_name], warmup + steps)
+
+    def counter_positions(directory, counter):
+        rows = sorted((r for r in _rocprof_rows(directory, "counter_collection.csv")
+                       if r.get("Counter_Name") == counter),
+                      key=lambda r: int(r.get("Dispatch_Id") or 0))
+        copy = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")]
+        vals = [float(r["Counter_Value"]) for r in rows if "k_weight_grad" in r["Kernel_Name"]]
+        runs = len(vals) // per if per else 0
+        pos, _ = by_position(vals, runs)
+        return {k: sum(v) / len(v) for k, v in pos.items()}, (max(copy) if copy else None)
+
+    fetch, fcopy = counter_positions(fetch_dir, "FETCH_SIZE")
+    write, wcopy = counter_positions(write_dir, "WRITE_SIZE")
+    fs = 1024 * 1024 / fcopy if fcopy else None
+    ws = 1024 * 1024 / wcopy if wcopy else None
+    lines = [f"# rocprofv3 summary: {workload} training step (forward keeping pre-activations + backward)",
+             "", "Commands (the profiled bench runs, then this summary):", "", "```", *commands, "```", ""]
+    if fs and ws:
+        lines += [f"Calibration: the plain 1 GiB device copy reads FETCH_SIZE = {fcopy:.0f} KiB and "
+                  f"WRITE_SIZE = {wcopy:.0f} KiB, so HBM bytes = FETCH_SIZE x {fs:.3f} KiB + WRITE_SIZE "
+                  f"x {ws:.3f} KiB.", ""]
+    lines += [f"Kernel durations from the trace ({warmup} warm-up + {steps} timed steps traced); "
+              "'timed' drops the warm-up steps' dispatches.", "",
+              "| kernel | dispatches | avg us (timed) | total us per step |", "|---|---|---|---|"]
+    runs = warmup + steps
+    for name in sorted(durs, key=lambda k: -sum(durs[k])):
+        d = durs[name]
+        n_timed = len(d) * steps // runs
+        timed = d[len(d) - n_timed:] if n_timed else d
+        short = name.replace("void ", "").replace("moe::(anonymous namespace)::", "").split("(")[0]
+        lines.append(f"| {short} | {len(d)} | {sum(timed) / len(timed):.1f} | {sum(timed) / steps:.1f} |")
+    lines += ["", f"The weight-gradient kernel, by launch position within a step ({per} per step):", "",
+              "| launch | avg us (timed) | FETCH KiB | WRITE KiB | HBM GB (scaled) |", "|---|---|---|---|---|"]
+    rec = None
+    for i in range(per):
+        d = pos_durs[i]
+        t = d[warmup:] if len(d) > warmup else d
+        avg = sum(t) / len(t)
+        fk, wk = fetch.get(i), write.get(i)
+        gb = (fk * fs + wk * ws) * 1024 / 1e9 if fs and ws and fk is not None and wk is not None else None
+        label = TRAIN_WGRAD_LAUNCHES[i] if i < len(TRAIN_WGRAD_LAUNCHES) else f"launch {i}"
+        lines.append(f"| {label} | {avg:.1f} | {'' if fk is None else f'{fk:.0f}'} | "
+                     f"{'' if wk is None else f'{wk:.0f}'} | {'' if gb is None else f'{gb:.3f}'} |")
+        if i == 1:
+            rec = {"workload": workload, "kernel": wg_name, "launch": label, "avg_us_timed": round(avg, 1),
+                   "timed_dispatches": len(t), "fetch_kib": fk, "write_kib": wk, "fetch_scale": fs,
+                   "write_scale": ws, "bytes_per_launch": int(gb * 1e9) if gb else None,
+                   "source": os.path.relpath(WGRAD_SOURCE, os.path.dirname(PROFILES)),
+                   "source_sha256": _source_sha(WGRAD_SOURCE)}
+    lines.append("")
+    if line:
+        lines += ["bench.py line of the traced run (stage times from HIP events):", "", "```",
+                  json.dumps(line.get("stages")), json.dumps(line.get("roofline")), "```", ""]
+        if rec:
+            rec["bench_launch_ms_events"] = line["roofline"].get("launch_ms")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"{workload}_train_kernels.md"), "w") as f:
+        f.write("\n".join(lines))
+    if rec:
+        with open(os.path.join(out_dir, f"{workload}_train_wgrad_traffic.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+    print("\n".join(lines))
+
+
+ACTIVITY_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS",
+                     "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVES")
+
+
+def summarize_activity(workload, pmc_dir, commands, out_dir, xcds=8, simds=1024):
+    """profiles/<workload>_activity.md from one rocprofv3 --pmc pass with
+    ACTIVITY_COUNTERS: per kernel, the mean dispatch duration and counter
+    values, the shader clock (GRBM_GUI_ACTIVE / XCDs / duration) and the
+    matrix cores' busy fraction (SQ_VALU_MFMA_BUSY_CYCLES / SIMDs /
+    (GRBM_GUI_ACTIVE / XCDs)); the derived two only for dispatches longer
+    than 100 us, shorter than the counters' sampling window."""
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))
+    durs = defaultdict(dict)
+    for r in _rocprof_rows(pmc_dir, "counter_collection.csv"):
+        name = r["Kernel_Name"].replace("void ", "").replace("moe::(anonymous namespace)::", "").split("(")[0]
+        vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        durs[name][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    lines = [f"# rocprofv3 activity counters: {workload}", "",
+             "One counter pass over a short bench run (means per dispatch):", "", "```", *commands, "```", "",
+             "Derived: shader clock = GRBM_GUI_ACTIVE / 8 XCDs / dispatch duration; matrix-core busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8). Both only for dispatches "
+             "longer than 100 us (for shorter ones the counters' window exceeds the dispatch).", "",
+             "| kernel | dispatches | duration us | GRBM_GUI_ACTIVE | SQ_VALU_MFMA_BUSY_CYCLES | SQ_INSTS_LDS "
+             "| SQ_LDS_BANK_CONFLICT | clock GHz | MFMA busy |", "|---|---|---|---|---|---|---|---|---|"]
+    def mean(x):
+        return sum(x) / len(x) if x else 0.0
+    for name in sorted(durs, key=lambda k: -sum(durs[k].values())):
+        v = vals[name]
+        dur = mean(list(durs[name].values()))
+        gui, mfma = mean(v["GRBM_GUI_ACTIVE"]), mean(v["SQ_VALU_MFMA_BUSY_CYCLES"])
+        clock = busy = "–"
+        if dur > 100 and gui > 0:
+            clock = f"{gui / xcds / (dur * 1e3):.2f}"
+            busy = f"{100 * mfma / simds / (gui / xcds):.1f}%"
+        lines.append(f"| {name} | {len(durs[name])} | {dur:.1f} | {gui:.4g} | {mfma:.4g} | "
+                     f"{mean(v['SQ_INSTS_LDS']):.4g} | {mean(v['SQ_LDS_BANK_CONFLICT']):.4g} | {clock} | {busy} |")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"{workload}_activity.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
@@ -474,7 +628,7 @@ def measured_train_traffic(workload):
     try:
         with open(TRAIN_TRAFFIC_FILE) as f:
             t = json.load(f)
-        with open(GEMM_SOURCE, "rb") as f:
+        with open(WGRAD_SOURCE, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
@@ -671,6 +825,10 @@ def main():
                     help="write profiles/WORKLOAD_kernels.md and WORKLOAD_gate_up_traffic.json from "
                          "rocprofv3 output (--trace-dir, --fetch-dir, --write-dir, --bench-line); "
                          "runs no GPU work")
+    ap.add_argument("--summarize-activity", metavar="WORKLOAD",
+                    help="write profiles/WORKLOAD_activity.md from a rocprofv3 --pmc pass of the "
+                         "activity counters (--pmc-dir); runs no GPU work")
+    ap.add_argument("--pmc-dir")
     ap.add_argument("--trace-dir")
     ap.add_argument("--fetch-dir")
     ap.add_argument("--write-dir")
@@ -680,9 +838,13 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
+    if args.summarize_activity:
+        summarize_activity(args.summarize_activity, args.pmc_dir, args.command, PROFILES)
+        return
     if args.summarize_profile:
-        summarize_profile(args.summarize_profile, args.trace_dir, args.fetch_dir, args.write_dir,
-                          args.bench_line, args.warmup, args.command, PROFILES)
+        summarize = summarize_train_profile if args.train else summarize_profile
+        summarize(args.summarize_profile, args.trace_dir, args.fetch_dir, args.write_dir,
+                  args.bench_line, args.warmup, args.command, PROFILES)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -291,9 +291,14 @@ __device__ __forceinline__ void wg_run(const u32x4 *__restrict__ A, const u32x4 
     // register v, output column 8 (v / 4) + 4 (l / 32) + v % 4 -- registers
     // 4 a .. 4 a + 3 are four consecutive columns of one row, one 8-byte bf16
     // word.  A 32-row block goes to the staging block row-major in bf16
-    // (32 rows x 128 bytes), 16-byte chunk c of row r at c ^ ((r / 2) % 8),
-    // which spreads the 64 lanes of a write or a read over all banks.  Each
-    // lane then reads 16 bytes of one row (8 lanes per row) and stores them:
+    // (32 rows x 128 bytes): 16-byte chunk c of row r sits at c ^ (r % 8),
+    // its two 8-byte halves swapped when bit 3 of r is set.  LDS writes are
+    // served 16 lanes (128 bytes) per cycle with banks repeating every 128
+    // bytes, and the 16 lanes of a write here are 16 rows of one half-chunk:
+    // the rotation gives them 16 different 8-byte slots.  (A rotation by
+    // r / 2 measured 2-way conflicts on every write.)  Each lane then reads 16
+    // bytes of one row (8 lanes per row, so 16 lanes cover two whole rows),
+    // swaps the halves back in rows 8..15 and 24..31, and stores them:
     // every store instruction writes 8 whole 128-byte rows.  The buffer
     // store's scalar offset carries the row step, so the stores need no
     // address arithmetic.
@@ -313,14 +318,16 @@ __device__ __forceinline__ void wg_run(const u32x4 *__restrict__ A, const u32x4 
           typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
           const bf16x4 pk = {(__bf16)acc[i][j][4 * a], (__bf16)acc[i][j][4 * a + 1],
                              (__bf16)acc[i][j][4 * a + 2], (__bf16)acc[i][j][4 * a + 3]};
-          const int chunk = (4 * j + a) ^ ((wrow >> 1) & 7);
-          *reinterpret_cast<u32x2 *>(stg + wrow * 128 + chunk * 16 + whalf * 8) = __builtin_bit_cast(u32x2, pk);
+          const int chunk = (4 * j + a) ^ (wrow & 7);
+          const int half = whalf ^ ((wrow >> 3) & 1);
+          *reinterpret_cast<u32x2 *>(stg + wrow * 128 + chunk * 16 + half * 8) = __builtin_bit_cast(u32x2, pk);
         }
       u32x4 q[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = 8 * u + rrow;
-        q[u] = *reinterpret_cast<const u32x4 *>(stg + r * 128 + ((rch ^ ((r >> 1) & 7)) << 4));
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + r * 128 + ((rch ^ (r & 7)) << 4));
+        q[u] = (u & 1) == 0 ? v : u32x4{v[2], v[3], v[0], v[1]};   // rows with bit 3 set (u odd)
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
