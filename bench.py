@@ -250,13 +250,20 @@ def summarize_profile(workload, trace_dir, fetch_dir, write_dir, bench_line, war
 
     Durations per kernel come from the kernel trace (end - start of each
     dispatch), both over all dispatches and over the timed ones (each
-    kernel's first `warmup` dispatches dropped); HBM bytes from one-counter
+    kernel's first `warmup` dispatches dropped, and only the bench line's
+    `steps` after them kept: later ones -- cold-cache steps, graph replays --
+    are not in the bench line's launch time); HBM bytes from one-counter
     passes FETCH_SIZE and WRITE_SIZE, scaled by what the counters read for
     the plain 1 GiB device copy of the same runs (--copy-calibration)."""
     from collections import defaultdict
     trace = _rocprof_rows(trace_dir, "kernel_trace.csv")
     if not trace:
         raise SystemExit(f"no kernel trace under {trace_dir}")
+    steps = None
+    if bench_line and os.path.exists(bench_line):
+        with open(bench_line) as f:
+            found = [json.loads(l) for l in f if l.startswith("{")]
+        steps = found[-1]["steps"] if found else None
     durs = defaultdict(list)
     for r in sorted(trace, key=lambda r: int(r["Start_Timestamp"])):
         gx = r.get("Grid_Size_X")
@@ -292,6 +299,8 @@ def summarize_profile(workload, trace_dir, fetch_dir, write_dir, bench_line, war
     for key in sorted(durs, key=lambda k: -sum(durs[k])):
         d = durs[key]
         timed = d[warmup:] if len(d) > warmup else d
+        if steps:
+            timed = timed[:steps]
         avg_all, avg_t = sum(d) / len(d), sum(timed) / len(timed)
         fk, wk = fetch.get(key), write.get(key)
         gb = ((fk or 0) * fs + (wk or 0) * ws) * 1024 / 1e9 if fs and (fk or wk) else None
@@ -819,6 +828,8 @@ def main():
                          "then the backward to dx, the weight gradients and dlogits (bf16 only)")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="after the timed steps, time this many more from cold caches")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the step replayed from a HIP graph")
     ap.add_argument("--no-alternatives", action="store_true",
                     help="skip timing the capacity-padded (CF 1, 1.25) and per-expert-loop forms")
     ap.add_argument("--summarize-profile", metavar="WORKLOAD",
@@ -952,6 +963,36 @@ def main():
                      "stages_ms": {name: round(sum(c[j].elapsed_time(c[j + 1]) for c in cold) / n_cold, 4)
                                    for j, name in enumerate(stages)}}
 
+    # The same step replayed from a HIP graph of its launches: what the eager
+    # step spends on launch overhead (the layer allocates nothing and sets no
+    # memory with memset, so it captures as is).  The replayed step's output
+    # is checked against the eager one's bits.
+    graph_info = None
+    if not args.no_graph:
+        y_eager = layer.y.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(layer.y, y_eager)) if not router else None
+        ge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ge[0].record(stream)
+        for _ in range(K):
+            g.replay()
+        ge[1].record(stream)
+        torch.cuda.synchronize()
+        gms = ge[0].elapsed_time(ge[1]) / K
+        graph_info = {"steps": K, "step_ms": round(gms, 4), "tokens_per_s": round(cfg.T / (gms * 1e-3), 1),
+                      "output_equals_eager": same}
+        del g
+
     from token_routing_expert_amd.layer import to_host
     counts = to_host(layer.counts)
     f_gate_up, f_down, f_shared = expert_flops(cfg)
@@ -1043,8 +1084,10 @@ def main():
         "headline": ("value: the K timed steps back to back (wall clock around them; a step may "
                      "find the previous step's data in the L2s and the 256 MB MALL); "
                      "cold_cache.tokens_per_s_p50: the median of steps each run after a 1 GiB fill "
-                     "that evicts both (HIP events, the fill outside them)"),
+                     "that evicts both (HIP events, the fill outside them); graph_replay: the same "
+                     "step's launches captured once in a HIP graph and replayed K times"),
         "cold_cache": cold_info,
+        "graph_replay": graph_info,
         "load": load_accounting(cfg, counts,
                                 to_host(layer.send_counts) if cfg.n_ep else None),
         "device": torch.cuda.get_device_name(0),
