@@ -380,6 +380,11 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
   static_assert(FM <= 5, "row blocks per wave");
   static_assert(VAR == 0 || (BF16 && !SWIGLU && !SAVE), "backward products: bf16, plain tiles");
   constexpr bool BT = VAR != 0;                  // B [K, N]: column-contiguous stages
+  // The forward's plain product (the down product, bf16) stores through
+  // LDS as whole 128-byte lines (STG); its MFMAs take the weight fragment
+  // first, so each 32 x 32 block holds the transposed output.
+  constexpr bool STG = BF16 && VAR == 0 && !SAVE && !SWIGLU;
+  constexpr bool kStoreNT = true;
 
   __shared__ u32x4 smem[SA * ASTAGE + SB * BSTAGE];
   u32x4 *const a_ring = smem;
@@ -586,7 +591,12 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
           for (int i = 0; i < NL; ++i)
             if (!DYN || i < live)
 #pragma unroll
-              for (int j = 0; j < NB; ++j) Mma<BF16>::run(fa[q][i], fb[q][j], acc[i][j]);
+              for (int j = 0; j < NB; ++j) {
+                if constexpr (STG)
+                  Mma<BF16>::run(fb[q][j], fa[q][i], acc[i][j]);
+                else
+                  Mma<BF16>::run(fa[q][i], fb[q][j], acc[i][j]);
+              }
         asm volatile("" ::: "memory");
         if (GRP == 0 && h == NH - 1 && kt + 1 < KT) wait_a(kt + 1);
         asm volatile("" ::: "memory");
@@ -596,6 +606,64 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
     }
     if (GRP == 0) phase_barrier();   // both groups leave the tile aligned
     asm volatile("" ::: "memory");
+
+    if constexpr (STG) {
+      // Epilogue through LDS.  Each block holds the transpose: lane l holds
+      // output row l % 32 and, in register v, column 8 (v / 4) + 4 (l / 32) +
+      // v % 4 of the block -- registers 4 a .. 4 a + 3 are four consecutive
+      // columns of one row, one 8-byte bf16 word.  A 32-row block of the
+      // wave (64 columns) goes to 4 KB of staging row-major: 16-byte chunk c
+      // of row r at c ^ (r % 8), its 8-byte halves swapped when bit 3 of r
+      // is set -- the 16 lanes of a write (16 rows of one half-chunk) then
+      // fill 16 different 8-byte bank slots.  Each lane reads 16 bytes of
+      // one row back (8 lanes per row), swaps the halves back in rows with
+      // bit 3 set, and stores them: 8 whole 128-byte rows per instruction,
+      // rows past the segment end left out.  The staging is in row stages
+      // DA .. SA - 1: the K loop's reads of them are done at the barrier
+      // that closes the tile, the next tile's first loads fill stages below
+      // DA, and stage DA is refilled only after the next tile's first
+      // barrier, which every wave reaches after its epilogue's reads.
+      static_assert((SA - DA) * ASTAGE * 16 >= 8 * 4096, "epilogue staging");
+      char *const stg = reinterpret_cast<char *>(a_ring + DA * ASTAGE) + wave * 4096;
+      const uint64_t cb = reinterpret_cast<uint64_t>(static_cast<uint16_t *>(C) + (int64_t)m0 * N);
+      const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<void *>(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(cb >> 32)) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)cb)),
+          (short)0, 0x7FFFFFFF, kBufferFlags);
+      const int wrow = lane & 31, whalf = lane >> 5;   // write side: row, 8-byte half of a chunk
+      const int rrow = lane >> 3, rch = lane & 7;      // read side: row (of 8), chunk
+      const uint32_t vout = ((uint32_t)rrow * (uint32_t)N + (uint32_t)(n0 + wn * 64 + 8 * rch)) * 2u;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        if (DYN && i >= live) continue;
+        const int rb = GRP + 2 * (wm + WMG * i);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            const bf16x4 pk = {(__bf16)acc[i][j][4 * a], (__bf16)acc[i][j][4 * a + 1],
+                               (__bf16)acc[i][j][4 * a + 2], (__bf16)acc[i][j][4 * a + 3]};
+            const int chunk = (4 * j + a) ^ (wrow & 7);
+            const int half = whalf ^ ((wrow >> 3) & 1);
+            *reinterpret_cast<u32x2 *>(stg + wrow * 128 + chunk * 16 + half * 8) = __builtin_bit_cast(u32x2, pk);
+          }
+        u32x4 q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 8 * u + rrow;
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + r * 128 + ((rch ^ (r & 7)) << 4));
+          q[u] = (u & 1) == 0 ? v : u32x4{v[2], v[3], v[0], v[1]};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (m0 + 32 * rb + 8 * u + rrow < hi)
+            __builtin_amdgcn_raw_buffer_store_b128(q[u], out_rsrc, vout,
+                                                   (uint32_t)(32 * rb + 8 * u) * (uint32_t)N * 2u,
+                                                   kStoreNT ? 2 : 0);
+      }
+      return;
+    }
 
     // Epilogue.  MFMA 32x32 output layout: lane l holds column l % 32 and, in
     // register v, row 8 (v / 4) + 4 (l / 32) + v % 4.  bf16 output: adjacent
