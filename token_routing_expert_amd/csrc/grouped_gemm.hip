@@ -385,6 +385,9 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
   // first, so each 32 x 32 block holds the transposed output.
   constexpr bool STG = BF16 && VAR == 0 && !SAVE && !SWIGLU;
   constexpr bool kStoreNT = true;
+  // The forward's SwiGLU product (bf16) stores h, and with SAVE the
+  // pre-activations, through LDS too (STGH), as 64-byte row segments.
+  constexpr bool STGH = BF16 && VAR == 0 && SWIGLU;
 
   __shared__ u32x4 smem[SA * ASTAGE + SB * BSTAGE];
   u32x4 *const a_ring = smem;
@@ -592,7 +595,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
             if (!DYN || i < live)
 #pragma unroll
               for (int j = 0; j < NB; ++j) {
-                if constexpr (STG)
+                if constexpr (STG || STGH)
                   Mma<BF16>::run(fb[q][j], fa[q][i], acc[i][j]);
                 else
                   Mma<BF16>::run(fa[q][i], fb[q][j], acc[i][j]);
@@ -661,6 +664,84 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
             __builtin_amdgcn_raw_buffer_store_b128(q[u], out_rsrc, vout,
                                                    (uint32_t)(32 * rb + 8 * u) * (uint32_t)N * 2u,
                                                    kStoreNT ? 2 : 0);
+      }
+      return;
+    }
+
+    if constexpr (STGH) {
+      // Epilogue through LDS for the SwiGLU product: a wave's 32 output
+      // columns of a 32-row block are 64 bytes per row.  As above, lane l
+      // holds row l % 32 and registers 4 a .. 4 a + 3 hold columns 8 a +
+      // 4 (l / 32) .. + 3.  Staging rows are 64 bytes: 16-byte chunk c of row
+      // r sits at c ^ ((r / 2) % 4), its halves swapped when bit 3 of r is
+      // set, so the 16 lanes of an 8-byte write (16 rows) fill 16 different
+      // 8-byte slots of 128 bytes.  Each lane reads 16 bytes back (4 lanes
+      // per row, 16 rows per read: 256 contiguous bytes) and stores them:
+      // 16 row segments of 64 bytes per instruction, the other half of each
+      // 128-byte line coming from the neighbouring wave, so these are plain
+      // stores that meet in the L2.  Same staging place and lifetime as the
+      // plain product's.
+      static_assert((SA - DA) * ASTAGE * 16 >= 8 * 2048, "epilogue staging");
+      char *const stg = reinterpret_cast<char *>(a_ring + DA * ASTAGE) + wave * 2048;
+      const int wrow = lane & 31, whalf = lane >> 5;
+      const int rrow = lane >> 2, rch = lane & 3;      // read side: row (of 16), logical chunk
+      const int pch = rch ^ ((rrow >> 1) & 3);         // its place in the staging row
+      const bool rswap = (rrow >> 3) & 1;
+      // Buffer resource from row m0 of a row-major [*, ld] bf16 matrix.
+      auto rsrc_at = [&](void *base, int64_t ld) {
+        const uint64_t cb = reinterpret_cast<uint64_t>(static_cast<uint16_t *>(base) + (int64_t)m0 * ld);
+        return __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<void *>(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(cb >> 32)) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)cb)),
+            (short)0, 0x7FFFFFFF, kBufferFlags);
+      };
+      // One 32 x 32 block of this lane's 16 values to rows 32 rb .. + 31 of
+      // the tile, columns col .. col + 31 of a matrix of pitch ld.
+      auto put_block = [&](__amdgpu_buffer_rsrc_t rsrc, uint32_t ld, int col, int rb, const float(&val)[16]) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          const bf16x4 pk = {(__bf16)val[4 * a], (__bf16)val[4 * a + 1], (__bf16)val[4 * a + 2],
+                             (__bf16)val[4 * a + 3]};
+          const int chunk = a ^ ((wrow >> 1) & 3);
+          const int half = whalf ^ ((wrow >> 3) & 1);
+          *reinterpret_cast<u32x2 *>(stg + wrow * 64 + chunk * 16 + half * 8) = __builtin_bit_cast(u32x2, pk);
+        }
+        u32x4 q[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + (16 * u + rrow) * 64 + pch * 16);
+          q[u] = rswap ? u32x4{v[2], v[3], v[0], v[1]} : v;
+        }
+        const uint32_t vout = ((uint32_t)rrow * ld + (uint32_t)(col + 8 * rch)) * 2u;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          if (m0 + 32 * rb + 16 * u + rrow < hi)
+            __builtin_amdgcn_raw_buffer_store_b128(q[u], rsrc, vout, (uint32_t)(32 * rb + 16 * u) * ld * 2u, 0);
+      };
+      const __amdgpu_buffer_rsrc_t h_rsrc = rsrc_at(C, N);
+      const int col = n0 + wn * 32;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        if (DYN && i >= live) continue;
+        const int rb = GRP + 2 * (wm + WMG * i);
+        float val[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) val[v] = silu(acc[i][0][v]) * acc[i][1][v];
+        put_block(h_rsrc, (uint32_t)N, col, rb, val);
+        if constexpr (SAVE) {
+          // Pre-activations for the backward: gate at column col, up at
+          // N + col of a [M, 2 N] row.
+          const __amdgpu_buffer_rsrc_t gu_rsrc = rsrc_at(GU, 2 * (int64_t)N);
+          float g[16], u[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            g[v] = acc[i][0][v];
+            u[v] = acc[i][1][v];
+          }
+          put_block(gu_rsrc, 2u * (uint32_t)N, col, rb, g);
+          put_block(gu_rsrc, 2u * (uint32_t)N, N + col, rb, u);
+        }
       }
       return;
     }
