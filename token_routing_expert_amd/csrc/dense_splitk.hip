@@ -17,9 +17,14 @@
 //           not depend on the schedule), then SwiGLU (gate/up) or a plain
 //           cast (down), rounded once to bf16.
 //
-// A (rows) and W (weights) are bf16, row-major and K-contiguous, so each MFMA
-// operand is one 16-byte load per lane straight from memory: lane l holds
-// row l % 32 and K positions 8 (l / 32) .. + 7 of a 16-deep K step.
+// A (rows) and W (weights) are bf16, row-major and K-contiguous.  A
+// workgroup streams its K range in 64-byte slices of the token rows and of
+// its 64 weight rows into LDS with direct buffer-to-LDS loads (each load
+// instruction fills 16 rows x 64 bytes; a ring of 4 stages, 3 slices ahead),
+// and every wave reads its MFMA operands from there: lane l holds row l % 32
+// and K positions 8 (l / 32) .. + 7 of a 16-deep K step.  Each weight byte
+// thus crosses the memory system once per workgroup, in whole 64-byte row
+// segments.
 #include "common.hpp"
 #include "gemm_common.hpp"
 
@@ -28,75 +33,108 @@ namespace {
 
 constexpr int kDenseBN = 64;       // output columns (weight rows) per workgroup
 constexpr int kDenseMaxRows = 256;  // 8 row blocks of 32, two per wave
-constexpr int kDenseU = 8;          // K steps whose operands are loaded together
 
 __device__ __forceinline__ void mma_bf16(const u32x4 &a, const u32x4 &b, f32x16 &c) {
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                               c, 0, 0, 0);
 }
 
+// Stage position (16-byte units) of chunk cc (0..3) of row r in a stage of
+// 64-byte rows: 16 consecutive rows at one chunk cover all 64 banks once.
+__device__ __forceinline__ int dense_slot(int r, int cc) { return r * 4 + (cc ^ ((r >> 2) & 3)); }
+
 // Workgroup (n tile blockIdx.x, K range blockIdx.y), 4 waves; wave w owns
-// row blocks w and w + 4 (the second only when M > 128) and both 32-column
-// blocks of the tile.  Rows past M read row M - 1 and are not stored.
-// Host guarantees: 1 <= M <= 256, N % 64 == 0, K % (16 S) == 0 with
-// kchunk = K / S, gridDim = (N / 64, S).
+// row blocks w and w + 4 (the second only when RB == 2) and both 32-column
+// blocks of the tile.  AR = 128 RB token rows are staged per slice (rows
+// past M re-read row M - 1 and are not stored), with the tile's 64 weight
+// rows.  Host guarantees: 1 <= M <= AR, N % 64 == 0, kchunk = K / S a
+// multiple of 32, gridDim = (N / 64, S).
+template <int RB>
 __global__ __launch_bounds__(256) void k_dense_partial(const u32x4 *__restrict__ A, int M, int K,
                                                        const u32x4 *__restrict__ W, int N, int kchunk,
                                                        float *__restrict__ P) {
+  constexpr int CPR = 4, RPI = 16, S = 4, DIST = S - 1;
+  constexpr int AR = 128 * RB, BRW = kDenseBN;
+  constexpr int ASTAGE = AR * CPR, STAGE = (AR + BRW) * CPR;
+  constexpr int NLA = AR / RPI / 4, NLB = BRW / RPI / 4;   // loads per wave per slice
+  __shared__ u32x4 smem[S * STAGE];
+
   const int lane = lane_id();
   const int wave = uniform(threadIdx.x >> 6);
   const int nrb = (M + 31) / 32;
-  if (wave >= nrb) return;   // no live row block (no barrier follows)
-  const bool two = wave + 4 < nrb;
   const int n0 = blockIdx.x * kDenseBN, s = blockIdx.y;
-  const int kvec = K / 8, lr = lane & 31, kh = lane >> 5;
-  const int c0 = s * (kchunk / 8) + kh;   // this lane's first 16-byte chunk
-  int r0 = wave * 32 + lr, r1 = (wave + 4) * 32 + lr;
-  r0 = r0 < M ? r0 : M - 1;
-  r1 = r1 < M ? r1 : M - 1;
-  const u32x4 *a0 = A + (int64_t)r0 * kvec + c0;
-  const u32x4 *a1 = A + (int64_t)r1 * kvec + c0;
-  const u32x4 *b0 = W + (int64_t)(n0 + lr) * kvec + c0;
-  const u32x4 *b1 = W + (int64_t)(n0 + 32 + lr) * kvec + c0;
-  const int steps = kchunk / 16;
+  const int kvec = K / 8;                       // 16-byte chunks per row
+  const int KT = kchunk / 32;                   // 64-byte slices in the K range
+  const uint32_t kbase = (uint32_t)(s * (kchunk / 8)) * 16u;   // byte offset of the range in a row
 
-  f32x16 acc[2][2];
+  // Load lane mapping: lane l fills row l / 4 of a 16-row group, slot l % 4,
+  // which holds global chunk (l % 4) ^ key of that row.
+  const int ld_row = lane / CPR, ld_slot = lane % CPR;
+  const uint32_t key = (uint32_t)((ld_row >> 2) & 3);
+  uint32_t aoff[NLA], boff[NLB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int r = 0; r < NLA; ++r) {
+    int row = (wave + 4 * r) * RPI + ld_row;
+    row = row < M ? row : M - 1;
+    aoff[r] = ((uint32_t)row * (uint32_t)kvec + ((uint32_t)ld_slot ^ key)) * 16u + kbase;
+  }
+#pragma unroll
+  for (int r = 0; r < NLB; ++r)
+    boff[r] = ((uint32_t)(n0 + (wave + 4 * r) * RPI + ld_row) * (uint32_t)kvec + ((uint32_t)ld_slot ^ key)) * 16u +
+              kbase;
+  const uint32_t a_bytes = (uint32_t)M * (uint32_t)kvec * 16u;
+  const uint32_t b_bytes = (uint32_t)N * (uint32_t)kvec * 16u;
+  auto issue = [&](int kt) {
+    u32x4 *stage = smem + (kt % S) * STAGE;
+#pragma unroll
+    for (int r = 0; r < NLA; ++r)
+      buffer_load_lds16(A, a_bytes, stage + (wave + 4 * r) * 64, aoff[r], (uint32_t)kt * 64u);
+#pragma unroll
+    for (int r = 0; r < NLB; ++r)
+      buffer_load_lds16(W, b_bytes, stage + ASTAGE + (wave + 4 * r) * 64, boff[r], (uint32_t)kt * 64u);
+  };
+
+  f32x16 acc[RB][2];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  const bool live[2] = {wave < nrb, wave + 4 < nrb};
 
-  for (int k0 = 0; k0 < steps; k0 += kDenseU) {
-    u32x4 fa0[kDenseU], fa1[kDenseU], fb0[kDenseU], fb1[kDenseU];
+  for (int j = 0; j < DIST && j < KT; ++j) issue(j);
+  // Slice kt: wait for this wave's loads of it (later slices stay in flight),
+  // barrier, refill the stage of slice kt - 1 (every wave's MFMAs consumed
+  // their reads of it before this barrier), then two K steps of MFMAs.
+  for (int kt = 0; kt < KT; ++kt) {
+    const int ahead = (KT - 1 < kt + DIST - 1 ? KT - 1 : kt + DIST - 1) - kt;
+    wait_vmcnt(ahead * (NLA + NLB));
+    __builtin_amdgcn_s_barrier();
+    if (kt + DIST < KT) issue(kt + DIST);
+    const u32x4 *st = smem + (kt % S) * STAGE;
 #pragma unroll
-    for (int u = 0; u < kDenseU; ++u)
-      if (k0 + u < steps) {
-        const int off = 2 * (k0 + u);   // one K step is two 16-byte chunks
-        fb0[u] = b0[off];
-        fb1[u] = b1[off];
-        fa0[u] = a0[off];
-        if (two) fa1[u] = a1[off];
-      }
+    for (int q = 0; q < 2; ++q) {
+      const int cc = 2 * q + (lane >> 5);
+      const u32x4 fb0 = st[ASTAGE + dense_slot(lane & 31, cc)];
+      const u32x4 fb1 = st[ASTAGE + dense_slot(32 + (lane & 31), cc)];
 #pragma unroll
-    for (int u = 0; u < kDenseU; ++u)
-      if (k0 + u < steps) {
-        mma_bf16(fa0[u], fb0[u], acc[0][0]);
-        mma_bf16(fa0[u], fb1[u], acc[0][1]);
-        if (two) {
-          mma_bf16(fa1[u], fb0[u], acc[1][0]);
-          mma_bf16(fa1[u], fb1[u], acc[1][1]);
+      for (int i = 0; i < RB; ++i)
+        if (live[i]) {
+          const u32x4 fa = st[dense_slot((wave + 4 * i) * 32 + (lane & 31), cc)];
+          mma_bf16(fa, fb0, acc[i][0]);
+          mma_bf16(fa, fb1, acc[i][1]);
         }
-      }
+    }
   }
 
   // MFMA 32x32 output layout: lane l holds column l % 32 and, in register v,
   // row 8 (v / 4) + 4 (l / 32) + v % 4 of the block.
   float *out = P + (int64_t)s * M * N;
+  const int kh = lane >> 5, lr = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (i == 1 && !two) break;
+  for (int i = 0; i < RB; ++i) {
+    if (!live[i]) continue;
     const int rb = (wave + 4 * i) * 32;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -153,12 +191,13 @@ __global__ __launch_bounds__(256) void k_dense_reduce(const float *__restrict__ 
 }
 
 // Splits of a K-deep reduction over N / 64 column tiles: enough workgroups
-// for two per CU (512), at most 16 splits, each split a multiple of 16 deep.
+// for two per CU (512), at most 16 splits, each split a multiple of 32 deep
+// (whole 64-byte slices).
 int dense_splits(int K, int N) {
   const int tiles = N / kDenseBN;
   int s = (512 + tiles - 1) / tiles;
   s = s < 1 ? 1 : (s > 16 ? 16 : s);
-  while (s > 1 && K % (16 * s) != 0) --s;
+  while (s > 1 && K % (32 * s) != 0) --s;
   return s;
 }
 
@@ -190,15 +229,23 @@ extern "C" moe_status moe_dense_swiglu(const void *x, moe_dtype dt, int M, int d
 
   // Gate/up: N = 2 ffn weight rows (gate rows, then up rows), K = d.
   const int s1 = dense_splits(d, 2 * ffn);
-  k_dense_partial<<<dim3(2 * ffn / kDenseBN, s1), dim3(256), 0, stream>>>(
-      static_cast<const u32x4 *>(x), M, d, static_cast<const u32x4 *>(w13), 2 * ffn, d / s1, P);
+  if (M <= 128)
+    k_dense_partial<1><<<dim3(2 * ffn / kDenseBN, s1), dim3(256), 0, stream>>>(
+        static_cast<const u32x4 *>(x), M, d, static_cast<const u32x4 *>(w13), 2 * ffn, d / s1, P);
+  else
+    k_dense_partial<2><<<dim3(2 * ffn / kDenseBN, s1), dim3(256), 0, stream>>>(
+        static_cast<const u32x4 *>(x), M, d, static_cast<const u32x4 *>(w13), 2 * ffn, d / s1, P);
   const int64_t q1 = (int64_t)M * ffn / 4;
   k_dense_reduce_swiglu<<<dim3((unsigned)((q1 + 255) / 256)), dim3(256), 0, stream>>>(
       P, s1, M, ffn, static_cast<uint16_t *>(h), static_cast<uint16_t *>(gu));
   // Down: N = d, K = ffn.
   const int s2 = dense_splits(ffn, d);
-  k_dense_partial<<<dim3(d / kDenseBN, s2), dim3(256), 0, stream>>>(
-      static_cast<const u32x4 *>(h), M, ffn, static_cast<const u32x4 *>(w2), d, ffn / s2, P);
+  if (M <= 128)
+    k_dense_partial<1><<<dim3(d / kDenseBN, s2), dim3(256), 0, stream>>>(
+        static_cast<const u32x4 *>(h), M, ffn, static_cast<const u32x4 *>(w2), d, ffn / s2, P);
+  else
+    k_dense_partial<2><<<dim3(d / kDenseBN, s2), dim3(256), 0, stream>>>(
+        static_cast<const u32x4 *>(h), M, ffn, static_cast<const u32x4 *>(w2), d, ffn / s2, P);
   const int64_t q2 = (int64_t)M * d / 4;
   k_dense_reduce<<<dim3((unsigned)((q2 + 255) / 256)), dim3(256), 0, stream>>>(P, s2, M, d,
                                                                              static_cast<uint16_t *>(y));
