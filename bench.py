@@ -244,6 +244,24 @@ def _rocprof_rows(directory, suffix):
     return rows
 
 
+def copy_calibration(fetch_dir, write_dir):
+    """KiB of HBM traffic per KiB of FETCH_SIZE and of WRITE_SIZE, from the
+    plain 1 GiB device copy of the counter runs (--copy-calibration 1024):
+    the largest dispatch of the runtime's copy kernel (smaller device copies
+    of the same kernel and grid, such as a clone of the layer output, are
+    not it).  (None, None) when there is no such dispatch."""
+    def largest(directory, counter):
+        best = 0.0
+        for r in _rocprof_rows(directory, "counter_collection.csv") if directory else []:
+            if r.get("Counter_Name") == counter and r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer"):
+                best = max(best, float(r["Counter_Value"]))
+        return best
+    f, w = largest(fetch_dir, "FETCH_SIZE"), largest(write_dir, "WRITE_SIZE")
+    if f < 1e5 or w < 1e5:
+        return None, None
+    return 1024 * 1024 / f, 1024 * 1024 / w   # 1 GiB in KiB
+
+
 def summarize_profile(workload, trace_dir, fetch_dir, write_dir, bench_line, warmup, commands, out_dir):
     """Summarise rocprofv3 runs of bench.py for one workload into
     out_dir/<workload>_kernels.md and out_dir/<workload>_gate_up_traffic.json.
@@ -281,10 +299,7 @@ def summarize_profile(workload, trace_dir, fetch_dir, write_dir, bench_line, war
         return {k: sum(v) / len(v) for k, v in vals.items()}
 
     fetch, write = counters(fetch_dir, "FETCH_SIZE"), counters(write_dir, "WRITE_SIZE")
-    copy = [k for k in fetch if k[0].startswith("__amd_rocclr_copyBuffer") and fetch[k] > 1e5]
-    fs = ws = None
-    if copy and write.get(copy[0]):
-        fs, ws = 1024 * 1024 / fetch[copy[0]], 1024 * 1024 / write[copy[0]]   # 1 GiB in KiB
+    fs, ws = copy_calibration(fetch_dir, write_dir)
     lines = [f"# rocprofv3 summary: {workload}", "",
              "Commands (the profiled bench runs, then this summary):", "", "```", *commands, "```", ""]
     if fs:
