@@ -48,10 +48,13 @@ __device__ __forceinline__ int count_tiles(const int32_t *__restrict__ offsets, 
   return uniform(sum);
 }
 
+constexpr int kMBlock = 4;   // m-tiles of an expert grouped together in the tile order
+
 // Which expert and which (m, n) tile is tile number L.  Tiles are numbered
-// expert by expert; inside an expert n-tile major and m-tile minor, so the
-// m-tiles that share one weight tile are adjacent and the n-tiles that share
-// the expert's rows follow each other.  Every wave computes the same answer.
+// expert by expert; inside an expert by blocks of kMBlock m-tiles, each
+// block n-tile major and m-tile minor, so the m-tiles that share one weight
+// tile are adjacent and the n-tiles that share a block's rows follow each
+// other.  Every wave computes the same answer.
 // A workgroup asks for increasing L, so the search resumes at the expert
 // (e0) and tile number (base) of the previous answer: one 64-expert window
 // per call in the usual case instead of a scan from expert 0.
@@ -85,8 +88,15 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
       const int first = uniform(__shfl(excl, src));
       const int local = L - first;
       const int mtiles = (t.hi - t.lo + BM - 1) / BM;
-      t.m0 = t.lo + (local % mtiles) * BM;
-      t.n_tile = local / mtiles;
+      // Inside an expert the m-tiles go in blocks of kMBlock: block by block,
+      // n-tile by n-tile, the block's m-tiles adjacent.  Tiles that run at
+      // the same time on one XCD then share kMBlock row tiles and a few
+      // weight tiles instead of one weight tile and many row tiles.
+      const int mb = min(local / (kMBlock * ntiles), (mtiles - 1) / kMBlock);
+      const int msize = min(kMBlock, mtiles - mb * kMBlock);
+      const int rem = local - mb * kMBlock * ntiles;
+      t.m0 = t.lo + (mb * kMBlock + rem % msize) * BM;
+      t.n_tile = rem / msize;
       e0 = t.expert;
       base = first;
       return true;
