@@ -120,7 +120,13 @@ __device__ __forceinline__ void wait_vmcnt_range(int n) {
 }
 __device__ __forceinline__ void wait_vmcnt(int n) { wait_vmcnt_range<0, 63>(n < 63 ? n : 63); }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// The logistic function with the hardware reciprocal (within 1 ulp in fp32)
+// instead of a correctly rounded division: the SwiGLU epilogues evaluate it
+// for every output, and the division's instruction sequence was a third of
+// a gate/up tile's epilogue.  e^-g overflowing to infinity gives 0, as the
+// division would.
+__device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu(float g) { return g * sigmoid_f(g); }
 
 // Source row of packed row p under a gather: token gather[p] / gk, clamped to
 // [0, a_rows) so a corrupt index can only steer a read inside A.

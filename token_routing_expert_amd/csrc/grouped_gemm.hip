@@ -832,7 +832,7 @@ __global__ __launch_bounds__(512) void k_grouped_gemm_pp(
               float dg[2], du[2];
 #pragma unroll
               for (int c = 0; c < 2; ++c) {
-                const float s = 1.0f / (1.0f + __expf(-g[c]));
+                const float s = sigmoid_f(g[c]);
                 dg[c] = dh[c] * u[c] * (s * (1.0f + g[c] * (1.0f - s)));
                 du[c] = dh[c] * (g[c] * s);
               }

@@ -329,7 +329,7 @@ __global__ __launch_bounds__(WM * 128) void k_grouped_gemm_bwd(const BwdParams p
                 const int64_t base = (int64_t)row * 2 * p.N + col;
                 const float g = static_cast<const float *>(p.gu)[base];
                 const float u = static_cast<const float *>(p.gu)[base + p.N];
-                const float s = 1.0f / (1.0f + __expf(-g));
+                const float s = sigmoid_f(g);
                 static_cast<float *>(p.c)[base] = x * u * (s * (1.0f + g * (1.0f - s)));
                 static_cast<float *>(p.c)[base + p.N] = x * (g * s);
               } else {
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(WM * 128) void k_grouped_gemm_bwd(const BwdParams p
             float dg[2], du[2];
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-              const float s = 1.0f / (1.0f + __expf(-g[c]));
+              const float s = sigmoid_f(g[c]);
               dg[c] = dh[c] * u[c] * (s * (1.0f + g[c] * (1.0f - s)));
               du[c] = dh[c] * (g[c] * s);
             }
