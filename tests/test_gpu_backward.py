@@ -99,6 +99,9 @@ BWD_CASES = [
     # medium family above, the large one here, with ragged tails
     (256, 512, [300, 0, 1000, 97]),
     (512, 768, [200, 333, 260, 250]),
+    # experts of 6 and 7 row tiles of 256: the tile order's blocks of 4
+    # m-tiles, the last one partial
+    (256, 256, [1300, 2, 1537, 257]),
 ]
 
 

@@ -391,6 +391,14 @@ GEMM_CASES = [
     ("bf16", 256, 256, [96]),
     ("bf16", 256, 256, [288, 288]),
     ("bf16", 256, 256, [289, 289]),
+    # experts of more than 4 row tiles: the tile order takes an expert's
+    # m-tiles in blocks of 4, the last block partial.  The small tiles (a
+    # problem this size gives the ping-pong tiles fewer tiles than CUs) ...
+    ("bf16", 256, 256, [1300, 2, 1537, 257]),
+    # ... and enough column tiles (d = 4096) for the ping-pong tiles: large
+    # (6, 1, 7, 2 m-tiles of 256 rows) and medium (6 m-tiles of 320 rows)
+    ("bf16", 4096, 128, [1300, 2, 1537, 257]),
+    ("bf16", 4096, 128, [1700] + [1] * 15),
 ]
 
 
