@@ -143,13 +143,16 @@ constexpr int kBufferFlags = 0x00020000;
 
 // One wave's 16-byte-per-lane buffer load straight into LDS: lane l's data
 // lands at lds + 16 l.  base/bytes describe the buffer; voff is the lane's
-// byte offset, soff a wave-uniform byte offset added to it.
+// byte offset, soff a wave-uniform byte offset added to it.  CPOL is the
+// instruction's cache policy (kNonTemporal: the nt bit).
+constexpr int kNonTemporal = 2;
+template <int CPOL = 0>
 __device__ __forceinline__ void buffer_load_lds16(const void *base, uint32_t bytes, u32x4 *lds,
                                                   uint32_t voff, uint32_t soff) {
   const __amdgpu_buffer_rsrc_t res =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferFlags);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (__attribute__((address_space(3))) void *)lds, 16,
-                                           voff, soff, 0, 0);
+                                           voff, soff, 0, CPOL);
 }
 
 // A workgroup barrier that is also a scheduling fence: without the fences the
