@@ -89,7 +89,11 @@ __global__ __launch_bounds__(WM *WN * 64) void k_grouped_gemm(
     void *__restrict__ GU) {
   constexpr int NW = WM * WN;
   constexpr int BR = SWIGLU ? 2 * BN : BN;      // weight rows per tile
-  constexpr int NWA = NW / 2, NWB = NW - NWA;   // row-tile loaders, weight-tile loaders
+  // Row-tile loaders, weight-tile loaders.  A 32-row tile is 4 loads per
+  // slice, which one wave issues; the other waves then share the weight
+  // stream (decode's gate/up product: 2.44 -> 2.19 ms with 3 weight loaders
+  // instead of 2).
+  constexpr int NWA = BM <= 32 ? 1 : NW / 2, NWB = NW - NWA;
   constexpr int A_TOT = BM / 8, B_TOT = BR / 8;  // 8-row groups per slice
   constexpr int A_PW = (A_TOT + NWA - 1) / NWA, B_PW = (B_TOT + NWB - 1) / NWB;
   constexpr int MAXLD = A_PW > B_PW ? A_PW : B_PW;
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_grouped_gemm(
   constexpr int WNR = BN / WN, FN = WNR / 32;   // columns, column blocks per wave
   constexpr int NB = SWIGLU ? 2 * FN : FN;      // B fragments (gate, then up) per k-group
   constexpr int ASTAGE = BM * 8, BSTAGE = BR * 8;   // 16-byte chunks per stage
-  static_assert(NWA >= 1 && BM % 8 == 0 && BR % 8 == 0, "tile / wave mismatch");
+  static_assert(NWA >= 1 && NWB >= 1 && BM % 8 == 0 && BR % 8 == 0, "tile / wave mismatch");
   static_assert(FM * WM * 32 == BM && FN >= 1, "wave tile");
   static_assert(SA >= 2 && SB >= 2 && (SA - 2) * A_PW < 64 && (SB - 2) * B_PW < 64, "rings");
 
