@@ -237,9 +237,10 @@ __global__ __launch_bounds__(WM * 128) void k_grouped_gemm_bwd(const BwdParams p
       } else {
         // The expert's weights stream past once per column tile: read them
         // non-temporally (decode-shaped input gradients 1.5-2% faster).
-        buffer_load_lds16<kNonTemporal>(static_cast<const char *>(p.b) + (int64_t)ti.e * p.K * p.N * ES,
-                          (uint32_t)((int64_t)p.K * p.N * ES), sb + g * 64,
-                          ((uint32_t)(kt * kKS + krow) * (uint32_t)p.N + (uint32_t)(ti.n0 + col)) * (uint32_t)ES, 0);
+        buffer_load_lds16<kNonTemporal>(
+            static_cast<const char *>(p.b) + (int64_t)ti.e * p.K * p.N * ES,
+            (uint32_t)((int64_t)p.K * p.N * ES), sb + g * 64,
+            ((uint32_t)(kt * kKS + krow) * (uint32_t)p.N + (uint32_t)(ti.n0 + col)) * (uint32_t)ES, 0);
       }
     }
     ++issued;
